@@ -1,0 +1,197 @@
+"""Throughput of batched speculative-sampling verification on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = the whole hot path on the headline workload (B = 256 sequences,
+gamma = 8 draft tokens, V = 128256 bf16 logits, half the sequences greedy and
+half at T = 1): specv_verify (accept prefix + bonus token) followed by
+specv_bonus_topk (F = 4 SSD bonus candidates per position). Inputs are seeded
+synthetic logits already resident in HBM when timing starts.
+
+Prints one JSON line: verified rows/s (B * (gamma + 1) per step), the verify
+kernel's roofline (algorithmic HBM bytes / its average duration, measured with
+HIP events on the launch stream), and the oracle timed on the host cores on a
+bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+WORKLOAD = "v128256_bf16_b256_g8"
+METRIC = "verified vocab rows/sec + achieved HBM GB/s (% peak) at V=128256, B=256, γ=8"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "speculative_sampling_verification_04_amd", "csrc")
+
+
+def algorithmic_bytes(w):
+    """Bytes each call must read at least once: every target row; a draft row
+    only for T > 0 sequences (greedy rows never read the draft) -- verify;
+    every draft row -- top-F. Token ids, temperatures and outputs are added."""
+    row = w.V * 2
+    n_sampled = int((w.temperature > 0).sum())
+    small = w.B * (w.gamma * 4 + 4) + w.B * (w.gamma + 1) * 4 + w.B * w.gamma * 8 + w.B * 8
+    verify = w.B * (w.gamma + 1) * row + n_sampled * w.gamma * row
+    topf = w.B * (w.gamma + 1) * row
+    return verify, verify + small, topf
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The oracle, as written, on a bounded sample of the workload: whole
+    sequences (verify + top-F), alternating greedy and sampled ones, until
+    the time budget is spent."""
+    import oracle
+
+    order = []
+    half = w.B // 2
+    for i in range(half):
+        order += [i, half + i]
+    t0 = time.perf_counter()
+    done = 0
+    for b in order:
+        u, v = oracle.philox.chain_uniforms(w.seed, w.offset, b, w.gamma)
+        oracle.sampling.verify_sequence(w.target[b].astype(np.float64), w.draft[b].astype(np.float64),
+                                        w.draft_tokens[b], float(w.temperature[b]), u, v)
+        oracle.topf.bonus_topf_batch(w.draft[b:b + 1].astype(np.float64), w.draft_tokens[b:b + 1], w.F)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    rows = done * (w.gamma + 1)
+    return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.B} sequences (alternating greedy / T=1), verify + top-F, "
+                      f"{rows} rows in {dt:.1f} s, numpy fp64 on one host thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verification library has no "
+              "multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    from speculative_sampling_verification_04_amd import binding
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.load_library()
+    w = workloads.make_workload(WORKLOAD)
+    target = torch.from_numpy(w.target).to(dev).to(torch.bfloat16)
+    draft = torch.from_numpy(w.draft).to(dev).to(torch.bfloat16)
+    tokens = torch.from_numpy(w.draft_tokens).to(dev)
+    temp = torch.from_numpy(w.temperature).to(dev)
+    B, gamma, F = w.B, w.gamma, w.F
+    out = dict(tokens=torch.empty((B, gamma + 1), dtype=torch.int32, device=dev),
+               num_accepted=torch.empty((B,), dtype=torch.int32, device=dev),
+               probs=torch.empty((B, gamma, 2), dtype=torch.float32, device=dev),
+               bonus_mass=torch.empty((B,), dtype=torch.float32, device=dev))
+    topk = (torch.empty((B, gamma + 1, F), dtype=torch.int32, device=dev),
+            torch.empty((B, gamma + 1, F), dtype=torch.float32, device=dev))
+    ws = torch.zeros(binding.verify_workspace_bytes(B, gamma, w.V), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        binding.verify(target, draft, tokens, temp, w.seed, i, workspace=ws, out=out)
+        if ev is not None:
+            ev[1].record()
+        binding.bonus_topk(draft, tokens, F, out=topk)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    verify_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    topf_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    ms_per_step = elapsed * 1e3 / args.steps
+    rows = B * (gamma + 1)
+    verify_bytes, verify_bytes_io, topf_bytes = algorithmic_bytes(w)
+    achieved = verify_bytes / (verify_ms * 1e-3) / 1e9
+    topf_gbps = topf_bytes / (topf_ms * 1e-3) / 1e9
+    step_gbps = (verify_bytes + topf_bytes) / (ms_per_step * 1e-3) / 1e9
+    traffic = measured_traffic("chain_verify_kernel")
+
+    line = {
+        "metric": METRIC,
+        "value": rows / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": B, "gamma": gamma, "V": w.V, "logits": "bf16",
+                   "F": F, "greedy_sequences": int((w.temperature == 0).sum()),
+                   "step": "specv_verify + specv_bonus_topk", "parallelism": "none"},
+        "hbm_gbps": step_gbps,
+        "hbm_pct_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": "chain_verify_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes": verify_bytes, "avg_ms": verify_ms},
+        "roofline_topf": {"bound": "hbm", "kernel": "topf_kernel", "achieved": topf_gbps,
+                          "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": topf_gbps / HBM_PEAK_GBPS,
+                          "algorithmic_bytes": topf_bytes, "avg_ms": topf_ms},
+        "mean_accepted": float(out["num_accepted"].float().mean().item()),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * specv -- batched speculative-sampling verification for AMD MI355X (gfx950).
+ *
+ * C ABI of libspecv.so. Every pointer argument documented as "device" is a
+ * device pointer owned by the caller; the library never allocates, frees or
+ * synchronises. Every call is asynchronous on the given HIP stream
+ * (hipStream_t, passed as void*; NULL = the null stream) and returns after
+ * enqueueing its kernels. Arguments are validated on the host before any
+ * launch; on a non-OK status nothing was launched (except SPECV_ERR_HIP, which
+ * reports a launch failure) and specv_last_error() describes the problem.
+ * No C++ exception crosses this interface.
+ *
+ * Sources, by page title and section:
+ *  [L5]  Lecture 5: Speculative Decoding and SpecInfer -- sec. 2.1 (tempered
+ *        softmax), 2.2 (accept iff u <= p(x)/q(x); resample from
+ *        norm(max(0, p - q))), 2.7 (greedy), 3.1 (one iteration: first
+ *        rejection, residual or a free token from p_{gamma+1}), 6.4
+ *        (VerifyGreedy and multi-step speculative sampling on token trees).
+ *  [DLN] Speculative Decoding (dl-note) -- sec. 2.2-2.3, Appendix
+ *        "Implementation Details" (vLLM: zero draft probability rejects).
+ *  [SSD] Speculative Speculative Decoding -- sec. 2.1 (outcome (k, t*)),
+ *        sec. 4.1.1 (top-F bonus candidates excluding the drafted token).
+ *
+ * Random numbers: uniforms come from Philox4x32-10 (Salmon et al., SC'11) with
+ * key = (seed mod 2^32, seed >> 32), counter = (offset mod 2^32, offset >> 32,
+ * sequence b, (tag << 24) | (j >> 2)), word = output[j & 3], mapped to
+ * ((word >> 8) + 1) * 2^-24 in (0, 1]. Chain verification uses tag 0 with
+ * j = i for the accept test at position i and j = gamma for the bonus; tree
+ * verification uses tag 1 with j = child node id for its test and j = N for
+ * the bonus. A call is fully determined by its inputs, seed and offset.
+ */
+#ifndef SPECV_H
+#define SPECV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPECV_OK = 0,
+    SPECV_ERR_INVALID_ARG = 1, /* bad size, null pointer, misaligned pointer */
+    SPECV_ERR_WORKSPACE = 2,   /* workspace missing, too small or misaligned */
+    SPECV_ERR_UNSUPPORTED = 3, /* dtype or combination not built */
+    SPECV_ERR_HIP = 4          /* a HIP launch failed */
+} specv_status;
+
+typedef enum {
+    SPECV_F32 = 0,  /* IEEE binary32 logits */
+    SPECV_BF16 = 1  /* bfloat16 logits (upper 16 bits of binary32) */
+} specv_dtype;
+
+/* A strided 3-D view of logits [batch][row][vocab] in device memory.
+ * `data` points at element [0][0][0] and must be aligned to the element size.
+ * Strides are in elements (not bytes), may be 0 (broadcast) and must be >= 0;
+ * the vocabulary dimension is contiguous. Rows whose start is 16-byte aligned
+ * are read with 16-byte vector loads, others element by element. */
+typedef struct {
+    const void* data;
+    int32_t dtype;        /* specv_dtype */
+    int64_t stride_seq;   /* elements between [b][.][.] and [b+1][.][.] */
+    int64_t stride_row;   /* elements between [.][r][.] and [.][r+1][.] */
+} specv_logits;
+
+/* Limits checked by the validators. */
+#define SPECV_MAX_GAMMA 64
+#define SPECV_MAX_VOCAB 1048576
+#define SPECV_MAX_TOPF 31
+#define SPECV_MAX_TREE_NODES 4096
+
+/* Bytes of workspace specv_verify needs for (batch, gamma, vocab). */
+specv_status specv_verify_workspace_size(int32_t batch, int32_t gamma,
+                                         int32_t vocab, size_t* bytes);
+
+/*
+ * Chain verification [L5 sec. 2.2, 3.1; DLN sec. 2.2-2.3; SSD sec. 2.1].
+ *
+ * For each sequence b with temperature T = temperature[b]:
+ *  T > 0: p_t = softmax(target[b][i]/T), p_d = softmax(draft[b][i]/T).
+ *         Position i < gamma accepts draft_tokens[b][i] = x iff p_d(x) > 0 and
+ *         u_i <= p_t(x)/p_d(x). k = the first rejected position (gamma if none).
+ *         If k < gamma the bonus is drawn from w = max(p_t - p_d, 0) of row k;
+ *         otherwise from w = p_t of row gamma. Drawing: the smallest index j
+ *         with w_0 + ... + w_j >= v * (w_0 + ... + w_{V-1}). If the residual
+ *         has zero total mass (rounding only) the bonus is drawn from p_t of
+ *         row k and out_bonus_mass reports 0.
+ *  T == 0 (greedy, [L5 sec. 2.7]): x is accepted iff it equals the target
+ *         argmax of row i (lowest index on ties); the bonus is the target
+ *         argmax of row k. Draft logits are not read.
+ *  A draft token outside [0, vocab) is rejected (it has probability 0).
+ *
+ * target: [batch][gamma+1][vocab]; draft: [batch][>= gamma][vocab] (row i is
+ * read for i < gamma, only when T > 0); both with the same dtype.
+ * draft_tokens: device int32 [batch][gamma], contiguous.
+ * temperature:  device float [batch]; must be >= 0 and finite. Every row read
+ *               must contain at least one finite logit.
+ * Outputs (device, contiguous):
+ *  out_tokens       int32 [batch][gamma+1]: x_0..x_{k-1}, the bonus, then -1.
+ *  out_num_accepted int32 [batch]: k.
+ *  out_probs        float [batch][gamma][2] or NULL: (p_t(x_i), p_d(x_i)) for
+ *                   every i < gamma; for greedy sequences (1 or 0, 1).
+ *  out_bonus_mass   float [batch] or NULL: total mass of the weights the bonus
+ *                   was drawn from (1 - alpha of row k after a rejection, ~1
+ *                   when every token was accepted, 1 for greedy, 0 on the
+ *                   zero-residual fallback).
+ * workspace: device memory of at least specv_verify_workspace_size() bytes,
+ *            256-byte aligned. It must be zero-filled before its first use;
+ *            every call leaves it zero-filled again, so one workspace can be
+ *            reused by calls that are ordered on one stream. Calls that may
+ *            run concurrently need separate workspaces.
+ */
+specv_status specv_verify(specv_logits target, specv_logits draft,
+                          const int32_t* draft_tokens, const float* temperature,
+                          int32_t batch, int32_t gamma, int32_t vocab,
+                          uint64_t seed, uint64_t offset,
+                          int32_t* out_tokens, int32_t* out_num_accepted,
+                          float* out_probs, float* out_bonus_mass,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * SSD/Saguaro bonus-token candidates [SSD sec. 4.1.1; Appendix A.3, Thm 19].
+ *
+ * For every sequence b and lookahead position k in [0, gamma]: the F token ids
+ * with the largest draft logits of row draft[b][k], ordered by logit
+ * (descending) then id (ascending), -0 equal to +0, after removing
+ * draft_tokens[b][k] when k < gamma (the token sent for verification cannot
+ * be the bonus). Position gamma excludes nothing. Temperature plays no part.
+ *
+ * draft: [batch][gamma+1][vocab]. draft_tokens: device int32 [batch][gamma] or
+ * NULL (no exclusion anywhere). 1 <= F <= min(SPECV_MAX_TOPF, vocab - 1).
+ * Outputs (device, contiguous): out_topk int32 [batch][gamma+1][F];
+ * out_topk_logits float [batch][gamma+1][F] or NULL (the candidates' logits).
+ * No workspace.
+ */
+specv_status specv_bonus_topk(specv_logits draft, const int32_t* draft_tokens,
+                              int32_t batch, int32_t gamma, int32_t vocab,
+                              int32_t F, int32_t* out_topk,
+                              float* out_topk_logits, void* stream);
+
+/* Bytes of workspace specv_tree_verify needs for (batch, nodes, vocab). */
+specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes,
+                                              int32_t vocab, size_t* bytes);
+
+/*
+ * Token-tree verification: VerifyGreedy (T == 0) and multi-step speculative
+ * sampling (T > 0) [L5 sec. 6.2, 6.4].
+ *
+ * A tree has `nodes` = N nodes in topological order: parent[b][0] = -1 and
+ * 0 <= parent[b][n] < n for n >= 1 (an entry breaking this is treated as
+ * "no parent": the node is never visited). tokens[b][n] is node n's token.
+ * target[b][n] holds the target logits after the path to node n; draft[b][n]
+ * holds the draft logits at node n, the distribution q its children were
+ * drawn from (children must be independent draws for MSS to be exact).
+ * Walk from the root: at node n with children c_1 < c_2 < ... (by id),
+ *  T > 0: r = p_n; child c with token t is accepted iff q(t) > 0 and
+ *         u_c <= r(t)/q(t); on acceptance the walk moves to c; on rejection
+ *         r <- norm(max(0, r - q)) (kept if that mass is 0). If every child is
+ *         rejected the bonus is drawn from r; at a leaf, from p of the leaf.
+ *  T == 0: move to the lowest-id child whose token is the target argmax of n;
+ *         if none, the bonus is that argmax.
+ *
+ * parent, tokens: device int32 [batch][N], contiguous. temperature: device
+ * float [batch]. target, draft: [batch][N][vocab] (draft rows are read only
+ * for nodes that have children, only when T > 0).
+ * Outputs (device, contiguous): out_path int32 [batch][N]: accepted node ids
+ * in walk order, then -1; out_num_accepted int32 [batch]; out_bonus int32
+ * [batch]. Workspace as for specv_verify (zero-filled before first use, left
+ * zero-filled by every call).
+ */
+specv_status specv_tree_verify(specv_logits target, specv_logits draft,
+                               const int32_t* parent, const int32_t* tokens,
+                               const float* temperature, int32_t batch,
+                               int32_t nodes, int32_t vocab, uint64_t seed,
+                               uint64_t offset, int32_t* out_path,
+                               int32_t* out_num_accepted, int32_t* out_bonus,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* The uniforms the kernels draw: out[b][j] = U(seed, offset, b, tag, j) for
+ * b < batch, j < count (device float [batch][count]). For tests and replay. */
+specv_status specv_uniforms(uint64_t seed, uint64_t offset, int32_t tag,
+                            int32_t batch, int32_t count, float* out,
+                            void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* specv_last_error(void);
+
+/* Library version string. */
+const char* specv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECV_H */

@@ -26,6 +26,8 @@ Readings where the pages are silent (each also listed in the design doc):
     S_j = w_0 + ... + w_j summed left to right, W = S_{V-1}.
   * A residual with zero total mass (possible only through rounding) falls back
     to p_t of the same row.
+  * A draft token outside [0, V) has probability 0 under both distributions,
+    so it is rejected (greedy: it is never the argmax).
 """
 
 from dataclasses import dataclass, field
@@ -57,6 +59,11 @@ def greedy_token(z):
         if z[j] > z[best]:
             best = j
     return best
+
+
+def prob_at(p, x):
+    """p(x), with 0 for a token outside the vocabulary."""
+    return float(p[x]) if 0 <= x < len(p) else 0.0
 
 
 def accept(pt_x, pd_x, u):
@@ -144,14 +151,14 @@ def verify_sequence(target, draft, draft_tokens, T, u, v):
     pd_rows = [tempered_probs(draft[i], T) for i in range(gamma)]
     for i in range(gamma):
         x = int(draft_tokens[i])
-        probs[i] = (pt_rows[i][x], pd_rows[i][x])
+        probs[i] = (prob_at(pt_rows[i], x), prob_at(pd_rows[i], x))
 
     margins = []
     k = gamma
     for i in range(gamma):
-        x = int(draft_tokens[i])
-        margins.append(accept_margin(pt_rows[i][x], pd_rows[i][x], u[i]))
-        if not accept(pt_rows[i][x], pd_rows[i][x], u[i]):
+        pt_x, pd_x = probs[i]
+        margins.append(accept_margin(pt_x, pd_x, u[i]))
+        if not accept(pt_x, pd_x, u[i]):
             k = i
             break
 

@@ -29,7 +29,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from .sampling import (NEAR_TIE, accept, accept_margin, greedy_token,
-                       inverse_cdf, tempered_probs)
+                       inverse_cdf, prob_at, tempered_probs)
 
 
 def children_of(parent, node):
@@ -56,8 +56,9 @@ def mss_node(p, q, child_tokens, u_children, v):
     q = np.asarray(q, dtype=np.float64)
     margins = []
     for j, t in enumerate(child_tokens):
-        margins.append(accept_margin(r[t], q[t], u_children[j]))
-        if accept(r[t], q[t], u_children[j]):
+        r_t, q_t = prob_at(r, t), prob_at(q, t)
+        margins.append(accept_margin(r_t, q_t, u_children[j]))
+        if accept(r_t, q_t, u_children[j]):
             return j, None, margins
         r = mss_residual(r, q)
     bonus, _, m = inverse_cdf(r, v)

@@ -1,0 +1,229 @@
+"""Python binding of libspecv.so: argument marshalling only.
+
+Takes torch tensors on a ROCm device, passes their data pointers, strides and
+torch's current HIP stream to the C ABI (include/specv.h), and returns the
+output tensors. Every step of verification runs in the library's HIP kernels;
+there is no fallback: if the library is missing or fails, this module raises.
+"""
+import ctypes
+import os
+import threading
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libspecv.so")
+
+SPECV_F32, SPECV_BF16 = 0, 1
+STATUS_NAMES = {0: "SPECV_OK", 1: "SPECV_ERR_INVALID_ARG", 2: "SPECV_ERR_WORKSPACE",
+                3: "SPECV_ERR_UNSUPPORTED", 4: "SPECV_ERR_HIP"}
+
+EXPORTED = ("specv_verify_workspace_size", "specv_verify", "specv_bonus_topk",
+            "specv_tree_verify_workspace_size", "specv_tree_verify",
+            "specv_uniforms", "specv_last_error", "specv_version")
+
+
+class SpecvError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class Logits(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("stride_seq", ctypes.c_int64), ("stride_row", ctypes.c_int64)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path=LIB_PATH):
+    """Loads libspecv.so (once). Raises FileNotFoundError if it was not built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise FileNotFoundError(
+                f"{path} not found: build it with "
+                "`python -m speculative_sampling_verification_04_amd.build`")
+        lib = ctypes.CDLL(path)
+        P, I32, I64, U64, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                ctypes.c_uint64, ctypes.c_size_t)
+        SZP = ctypes.POINTER(ctypes.c_size_t)
+        sig = {
+            "specv_verify_workspace_size": [I32, I32, I32, SZP],
+            "specv_tree_verify_workspace_size": [I32, I32, I32, SZP],
+            "specv_verify": [Logits, Logits, P, P, I32, I32, I32, U64, U64,
+                             P, P, P, P, P, SZ, P],
+            "specv_bonus_topk": [Logits, P, I32, I32, I32, I32, P, P, P],
+            "specv_tree_verify": [Logits, Logits, P, P, P, I32, I32, I32, U64, U64,
+                                  P, P, P, P, SZ, P],
+            "specv_uniforms": [U64, U64, I32, I32, I32, P, P],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.specv_last_error.restype = ctypes.c_char_p
+        lib.specv_last_error.argtypes = []
+        lib.specv_version.restype = ctypes.c_char_p
+        lib.specv_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def _check(status):
+    if status != 0:
+        raise SpecvError(status, load_library().specv_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def logits_view(t):
+    """A [batch, rows, vocab] tensor (fp32 or bf16, contiguous along vocab) as
+    the ABI's strided view."""
+    if t.dim() != 3:
+        raise ValueError("logits must be [batch, rows, vocab]")
+    if t.dtype == torch.float32:
+        dt = SPECV_F32
+    elif t.dtype == torch.bfloat16:
+        dt = SPECV_BF16
+    else:
+        raise TypeError(f"logits dtype {t.dtype} is not float32 or bfloat16")
+    if t.size(2) > 1 and t.stride(2) != 1:
+        raise ValueError("logits must be contiguous along the vocabulary")
+    return Logits(t.data_ptr(), dt, t.stride(0), t.stride(1))
+
+
+def _int32(t, shape, name):
+    if t.dtype != torch.int32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous int32 tensor of shape {tuple(shape)}")
+    return t
+
+
+class _WorkspaceCache:
+    """One zero-filled workspace per device, grown on demand. The kernels leave
+    it zero-filled, so calls ordered on one stream can share it."""
+
+    def __init__(self):
+        self._bufs = {}
+
+    def get(self, nbytes, device):
+        key = torch.device(device)
+        buf = self._bufs.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+            self._bufs[key] = buf
+        return buf
+
+
+_workspaces = _WorkspaceCache()
+
+
+def verify_workspace_bytes(batch, gamma, vocab):
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.specv_verify_workspace_size(batch, gamma, vocab, ctypes.byref(n)))
+    return n.value
+
+
+def tree_workspace_bytes(batch, nodes, vocab):
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.specv_tree_verify_workspace_size(batch, nodes, vocab, ctypes.byref(n)))
+    return n.value
+
+
+def verify(target, draft, draft_tokens, temperature, seed, offset=0, *,
+           with_probs=True, with_mass=True, workspace=None, out=None):
+    """Chain verification (specv_verify). target [B, gamma+1, V], draft
+    [B, >= gamma, V], draft_tokens int32 [B, gamma], temperature float32 [B].
+    Returns dict(tokens [B, gamma+1], num_accepted [B], probs [B, gamma, 2],
+    bonus_mass [B])."""
+    lib = load_library()
+    B, rows, V = target.shape
+    gamma = rows - 1
+    dev = target.device
+    _int32(draft_tokens, (B, gamma), "draft_tokens")
+    if temperature.dtype != torch.float32 or temperature.shape != (B,) or not temperature.is_contiguous():
+        raise ValueError("temperature must be a contiguous float32 tensor of shape (B,)")
+    if draft.shape[0] != B or draft.shape[1] < gamma or draft.shape[2] != V:
+        raise ValueError("draft must be [B, >= gamma, V]")
+    if out is None:
+        out = dict(
+            tokens=torch.empty((B, gamma + 1), dtype=torch.int32, device=dev),
+            num_accepted=torch.empty((B,), dtype=torch.int32, device=dev),
+            probs=torch.empty((B, gamma, 2), dtype=torch.float32, device=dev) if with_probs else None,
+            bonus_mass=torch.empty((B,), dtype=torch.float32, device=dev) if with_mass else None)
+    nbytes = verify_workspace_bytes(B, gamma, V)
+    ws = workspace if workspace is not None else _workspaces.get(nbytes, dev)
+    _check(lib.specv_verify(logits_view(target), logits_view(draft), _ptr(draft_tokens),
+                            _ptr(temperature), B, gamma, V, seed, offset,
+                            _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out["probs"]),
+                            _ptr(out["bonus_mass"]), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def bonus_topk(draft, draft_tokens, F, *, with_logits=True, out=None):
+    """SSD top-F bonus candidates (specv_bonus_topk). draft [B, gamma+1, V],
+    draft_tokens int32 [B, gamma] or None. Returns (topk [B, gamma+1, F] int32,
+    logits [B, gamma+1, F] float32 or None)."""
+    lib = load_library()
+    B, rows, V = draft.shape
+    gamma = rows - 1
+    dev = draft.device
+    if draft_tokens is not None:
+        _int32(draft_tokens, (B, gamma), "draft_tokens")
+    if out is None:
+        out = (torch.empty((B, rows, F), dtype=torch.int32, device=dev),
+               torch.empty((B, rows, F), dtype=torch.float32, device=dev) if with_logits else None)
+    _check(lib.specv_bonus_topk(logits_view(draft), _ptr(draft_tokens), B, gamma, V, F,
+                                _ptr(out[0]), _ptr(out[1]), _stream(dev)))
+    return out
+
+
+def tree_verify(target, draft, parent, tokens, temperature, seed, offset=0, *, workspace=None, out=None):
+    """Token-tree verification (specv_tree_verify). target/draft [B, N, V],
+    parent/tokens int32 [B, N], temperature float32 [B]. Returns dict(path
+    [B, N], num_accepted [B], bonus [B])."""
+    lib = load_library()
+    B, N, V = target.shape
+    dev = target.device
+    _int32(parent, (B, N), "parent")
+    _int32(tokens, (B, N), "tokens")
+    if temperature.dtype != torch.float32 or temperature.shape != (B,) or not temperature.is_contiguous():
+        raise ValueError("temperature must be a contiguous float32 tensor of shape (B,)")
+    if tuple(draft.shape) != (B, N, V):
+        raise ValueError("draft must be [B, N, V]")
+    if out is None:
+        out = dict(path=torch.empty((B, N), dtype=torch.int32, device=dev),
+                   num_accepted=torch.empty((B,), dtype=torch.int32, device=dev),
+                   bonus=torch.empty((B,), dtype=torch.int32, device=dev))
+    nbytes = tree_workspace_bytes(B, N, V)
+    ws = workspace if workspace is not None else _workspaces.get(nbytes, dev)
+    _check(lib.specv_tree_verify(logits_view(target), logits_view(draft), _ptr(parent), _ptr(tokens),
+                                 _ptr(temperature), B, N, V, seed, offset, _ptr(out["path"]),
+                                 _ptr(out["num_accepted"]), _ptr(out["bonus"]), _ptr(ws), ws.numel(),
+                                 _stream(dev)))
+    return out
+
+
+def uniforms(seed, offset, tag, batch, count, device="cuda"):
+    """The kernels' uniforms U(seed, offset, b, tag, j) as a [batch, count]
+    float32 tensor (specv_uniforms)."""
+    lib = load_library()
+    out = torch.empty((batch, count), dtype=torch.float32, device=device)
+    _check(lib.specv_uniforms(seed, offset, tag, batch, count, _ptr(out), _stream(out.device)))
+    return out
+
+
+def version():
+    return load_library().specv_version().decode()

@@ -1,0 +1,258 @@
+// C ABI of libspecv.so (declared in include/specv.h): argument validation,
+// workspace sizing and kernel launches. Nothing here allocates device memory
+// or synchronises; a non-OK status means nothing was launched (except
+// SPECV_ERR_HIP, a failed launch).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/specv.h"
+#include "specv_device.hpp"
+#include "specv_launch.hpp"
+
+namespace specv {
+
+namespace {
+
+thread_local std::string g_error;
+
+specv_status fail(specv_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+
+specv_status ok() {
+    g_error.clear();
+    return SPECV_OK;
+}
+
+int elem_size(int32_t dtype) { return dtype == SPECV_BF16 ? 2 : 4; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Largest grid the launches accept (grid.x * 256 threads must fit 32 bits).
+constexpr int64_t kMaxGrid = (int64_t(1) << 32) / kThreads - 1;
+
+specv_status check_logits(const char* name, const specv_logits& l) {
+    if (l.data == nullptr) return fail(SPECV_ERR_INVALID_ARG, "%s.data is NULL", name);
+    if (l.dtype != SPECV_F32 && l.dtype != SPECV_BF16)
+        return fail(SPECV_ERR_UNSUPPORTED, "%s.dtype %d is not SPECV_F32 or SPECV_BF16", name, l.dtype);
+    if (reinterpret_cast<uintptr_t>(l.data) % elem_size(l.dtype) != 0)
+        return fail(SPECV_ERR_INVALID_ARG, "%s.data is not aligned to its element size", name);
+    if (l.stride_seq < 0 || l.stride_row < 0)
+        return fail(SPECV_ERR_INVALID_ARG, "%s strides must be >= 0", name);
+    return SPECV_OK;
+}
+
+specv_status check_workspace(void* ws, size_t have, size_t need) {
+    if (need > 0 && ws == nullptr) return fail(SPECV_ERR_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
+        return fail(SPECV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (have < need)
+        return fail(SPECV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+    return SPECV_OK;
+}
+
+RowView view(const specv_logits& l) { return RowView{l.data, l.stride_seq, l.stride_row}; }
+
+// Workspace: one 64-bit slot per workgroup (row chunk).
+struct Layout {
+    int32_t S;
+    int64_t chunk;
+    size_t slot_bytes;
+    size_t total() const { return slot_bytes; }
+};
+
+Layout layout_for(int64_t batch, int64_t row_tasks_per_seq, int64_t vocab) {
+    Layout L;
+    choose_split(batch * row_tasks_per_seq, vocab, &L.S, &L.chunk);
+    L.slot_bytes = round_up(size_t(batch) * row_tasks_per_seq * L.S * sizeof(uint64_t));
+    return L;
+}
+
+specv_status check_chain_sizes(int32_t batch, int32_t gamma, int32_t vocab) {
+    if (batch < 1) return fail(SPECV_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+    if (gamma < 1 || gamma > SPECV_MAX_GAMMA)
+        return fail(SPECV_ERR_INVALID_ARG, "gamma must be in [1, %d] (got %d)", SPECV_MAX_GAMMA, gamma);
+    if (vocab < 1 || vocab > SPECV_MAX_VOCAB)
+        return fail(SPECV_ERR_INVALID_ARG, "vocab must be in [1, %d] (got %d)", SPECV_MAX_VOCAB, vocab);
+    return SPECV_OK;
+}
+
+specv_status check_tree_sizes(int32_t batch, int32_t nodes, int32_t vocab) {
+    if (batch < 1) return fail(SPECV_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+    if (nodes < 1 || nodes > SPECV_MAX_TREE_NODES)
+        return fail(SPECV_ERR_INVALID_ARG, "nodes must be in [1, %d] (got %d)", SPECV_MAX_TREE_NODES, nodes);
+    if (vocab < 1 || vocab > SPECV_MAX_VOCAB)
+        return fail(SPECV_ERR_INVALID_ARG, "vocab must be in [1, %d] (got %d)", SPECV_MAX_VOCAB, vocab);
+    return SPECV_OK;
+}
+
+}  // namespace
+
+__global__ void uniforms_kernel(uint64_t seed, uint64_t offset, uint32_t tag, int32_t B, int32_t J, float* out) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < int64_t(B) * J)
+        out[i] = stream_uniform(seed, offset, uint32_t(i / J), tag, uint32_t(i % J));
+}
+
+hipError_t launch_uniforms(uint64_t seed, uint64_t offset, int32_t tag, int32_t B, int32_t J, float* out,
+                           hipStream_t stream) {
+    const int64_t n = int64_t(B) * J;
+    const unsigned blocks = unsigned((n + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(uniforms_kernel, dim3(blocks), dim3(kThreads), 0, stream, seed, offset, uint32_t(tag), B,
+                       J, out);
+    return hipGetLastError();
+}
+
+}  // namespace specv
+
+using namespace specv;
+
+extern "C" {
+
+const char* specv_last_error(void) { return g_error.c_str(); }
+
+const char* specv_version(void) { return "specv 0.1 (gfx950)"; }
+
+specv_status specv_verify_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, size_t* bytes) {
+    if (bytes == nullptr) return fail(SPECV_ERR_INVALID_ARG, "bytes is NULL");
+    specv_status st = check_chain_sizes(batch, gamma, vocab);
+    if (st != SPECV_OK) return st;
+    *bytes = layout_for(batch, 2 * int64_t(gamma) + 1, vocab).total();
+    return ok();
+}
+
+specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes, int32_t vocab, size_t* bytes) {
+    if (bytes == nullptr) return fail(SPECV_ERR_INVALID_ARG, "bytes is NULL");
+    specv_status st = check_tree_sizes(batch, nodes, vocab);
+    if (st != SPECV_OK) return st;
+    *bytes = layout_for(batch, 2 * int64_t(nodes), vocab).total();
+    return ok();
+}
+
+specv_status specv_verify(specv_logits target, specv_logits draft, const int32_t* draft_tokens,
+                          const float* temperature, int32_t batch, int32_t gamma, int32_t vocab, uint64_t seed,
+                          uint64_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                          float* out_bonus_mass, void* workspace, size_t workspace_bytes, void* stream) {
+    specv_status st = check_chain_sizes(batch, gamma, vocab);
+    if (st != SPECV_OK) return st;
+    if ((st = check_logits("target", target)) != SPECV_OK) return st;
+    if ((st = check_logits("draft", draft)) != SPECV_OK) return st;
+    if (target.dtype != draft.dtype)
+        return fail(SPECV_ERR_UNSUPPORTED, "target and draft must have the same dtype");
+    if (!draft_tokens || !temperature || !out_tokens || !out_num_accepted)
+        return fail(SPECV_ERR_INVALID_ARG, "draft_tokens, temperature, out_tokens and out_num_accepted are required");
+    const Layout L = layout_for(batch, 2 * int64_t(gamma) + 1, vocab);
+    const int64_t grid = int64_t(batch) * (2 * gamma + 1) * L.S;
+    if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch (%lld workgroups)", (long long)grid);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
+
+    ChainArgs a;
+    a.target = view(target);
+    a.draft = view(draft);
+    a.tokens = draft_tokens;
+    a.temperature = temperature;
+    a.B = batch;
+    a.gamma = gamma;
+    a.V = vocab;
+    a.S = L.S;
+    a.chunk = L.chunk;
+    a.seed = seed;
+    a.offset = offset;
+    a.out_tokens = out_tokens;
+    a.out_nacc = out_num_accepted;
+    a.out_probs = out_probs;
+    a.out_mass = out_bonus_mass;
+    a.slots = static_cast<uint64_t*>(workspace);
+    const hipError_t e = launch_chain(a, target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_verify launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+specv_status specv_bonus_topk(specv_logits draft, const int32_t* draft_tokens, int32_t batch, int32_t gamma,
+                              int32_t vocab, int32_t F, int32_t* out_topk, float* out_topk_logits, void* stream) {
+    specv_status st = check_chain_sizes(batch, gamma, vocab);
+    if (st != SPECV_OK) return st;
+    if ((st = check_logits("draft", draft)) != SPECV_OK) return st;
+    if (F < 1 || F > SPECV_MAX_TOPF || F > vocab - 1)
+        return fail(SPECV_ERR_INVALID_ARG, "F must be in [1, min(%d, vocab - 1)] (got %d, vocab %d)", SPECV_MAX_TOPF,
+                    F, vocab);
+    if (!out_topk) return fail(SPECV_ERR_INVALID_ARG, "out_topk is required");
+    const int64_t grid = int64_t(batch) * (gamma + 1);
+    if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch");
+    TopFArgs a;
+    a.draft = view(draft);
+    a.tokens = draft_tokens;
+    a.B = batch;
+    a.gamma = gamma;
+    a.V = vocab;
+    a.F = F;
+    a.out_topk = out_topk;
+    a.out_logits = out_topk_logits;
+    const hipError_t e = launch_topf(a, draft.dtype == SPECV_BF16 ? DT_BF16 : DT_F32, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_bonus_topk launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+specv_status specv_tree_verify(specv_logits target, specv_logits draft, const int32_t* parent, const int32_t* tokens,
+                               const float* temperature, int32_t batch, int32_t nodes, int32_t vocab, uint64_t seed,
+                               uint64_t offset, int32_t* out_path, int32_t* out_num_accepted, int32_t* out_bonus,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    specv_status st = check_tree_sizes(batch, nodes, vocab);
+    if (st != SPECV_OK) return st;
+    if ((st = check_logits("target", target)) != SPECV_OK) return st;
+    if ((st = check_logits("draft", draft)) != SPECV_OK) return st;
+    if (target.dtype != draft.dtype)
+        return fail(SPECV_ERR_UNSUPPORTED, "target and draft must have the same dtype");
+    if (!parent || !tokens || !temperature || !out_path || !out_num_accepted || !out_bonus)
+        return fail(SPECV_ERR_INVALID_ARG, "parent, tokens, temperature and the outputs are required");
+    const Layout L = layout_for(batch, 2 * int64_t(nodes), vocab);
+    const int64_t grid = int64_t(batch) * 2 * nodes * L.S;
+    if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch");
+    if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
+
+    TreeArgs a;
+    a.target = view(target);
+    a.draft = view(draft);
+    a.parent = parent;
+    a.tokens = tokens;
+    a.temperature = temperature;
+    a.B = batch;
+    a.N = nodes;
+    a.V = vocab;
+    a.S = L.S;
+    a.chunk = L.chunk;
+    a.seed = seed;
+    a.offset = offset;
+    a.out_path = out_path;
+    a.out_nacc = out_num_accepted;
+    a.out_bonus = out_bonus;
+    a.slots = static_cast<uint64_t*>(workspace);
+    const hipError_t e = launch_tree(a, target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_tree_verify launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+specv_status specv_uniforms(uint64_t seed, uint64_t offset, int32_t tag, int32_t batch, int32_t count, float* out,
+                            void* stream) {
+    if (batch < 1 || count < 1) return fail(SPECV_ERR_INVALID_ARG, "batch and count must be >= 1");
+    if (tag < 0 || tag > 255) return fail(SPECV_ERR_INVALID_ARG, "tag must be in [0, 255]");
+    if (count > (1 << 26)) return fail(SPECV_ERR_INVALID_ARG, "count must be <= 2^26");
+    if (int64_t(batch) * count > (int64_t(1) << 31)) return fail(SPECV_ERR_INVALID_ARG, "batch * count too large");
+    if (!out) return fail(SPECV_ERR_INVALID_ARG, "out is NULL");
+    const hipError_t e = launch_uniforms(seed, offset, tag, batch, count, out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_uniforms launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

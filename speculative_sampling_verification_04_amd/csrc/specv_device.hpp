@@ -1,0 +1,401 @@
+// Device building blocks shared by the verification kernels (gfx950, wave64).
+//
+// Rows are streamed once from HBM with 16-byte loads; each lane keeps running
+// statistics in registers:
+//  * SoftmaxAcc: online max and sum of 2^(z*c - mc) with c = log2(e)/T, the
+//    normaliser of softmax(z/T) [Lecture 5: Speculative Decoding and
+//    SpecInfer, sec. 2.1]. mc is the fp32 product m*c of the running max, and
+//    every term is evaluated as exp2(fma(z, c, -mc)), so all terms of a lane
+//    share one reference and rescaling is exact up to one rounding.
+//  * ArgmaxAcc: the greedy (one-hot) token, lowest index on ties [sec. 2.7].
+//  * TopKAcc: the K largest (logit, -index) keys, for the SSD bonus-token
+//    candidates [Speculative Speculative Decoding, sec. 4.1.1].
+// Lane results are merged within the wave by xor-shuffles and across the
+// workgroup's waves through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specv {
+
+constexpr int kThreads = 256;               // one workgroup = 4 waves
+constexpr int kWaveSize = 64;
+constexpr int kWaves = kThreads / kWaveSize;
+constexpr int kLaneElems = 8;               // elements per lane per step
+constexpr int kTileElems = kWaveSize * kLaneElems;  // residual tile: 512
+constexpr int kMaxTiles = 2048;             // vocab <= 2048 * 512
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+// ---------------------------------------------------------------- elements
+
+template <int DT> struct ElemT;
+template <> struct ElemT<DT_F32> { static constexpr int kBytes = 4; };
+template <> struct ElemT<DT_BF16> { static constexpr int kBytes = 2; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* row, int64_t j) {
+    if constexpr (DT == DT_F32) {
+        return static_cast<const float*>(row)[j];
+    } else {
+        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(row)[j]) << 16);
+    }
+}
+
+// Raw storage of kLaneElems consecutive elements: one 16-byte word for bf16,
+// two for fp32.
+template <int DT> struct Raw8 { uint4 w[ElemT<DT>::kBytes / 2]; };
+
+template <int DT>
+__device__ __forceinline__ void load_raw8(Raw8<DT>& r, const char* p) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < ElemT<DT>::kBytes / 2; ++i) r.w[i] = q[i];
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack8(const Raw8<DT>& r, float v[kLaneElems]) {
+    if constexpr (DT == DT_F32) {
+        v[0] = __uint_as_float(r.w[0].x); v[1] = __uint_as_float(r.w[0].y);
+        v[2] = __uint_as_float(r.w[0].z); v[3] = __uint_as_float(r.w[0].w);
+        v[4] = __uint_as_float(r.w[1].x); v[5] = __uint_as_float(r.w[1].y);
+        v[6] = __uint_as_float(r.w[1].z); v[7] = __uint_as_float(r.w[1].w);
+    } else {
+        v[0] = bf16_lo(r.w[0].x); v[1] = bf16_hi(r.w[0].x);
+        v[2] = bf16_lo(r.w[0].y); v[3] = bf16_hi(r.w[0].y);
+        v[4] = bf16_lo(r.w[0].z); v[5] = bf16_hi(r.w[0].z);
+        v[6] = bf16_lo(r.w[0].w); v[7] = bf16_hi(r.w[0].w);
+    }
+}
+
+__device__ __forceinline__ float max8(const float v[kLaneElems]) {
+    return fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
+                 fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+}
+
+// ------------------------------------------------------------- streaming
+//
+// Visits elements [lo, hi) of `row`. When the chunk start is 16-byte aligned
+// the body is read in steps of kLaneElems elements per lane, U steps in flight
+// per lane per iteration (lane t takes steps t, t + kThreads, ...), and the
+// remainder element by element; otherwise every element is read singly.
+// The loop bound is uniform over the workgroup, so every lane calls the
+// visitor's block() on every iteration (visitors may use wave-wide operations);
+// steps past the end arrive as -inf with valid = false.
+template <int DT, int U, class Acc>
+__device__ __forceinline__ void stream_chunk(const void* row, int64_t lo, int64_t hi, Acc& acc) {
+    constexpr int kB = ElemT<DT>::kBytes;
+    const char* base = static_cast<const char*>(row) + lo * kB;
+    const int64_t n = hi - lo;
+    const bool aligned = (reinterpret_cast<uintptr_t>(base) & 15u) == 0;
+    const int64_t nstep = aligned ? n / kLaneElems : 0;
+    for (int64_t base0 = 0; base0 < nstep; base0 += int64_t(kThreads) * U) {
+        Raw8<DT> raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t s = base0 + threadIdx.x + int64_t(u) * kThreads;
+            if (s < nstep) load_raw8<DT>(raw[u], base + s * (kLaneElems * kB));
+        }
+        float v[U][kLaneElems];
+        int64_t idx[U];
+        bool valid[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t s = base0 + threadIdx.x + int64_t(u) * kThreads;
+            valid[u] = s < nstep;
+            idx[u] = lo + s * kLaneElems;
+            if (valid[u]) {
+                unpack8<DT>(raw[u], v[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < kLaneElems; ++e) v[u][e] = -INFINITY;
+            }
+        }
+        acc.template block<U>(v, idx, valid);
+    }
+    for (int64_t j = nstep * kLaneElems + threadIdx.x; j < n; j += kThreads)
+        acc.one(load_elem<DT>(row, lo + j), lo + j);
+}
+
+// ------------------------------------------------------------------ Philox
+//
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64-bit products, key bumped by the Weyl constants between rounds.
+
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    }
+    return c;
+}
+
+// U(seed, offset, b, tag, j) in (0, 1]: word j & 3 of the block at counter
+// (offset lo, offset hi, b, tag << 24 | j >> 2), top 24 bits plus one, / 2^24.
+__device__ __forceinline__ float stream_uniform(uint64_t seed, uint64_t offset, uint32_t b,
+                                                uint32_t tag, uint32_t j) {
+    const uint4 o = philox4x32_10(
+        make_uint4(uint32_t(offset), uint32_t(offset >> 32), b, (tag << 24) | (j >> 2)),
+        uint32_t(seed), uint32_t(seed >> 32));
+    const uint32_t w = (j & 3) == 0 ? o.x : (j & 3) == 1 ? o.y : (j & 3) == 2 ? o.z : o.w;
+    return float((w >> 8) + 1u) * 5.9604644775390625e-08f;  // 2^-24
+}
+
+// ---------------------------------------------------------- reductions
+
+// A chunk's statistics are published as one 64-bit word, so that a single
+// agent-scope atomic store carries both the value and its readiness, and a
+// reader that sees the word sees all of it (no fence is needed; on gfx950 an
+// agent-scope release fence is an L2 write-back). The low half is never 0 for
+// a published word, so a zero-filled slot means "not published yet".
+//   softmax: hi = bits(max logit m), lo = ~bits(fp32 s), s = sum 2^(z*c - mc)
+//            relative to mc = fp32(m * c), which the reader recomputes;
+//   greedy:  hi = bits(best logit),  lo = ~uint32(index), index >= 0;
+//   skipped row (nothing read): hi = bits(-inf), lo = ~bits(0.0f).
+__device__ __forceinline__ uint64_t pack_slot(float hi, uint32_t lo) {
+    return (uint64_t(__float_as_uint(hi)) << 32) | uint64_t(lo);
+}
+__device__ __forceinline__ uint64_t pack_softmax(float m, double s) { return pack_slot(m, ~__float_as_uint(float(s))); }
+__device__ __forceinline__ uint64_t pack_argmax(float v, int32_t idx) { return pack_slot(v, ~uint32_t(idx)); }
+__device__ __forceinline__ uint64_t pack_skipped() { return pack_slot(-INFINITY, ~__float_as_uint(0.0f)); }
+__device__ __forceinline__ bool slot_ready(uint64_t w) { return uint32_t(w) != 0u; }
+__device__ __forceinline__ float slot_hi(uint64_t w) { return __uint_as_float(uint32_t(w >> 32)); }
+__device__ __forceinline__ float slot_s(uint64_t w) { return __uint_as_float(~uint32_t(w)); }
+__device__ __forceinline__ int32_t slot_idx(uint64_t w) { return int32_t(~uint32_t(w)); }
+
+__device__ __forceinline__ void publish(uint64_t* slot, uint64_t w) {
+    __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t peek(const uint64_t* slot) {
+    return __hip_atomic_load(const_cast<uint64_t*>(slot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// a += b for softmax partials (both relative to their own mc).
+__device__ __forceinline__ void merge_softmax(float& m, float& mc, double& s,
+                                              float bm, float bmc, double bs) {
+    if (bm == -INFINITY) return;
+    if (m == -INFINITY) { m = bm; mc = bmc; s = bs; return; }
+    if (bm > m) {
+        s = s * exp2(double(mc) - double(bmc)) + bs;
+        m = bm; mc = bmc;
+    } else {
+        s += bs * exp2(double(bmc) - double(mc));
+    }
+}
+
+// Greedy order: larger value first, then lower index.
+// (v, i) beats (bv, bi); an index < 0 marks "no element".
+__device__ __forceinline__ bool argmax_better(float v, int32_t i, float bv, int32_t bi) {
+    if (i < 0) return false;
+    if (bi < 0) return true;
+    return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ void wave_merge_softmax(float& m, float& mc, double& s) {
+#pragma unroll
+    for (int o = 1; o < kWaveSize; o <<= 1) {
+        const float om = __shfl_xor(m, o);
+        const float omc = __shfl_xor(mc, o);
+        const double os = __shfl_xor(s, o);
+        merge_softmax(m, mc, s, om, omc, os);
+    }
+}
+
+__device__ __forceinline__ void wave_merge_argmax(float& v, int32_t& i) {
+#pragma unroll
+    for (int o = 1; o < kWaveSize; o <<= 1) {
+        const float ov = __shfl_xor(v, o);
+        const int32_t oi = __shfl_xor(i, o);
+        if (argmax_better(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+    for (int o = 1; o < kWaveSize; o <<= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 1; o < kWaveSize; o <<= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Inclusive prefix sum across the wave (lane order).
+__device__ __forceinline__ double wave_inclusive_scan(double x) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+#pragma unroll
+    for (int o = 1; o < kWaveSize; o <<= 1) {
+        const double y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#pragma unroll
+    for (int o = 1; o < kWaveSize; o <<= 1) {
+        const uint64_t y = __shfl_xor(x, o);
+        x = y > x ? y : x;
+    }
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+    for (int o = 1; o < kWaveSize; o <<= 1) {
+        const uint32_t y = __shfl_xor(x, o);
+        x = y > x ? y : x;
+    }
+    return x;
+}
+
+// ------------------------------------------------------------ accumulators
+
+// Online softmax statistics of one lane. c = log2(e)/T as fp32.
+struct SoftmaxAcc {
+    float c;
+    float m = -INFINITY;
+    float mc = -INFINITY;
+    double s = 0.0;
+
+    __device__ explicit SoftmaxAcc(float c_) : c(c_) {}
+
+    __device__ __forceinline__ void rebase(float cm) {
+        if (cm > m) {
+            const float mcn = cm * c;
+            s = (m == -INFINITY) ? 0.0 : s * double(__builtin_amdgcn_exp2f(mc - mcn));
+            m = cm;
+            mc = mcn;
+        }
+    }
+
+    template <int U>
+    __device__ __forceinline__ void block(const float (&v)[U][kLaneElems], const int64_t*, const bool*) {
+        float cm = max8(v[0]);
+#pragma unroll
+        for (int u = 1; u < U; ++u) cm = fmaxf(cm, max8(v[u]));
+        rebase(cm);
+        const float nmc = (m == -INFINITY) ? 0.0f : -mc;
+        float part[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float t[kLaneElems];
+#pragma unroll
+            for (int e = 0; e < kLaneElems; ++e) t[e] = __builtin_amdgcn_exp2f(fmaf(v[u][e], c, nmc));
+            part[u] = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+        }
+        float tot = part[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) tot += part[u];
+        s += double(tot);
+    }
+
+    __device__ __forceinline__ void one(float z, int64_t) {
+        rebase(z);
+        if (m != -INFINITY) s += double(__builtin_amdgcn_exp2f(fmaf(z, c, -mc)));
+    }
+};
+
+// Greedy argmax of one lane: lanes see their elements in increasing index
+// order, so a strict comparison keeps the lowest index.
+struct ArgmaxAcc {
+    float best = -INFINITY;
+    int32_t idx = -1;
+
+    template <int U>
+    __device__ __forceinline__ void block(const float (&v)[U][kLaneElems], const int64_t* base, const bool* valid) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float vm = max8(v[u]);
+            if (valid[u] && (vm > best || idx < 0)) {
+                int e = kLaneElems - 1;
+#pragma unroll
+                for (int k = kLaneElems - 2; k >= 0; --k) e = (v[u][k] == vm) ? k : e;
+                best = vm;
+                idx = int32_t(base[u] + e);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void one(float z, int64_t j) {
+        if (z > best || idx < 0) { best = z; idx = int32_t(j); }
+    }
+};
+
+// Order-preserving 32-bit key of a logit (-0 mapped to +0): larger logit,
+// larger key. Full 64-bit key = (logit key << 32) | ~index, so equal logits
+// order by lower index first.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_logit(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ uint64_t full_key(float v, int64_t j) {
+    return (uint64_t(logit_key(v)) << 32) | uint64_t(~uint32_t(j));
+}
+
+// The K largest keys seen by one lane, sorted descending. A wave-wide
+// threshold (the largest K-th key over the wave's lanes, logit part only)
+// filters elements: anything below it cannot be among the row's K largest.
+template <int K>
+struct TopKAcc {
+    uint64_t a[K];
+    uint32_t theta = 0;          // logit key of the wave threshold
+    float theta_val = -INFINITY; // its logit
+
+    __device__ TopKAcc() {
+#pragma unroll
+        for (int i = 0; i < K; ++i) a[i] = 0;
+    }
+
+    __device__ __forceinline__ void insert(uint64_t key) {
+#pragma unroll
+        for (int i = K - 1; i > 0; --i) {
+            const uint64_t hi = a[i - 1];
+            a[i] = key > hi ? hi : (key > a[i] ? key : a[i]);
+        }
+        a[0] = key > a[0] ? key : a[0];
+    }
+
+    __device__ __forceinline__ void consider(float v, int64_t j) {
+        if (logit_key(v) >= theta) {
+            const uint64_t key = full_key(v, j);
+            if (key > a[K - 1]) insert(key);
+        }
+    }
+
+    __device__ __forceinline__ void refresh_threshold() {
+        theta = wave_max_u32(uint32_t(a[K - 1] >> 32));
+        theta_val = theta == 0 ? -INFINITY : key_logit(theta);
+    }
+
+    template <int U>
+    __device__ __forceinline__ void block(const float (&v)[U][kLaneElems], const int64_t* base, const bool* valid) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (valid[u] && max8(v[u]) >= theta_val) {
+#pragma unroll
+                for (int e = 0; e < kLaneElems; ++e) consider(v[u][e], base[u] + e);
+            }
+        }
+        refresh_threshold();
+    }
+
+    __device__ __forceinline__ void one(float z, int64_t j) { consider(z, j); }
+};
+
+}  // namespace specv

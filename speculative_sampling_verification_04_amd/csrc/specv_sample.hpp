@@ -1,0 +1,290 @@
+// Workgroup-level pieces of the resolve step of the verification kernels:
+// collecting the published row statistics, block merges, and inverse-CDF
+// sampling from a row of non-negative weights.
+//
+// Inverse CDF [reading of Lecture 5: Speculative Decoding and SpecInfer, sec.
+// 2.2 step 4 / Speculative Decoding (dl-note), sec. 2.3]: the sample is the
+// smallest index j with w_0 + ... + w_j >= v * W, W = sum of all weights.
+// Two passes over the row: (A) the waves sum 512-element tiles (64 lanes x 8
+// consecutive elements), several tiles in flight per wave, into LDS; (B) wave 0
+// scans the tile sums in fp64 to find the tile that holds v*W, recomputes that
+// tile's weights (bit-identical to pass A) and scans them for the index. Only
+// the one row (pair) that needs a sample is read a second time.
+#pragma once
+
+#include "specv_device.hpp"
+
+namespace specv {
+
+constexpr int kTilesInFlight = 4;      // residual pass: tiles per wave per iteration
+constexpr int kMaxSpin = 1 << 24;      // bound on the resolver's wait (about a second)
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWaveSize - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWaveSize; }
+
+__device__ __forceinline__ void block_merge_softmax(float& m, float& mc, double& s) {
+    __shared__ float sm[kWaves], smc[kWaves];
+    __shared__ double ss[kWaves];
+    wave_merge_softmax(m, mc, s);
+    if (lane_id() == 0) { sm[wave_id()] = m; smc[wave_id()] = mc; ss[wave_id()] = s; }
+    __syncthreads();
+    m = sm[0]; mc = smc[0]; s = ss[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) merge_softmax(m, mc, s, sm[w], smc[w], ss[w]);
+    __syncthreads();
+}
+
+__device__ __forceinline__ void block_merge_argmax(float& v, int32_t& i) {
+    __shared__ float sv[kWaves];
+    __shared__ int32_t si[kWaves];
+    wave_merge_argmax(v, i);
+    if (lane_id() == 0) { sv[wave_id()] = v; si[wave_id()] = i; }
+    __syncthreads();
+    v = sv[0]; i = si[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+        if (argmax_better(sv[w], si[w], v, i)) { v = sv[w]; i = si[w]; }
+    __syncthreads();
+}
+
+// Waits until the n slots are all published (wave 0 polls with agent-scope
+// atomic loads). Every slot's writer is a workgroup with a lower index, which
+// is dispatched before the caller and never waits itself, so the wait ends;
+// the spin is bounded anyway. Returns false if the bound was reached.
+__device__ bool wait_slots(const uint64_t* slots, int64_t n) {
+    __shared__ int s_ok;
+    if (wave_id() == 0) {
+        int ok = 0;
+        for (int spin = 0; spin < kMaxSpin; ++spin) {
+            bool mine = true;
+            for (int64_t i = lane_id(); i < n; i += kWaveSize) mine = mine && slot_ready(peek(slots + i));
+            if (__all(mine)) { ok = 1; break; }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane_id() == 0) s_ok = ok;
+    }
+    __syncthreads();
+    return s_ok != 0;
+}
+
+// Returns the n slots to zero (the workspace's resting state).
+__device__ __forceinline__ void zero_slots(uint64_t* slots, int64_t n) {
+    for (int64_t i = threadIdx.x; i < n; i += kThreads) publish(slots + i, 0ull);
+}
+
+// Merged statistics of one row (all chunks).
+struct RowStats {
+    float m;     // max logit (greedy: best logit)
+    float mc;    // fp32 m * c
+    int32_t idx; // greedy argmax
+    double Z;    // sum of 2^(z*c - mc)
+};
+
+__device__ __forceinline__ RowStats merge_slots(const uint64_t* p, int S, bool greedy, float c) {
+    RowStats r;
+    r.m = -INFINITY; r.mc = -INFINITY; r.idx = -1; r.Z = 0.0;
+    for (int k = 0; k < S; ++k) {
+        const uint64_t w = peek(p + k);
+        if (greedy) {
+            const float v = slot_hi(w);
+            const int32_t i = slot_idx(w);
+            if (argmax_better(v, i, r.m, r.idx)) { r.m = v; r.idx = i; }
+        } else {
+            const float m = slot_hi(w);
+            merge_softmax(r.m, r.mc, r.Z, m, m * c, double(slot_s(w)));
+        }
+    }
+    return r;
+}
+
+// p(x) = 2^(z*c - mc) / Z in fp64, the same reference the streaming pass used.
+__device__ __forceinline__ double prob_of(float z, float c, const RowStats& st) {
+    if (z == -INFINITY) return 0.0;
+    return exp2(double(z) * double(c) - double(st.mc)) / st.Z;
+}
+
+// Raw bits of 8 consecutive elements [j0, j0+8): one or two 16-byte loads when
+// the row start is 16-byte aligned (`vec`) and the group is whole; element
+// loads otherwise, -inf past the end of the row.
+template <int DT>
+__device__ __forceinline__ void load_group(const void* row, int64_t j0, int64_t V, bool vec, Raw8<DT>& r) {
+    if (vec && j0 + kLaneElems <= V) {
+        load_raw8<DT>(r, static_cast<const char*>(row) + j0 * ElemT<DT>::kBytes);
+        return;
+    }
+    uint32_t h[kLaneElems];
+    if constexpr (DT == DT_BF16) {
+        const uint16_t* p = static_cast<const uint16_t*>(row);
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) h[e] = (j0 + e < V) ? uint32_t(p[j0 + e]) : 0xFF80u;
+        r.w[0] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    } else {
+        const uint32_t* p = static_cast<const uint32_t*>(row);
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) h[e] = (j0 + e < V) ? p[j0 + e] : 0xFF800000u;
+        r.w[0] = make_uint4(h[0], h[1], h[2], h[3]);
+        r.w[1] = make_uint4(h[4], h[5], h[6], h[7]);
+    }
+}
+
+// Probabilities p = 2^(z*c - mc) / Z of one row (fp32).
+template <int DT>
+struct ProbRow {
+    const void* row;
+    float c, nmc, invZ;
+    bool vec;
+    __device__ void init(const void* r, float c_, const RowStats& st) {
+        row = r; c = c_; nmc = -st.mc; invZ = float(1.0 / st.Z);
+        vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0;
+    }
+    __device__ __forceinline__ void probs(const Raw8<DT>& raw, float p[kLaneElems]) const {
+        float z[kLaneElems];
+        unpack8<DT>(raw, z);
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(z[e], c, nmc)) * invZ;
+    }
+};
+
+// Weights p of one row (the bonus after every draft was accepted, a leaf).
+template <int DT>
+struct TargetWeights {
+    struct Raw { Raw8<DT> p; };
+    ProbRow<DT> p;
+    int64_t V;
+    __device__ __forceinline__ void load(int64_t j0, Raw& r) const { load_group<DT>(p.row, j0, V, p.vec, r.p); }
+    __device__ __forceinline__ void weights(const Raw& r, float w[kLaneElems]) const { p.probs(r.p, w); }
+};
+
+// Weights max(p - coef * q, 0): the chain residual (coef = 1) and the MSS
+// residual after rejections (coef = c_j of the tree kernel's recurrence).
+template <int DT>
+struct ResidualWeights {
+    struct Raw { Raw8<DT> p, q; };
+    ProbRow<DT> p, q;
+    float coef;
+    int64_t V;
+    __device__ __forceinline__ void load(int64_t j0, Raw& r) const {
+        load_group<DT>(p.row, j0, V, p.vec, r.p);
+        load_group<DT>(q.row, j0, V, q.vec, r.q);
+    }
+    __device__ __forceinline__ void weights(const Raw& r, float w[kLaneElems]) const {
+        float a[kLaneElems], b[kLaneElems];
+        p.probs(r.p, a);
+        q.probs(r.q, b);
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) w[e] = fmaxf(fmaf(-coef, b[e], a[e]), 0.0f);
+    }
+};
+
+// Pass A: per-tile sums of the weights into `tile_sum` (fp32) and their total
+// (fp64). Every wave keeps kTilesInFlight tiles' loads in flight.
+template <class WFn>
+__device__ double weight_tiles(const WFn& f, int64_t V, float* tile_sum) {
+    const int ntiles = int((V + kTileElems - 1) / kTileElems);
+    for (int t0 = wave_id() * kTilesInFlight; t0 < ntiles; t0 += kWaves * kTilesInFlight) {
+        typename WFn::Raw raw[kTilesInFlight];
+#pragma unroll
+        for (int u = 0; u < kTilesInFlight; ++u)
+            f.load(int64_t(t0 + u) * kTileElems + lane_id() * kLaneElems, raw[u]);
+#pragma unroll
+        for (int u = 0; u < kTilesInFlight; ++u) {
+            float w[kLaneElems];
+            f.weights(raw[u], w);
+            const float ls = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
+            const float ts = wave_sum(ls);
+            if (lane_id() == 0 && t0 + u < ntiles) tile_sum[t0 + u] = ts;
+        }
+    }
+    __syncthreads();
+    __shared__ double s_total;
+    if (wave_id() == 0) {
+        double ps = 0.0;
+        for (int t = lane_id(); t < ntiles; t += kWaveSize) ps += tile_sum[t];
+        ps = wave_sum(ps);
+        if (lane_id() == 0) s_total = ps;
+    }
+    __syncthreads();
+    return s_total;
+}
+
+// Pass B: given the tile sums of pass A, the smallest j with S_j >= v * W.
+// Returns -1 when the total is 0.
+template <class WFn>
+__device__ int32_t sample_from_tiles(const WFn& f, int64_t V, float v, const float* tile_sum) {
+    const int ntiles = int((V + kTileElems - 1) / kTileElems);
+    const int lane = lane_id();
+    __shared__ int32_t s_tile;
+    __shared__ double s_tin;
+    __shared__ int32_t s_idx;
+    if (wave_id() == 0) {
+        const int seg = (ntiles + kWaveSize - 1) / kWaveSize;
+        const int t0 = lane * seg;
+        const int t1 = min(ntiles, t0 + seg);
+        double ps = 0.0;
+        for (int t = t0; t < t1; ++t) ps += tile_sum[t];
+        const double incl = wave_inclusive_scan(ps);
+        const double W = __shfl(incl, kWaveSize - 1);
+        double excl = __shfl_up(incl, 1);
+        if (lane == 0) excl = 0.0;
+        const double target = double(v) * W;
+        const uint64_t m = __ballot(W > 0.0 && incl >= target);
+        int tile = -1;
+        double tin = 0.0;
+        if (m != 0) {
+            const int L = __builtin_ctzll(m);
+            if (lane == L) {
+                double acc = excl;
+                for (int t = t0; t < t1; ++t) {
+                    const float ts = tile_sum[t];
+                    const double nx = acc + double(ts);
+                    if (ts > 0.0f && nx >= target) { tile = t; tin = target - acc; break; }
+                    acc = nx;
+                }
+                if (tile < 0) {  // rounding left v*W past this segment: take its last positive tile
+                    for (int t = t1 - 1; t >= t0; --t)
+                        if (tile_sum[t] > 0.0f) { tile = t; tin = double(tile_sum[t]); break; }
+                }
+            }
+            tile = __shfl(tile, L);
+            tin = __shfl(tin, L);
+        }
+        if (lane == 0) { s_tile = tile; s_tin = tin; }
+    }
+    __syncthreads();
+    const int tile = s_tile;
+    if (wave_id() == 0 && tile >= 0) {
+        typename WFn::Raw raw;
+        f.load(int64_t(tile) * kTileElems + lane * kLaneElems, raw);
+        float w[kLaneElems];
+        f.weights(raw, w);
+        double ls = 0.0;
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) ls += double(w[e]);
+        const double incl = wave_inclusive_scan(ls);
+        double acc = __shfl_up(incl, 1);
+        if (lane == 0) acc = 0.0;
+        const double tin = s_tin;
+        int fe = -1, le = -1;
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) {
+            acc += double(w[e]);
+            if (fe < 0 && w[e] > 0.0f && acc >= tin) fe = e;
+            if (w[e] > 0.0f) le = e;
+        }
+        const uint64_t m = __ballot(fe >= 0);
+        int32_t idx;
+        if (m != 0) {
+            const int L = __builtin_ctzll(m);
+            idx = tile * kTileElems + L * kLaneElems + __shfl(fe, L);
+        } else {  // rounding: v*W fell past the tile's scanned total; take its last positive element
+            const uint64_t m2 = __ballot(le >= 0);
+            const int L = 63 - __builtin_clzll(m2);
+            idx = tile * kTileElems + L * kLaneElems + __shfl(le, L);
+        }
+        if (lane == 0) s_idx = idx;
+    }
+    __syncthreads();
+    return tile >= 0 ? s_idx : -1;
+}
+
+}  // namespace specv

@@ -1,0 +1,79 @@
+"""GPU parity of the SSD top-F bonus candidates: bit-exact ids (and logits)
+against the oracle, including heavy ties, -0/+0, -inf and every F bucket."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_common import log, run_topf_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from speculative_sampling_verification_04_amd import binding
+    binding.load_library()
+
+
+def check(draft, tokens, F, dtype, rows_to_check=None, name=""):
+    B, R, V = draft.shape
+    if dtype == "bf16":          # the oracle sees exactly the values the GPU reads
+        draft = workloads.round_to_bf16(draft)
+    d = to_dev(draft, dtype)
+    t = torch.from_numpy(np.ascontiguousarray(tokens, np.int32)).cuda() if tokens is not None else None
+    log(f"topf {name} B={B} rows={R} V={V} F={F} {dtype}")
+    ids, vals = run_topf_gpu(d, t, F)
+    seqs = range(B) if rows_to_check is None else rows_to_check
+    for b in seqs:
+        ref_ids, ref_vals = oracle.topf.bonus_topf_batch(draft[b:b + 1].astype(np.float64),
+                                                         None if tokens is None else tokens[b:b + 1], F)
+        np.testing.assert_array_equal(ids[b], ref_ids[0], err_msg=f"{name}: sequence {b}")
+        np.testing.assert_array_equal(vals[b].astype(np.float64), ref_vals[0], err_msg=f"{name}: logits {b}")
+
+
+def test_headline_top4():
+    w = workloads.make_workload("v128256_bf16_b256_g8")
+    sample = list(range(0, 256, 5))      # 52 sequences x 9 rows through the oracle
+    check(w.draft, w.draft_tokens, w.F, "bf16", sample, "headline")
+
+
+@pytest.mark.parametrize("F", [1, 2, 3, 4, 7, 8, 15, 16, 31])
+def test_every_bucket_with_ties(F):
+    rng = np.random.default_rng(F)
+    B, gamma, V = 6, 3, 5000
+    pool = np.array([-np.inf, -2.0, -0.0, 0.0, 0.5, 1.0, 1.5, 2.0], np.float32)
+    draft = rng.choice(pool, size=(B, gamma + 1, V)).astype(np.float32)
+    draft[0] = rng.normal(0, 3, (gamma + 1, V)).astype(np.float32)
+    draft[1] = np.float32(1.0)                           # all equal
+    tokens = rng.integers(0, 20, (B, gamma)).astype(np.int32)
+    check(draft, tokens, F, "bf16", name=f"ties F={F}")
+    check(draft, None, F, "f32", name=f"ties no-exclusion F={F}")
+
+
+@pytest.mark.parametrize("V", [2, 5, 9, 100, 4097, 152064])
+def test_vocab_sizes(V):
+    rng = np.random.default_rng(V)
+    B, gamma = 3, 2
+    draft = workloads.round_to_bf16(rng.normal(0, 4, (B, gamma + 1, V)).astype(np.float32))
+    tokens = np.array([[int(np.argmax(draft[b, k])) for k in range(gamma)] for b in range(B)], np.int32)
+    F = min(4, V - 1)
+    check(draft, tokens, F, "bf16", name=f"V={V}")
+
+
+def test_unaligned_rows():
+    rng = np.random.default_rng(5)
+    B, gamma, V = 3, 2, 999
+    draft = rng.normal(0, 1, (B, gamma + 1, V)).round(1).astype(np.float32)
+    tokens = rng.integers(0, V, (B, gamma)).astype(np.int32)
+    big = torch.zeros((B, gamma + 1, V + 5), dtype=torch.bfloat16, device="cuda")
+    view = big[:, :, 3:3 + V]
+    view.copy_(to_dev(draft, "bf16"))
+    from speculative_sampling_verification_04_amd import binding
+    ids, vals = binding.bonus_topk(view, torch.from_numpy(tokens).cuda(), 5)
+    torch.cuda.synchronize()
+    ref_ids, _ = oracle.topf.bonus_topf_batch(workloads.round_to_bf16(draft).astype(np.float64), tokens, 5)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)

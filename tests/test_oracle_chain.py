@@ -292,3 +292,13 @@ def test_near_tie_flag():
     r = verify_sequence(np.stack([lt, lt]), np.stack([ld]), [0], 1.0,
                         [ratio + 5e-6], 0.5)
     assert not r.near_tie
+
+
+def test_out_of_range_token_is_rejected():
+    target = np.zeros((3, 4))
+    draft = np.zeros((2, 4))
+    for bad in (4, 9, -1):
+        r = verify_sequence(target, draft, [1, bad], 1.0, [0.5, 2.0 ** -24], 0.5)
+        assert r.k == 1 and r.probs[1].tolist() == [0.0, 0.0]
+        g = verify_sequence(target, draft, [0, bad], 0.0, [0.5, 0.5], 0.5)
+        assert g.k == 1
