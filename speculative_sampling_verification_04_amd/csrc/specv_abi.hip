@@ -7,7 +7,7 @@
 
 #include <string>
 
-#include "../../include/specv.h"
+#include "specv.h"
 #include "specv_device.hpp"
 #include "specv_launch.hpp"
 

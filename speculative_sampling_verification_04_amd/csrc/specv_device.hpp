@@ -8,8 +8,7 @@
 //    every term is evaluated as exp2(fma(z, c, -mc)), so all terms of a lane
 //    share one reference and rescaling is exact up to one rounding.
 //  * ArgmaxAcc: the greedy (one-hot) token, lowest index on ties [sec. 2.7].
-//  * TopKAcc: the K largest (logit, -index) keys, for the SSD bonus-token
-//    candidates [Speculative Speculative Decoding, sec. 4.1.1].
+// (The top-K selection for the SSD bonus candidates is in specv_topk.hpp.)
 // Lane results are merged within the wave by xor-shuffles and across the
 // workgroup's waves through LDS.
 #pragma once
@@ -83,22 +82,32 @@ __device__ __forceinline__ float max8(const float v[kLaneElems]) {
 // the body is read in steps of kLaneElems elements per lane, U steps in flight
 // per lane per iteration (lane t takes steps t, t + kThreads, ...), and the
 // remainder element by element; otherwise every element is read singly.
-// The loop bound is uniform over the workgroup, so every lane calls the
-// visitor's block() on every iteration (visitors may use wave-wide operations);
-// steps past the end arrive as -inf with valid = false.
+// Both loop bounds are uniform over the workgroup, so every lane calls the
+// visitor's block() and one() on every iteration (visitors may use wave-wide
+// operations); steps or elements past the end arrive as -inf with valid = false.
 template <int DT, int U, class Acc>
 __device__ __forceinline__ void stream_chunk(const void* row, int64_t lo, int64_t hi, Acc& acc) {
     constexpr int kB = ElemT<DT>::kBytes;
+    constexpr int64_t kStride = int64_t(kThreads) * U;
     const char* base = static_cast<const char*>(row) + lo * kB;
     const int64_t n = hi - lo;
     const bool aligned = (reinterpret_cast<uintptr_t>(base) & 15u) == 0;
     const int64_t nstep = aligned ? n / kLaneElems : 0;
-    for (int64_t base0 = 0; base0 < nstep; base0 += int64_t(kThreads) * U) {
-        Raw8<DT> raw[U];
+    // Software pipelined: the next iteration's U loads are issued before the
+    // current iteration's data is processed.
+    Raw8<DT> cur[U], nxt[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t s = base0 + threadIdx.x + int64_t(u) * kThreads;
-            if (s < nstep) load_raw8<DT>(raw[u], base + s * (kLaneElems * kB));
+    for (int u = 0; u < U; ++u) {
+        const int64_t s = threadIdx.x + int64_t(u) * kThreads;
+        if (s < nstep) load_raw8<DT>(cur[u], base + s * (kLaneElems * kB));
+    }
+    for (int64_t base0 = 0; base0 < nstep; base0 += kStride) {
+        if (base0 + kStride < nstep) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t s = base0 + kStride + threadIdx.x + int64_t(u) * kThreads;
+                if (s < nstep) load_raw8<DT>(nxt[u], base + s * (kLaneElems * kB));
+            }
         }
         float v[U][kLaneElems];
         int64_t idx[U];
@@ -109,16 +118,21 @@ __device__ __forceinline__ void stream_chunk(const void* row, int64_t lo, int64_
             valid[u] = s < nstep;
             idx[u] = lo + s * kLaneElems;
             if (valid[u]) {
-                unpack8<DT>(raw[u], v[u]);
+                unpack8<DT>(cur[u], v[u]);
             } else {
 #pragma unroll
                 for (int e = 0; e < kLaneElems; ++e) v[u][e] = -INFINITY;
             }
         }
         acc.template block<U>(v, idx, valid);
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     }
-    for (int64_t j = nstep * kLaneElems + threadIdx.x; j < n; j += kThreads)
-        acc.one(load_elem<DT>(row, lo + j), lo + j);
+    for (int64_t j0 = nstep * kLaneElems; j0 < n; j0 += kThreads) {
+        const int64_t j = j0 + threadIdx.x;
+        const bool ok = j < n;
+        acc.one(ok ? load_elem<DT>(row, lo + j) : -INFINITY, lo + j, ok);
+    }
 }
 
 // ------------------------------------------------------------------ Philox
@@ -299,7 +313,8 @@ struct SoftmaxAcc {
         s += double(tot);
     }
 
-    __device__ __forceinline__ void one(float z, int64_t) {
+    __device__ __forceinline__ void one(float z, int64_t, bool ok) {
+        if (!ok) return;
         rebase(z);
         if (m != -INFINITY) s += double(__builtin_amdgcn_exp2f(fmaf(z, c, -mc)));
     }
@@ -326,8 +341,8 @@ struct ArgmaxAcc {
         }
     }
 
-    __device__ __forceinline__ void one(float z, int64_t j) {
-        if (z > best || idx < 0) { best = z; idx = int32_t(j); }
+    __device__ __forceinline__ void one(float z, int64_t j, bool ok) {
+        if (ok && (z > best || idx < 0)) { best = z; idx = int32_t(j); }
     }
 };
 
@@ -347,55 +362,5 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
 __device__ __forceinline__ uint64_t full_key(float v, int64_t j) {
     return (uint64_t(logit_key(v)) << 32) | uint64_t(~uint32_t(j));
 }
-
-// The K largest keys seen by one lane, sorted descending. A wave-wide
-// threshold (the largest K-th key over the wave's lanes, logit part only)
-// filters elements: anything below it cannot be among the row's K largest.
-template <int K>
-struct TopKAcc {
-    uint64_t a[K];
-    uint32_t theta = 0;          // logit key of the wave threshold
-    float theta_val = -INFINITY; // its logit
-
-    __device__ TopKAcc() {
-#pragma unroll
-        for (int i = 0; i < K; ++i) a[i] = 0;
-    }
-
-    __device__ __forceinline__ void insert(uint64_t key) {
-#pragma unroll
-        for (int i = K - 1; i > 0; --i) {
-            const uint64_t hi = a[i - 1];
-            a[i] = key > hi ? hi : (key > a[i] ? key : a[i]);
-        }
-        a[0] = key > a[0] ? key : a[0];
-    }
-
-    __device__ __forceinline__ void consider(float v, int64_t j) {
-        if (logit_key(v) >= theta) {
-            const uint64_t key = full_key(v, j);
-            if (key > a[K - 1]) insert(key);
-        }
-    }
-
-    __device__ __forceinline__ void refresh_threshold() {
-        theta = wave_max_u32(uint32_t(a[K - 1] >> 32));
-        theta_val = theta == 0 ? -INFINITY : key_logit(theta);
-    }
-
-    template <int U>
-    __device__ __forceinline__ void block(const float (&v)[U][kLaneElems], const int64_t* base, const bool* valid) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (valid[u] && max8(v[u]) >= theta_val) {
-#pragma unroll
-                for (int e = 0; e < kLaneElems; ++e) consider(v[u][e], base[u] + e);
-            }
-        }
-        refresh_threshold();
-    }
-
-    __device__ __forceinline__ void one(float z, int64_t j) { consider(z, j); }
-};
 
 }  // namespace specv

@@ -16,7 +16,7 @@
 
 namespace specv {
 
-constexpr int kTilesInFlight = 4;      // residual pass: tiles per wave per iteration
+constexpr int kTilesInFlight = 8;      // residual pass: tiles per wave per iteration
 constexpr int kMaxSpin = 1 << 24;      // bound on the resolver's wait (about a second)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWaveSize - 1); }
@@ -45,6 +45,48 @@ __device__ __forceinline__ void block_merge_argmax(float& v, int32_t& i) {
     for (int w = 1; w < kWaves; ++w)
         if (argmax_better(sv[w], si[w], v, i)) { v = sv[w]; i = si[w]; }
     __syncthreads();
+}
+
+constexpr int kMaxOrderedBatch = 4096;
+
+// Dispatch order of sequences: those with T > 0 first, then the greedy ones,
+// each group by increasing index (identity when B > kMaxOrderedBatch). A
+// sequence's last workgroup resolves it, and only T > 0 sequences re-read a
+// row to draw the bonus, so this keeps the cheap resolves at the end of the
+// grid. Returns the sequence handled by dispatch slot s (whole workgroup).
+__device__ int sequence_for_slot(const float* temperature, int B, int s) {
+    if (B > kMaxOrderedBatch) return s;
+    __shared__ uint64_t masks[kMaxOrderedBatch / kWaveSize];
+    __shared__ int s_b;
+    const int nm = (B + kWaveSize - 1) / kWaveSize;
+    for (int c = wave_id(); c < nm; c += kWaves) {
+        const int i = c * kWaveSize + lane_id();
+        const uint64_t m = __ballot(i < B && temperature[i] > 0.0f);
+        if (lane_id() == 0) masks[c] = m;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int total = 0;
+        for (int c = 0; c < nm; ++c) total += __popcll(masks[c]);
+        const bool sampled = s < total;
+        int k = sampled ? s : s - total;
+        int b = s;
+        for (int c = 0; c < nm; ++c) {
+            uint64_t m = sampled ? masks[c] : ~masks[c];
+            const int valid = min(kWaveSize, B - c * kWaveSize);
+            if (valid < kWaveSize) m &= (1ull << valid) - 1ull;
+            const int cnt = __popcll(m);
+            if (k < cnt) {
+                for (int i = 0; i < k; ++i) m &= m - 1ull;
+                b = c * kWaveSize + __builtin_ctzll(m);
+                break;
+            }
+            k -= cnt;
+        }
+        s_b = b;
+    }
+    __syncthreads();
+    return s_b;
 }
 
 // Waits until the n slots are all published (wave 0 polls with agent-scope

@@ -53,14 +53,13 @@ __device__ int child_with_token(const int32_t* par, const int32_t* tok, int N, i
 }
 
 template <int DT>
-__device__ void tree_resolve(const TreeArgs& a, int b, float T) {
+__device__ void tree_resolve(const TreeArgs& a, int b, float T, uint64_t* slots) {
     constexpr int esz = ElemT<DT>::kBytes;
     const int N = a.N;
     const bool greedy = !(T > 0.0f);
     const float c = greedy ? 0.0f : log2e_over(T);
     const int32_t* par = a.parent + int64_t(b) * N;
     const int32_t* tok = a.tokens + int64_t(b) * N;
-    uint64_t* slots = a.slots + int64_t(b) * 2 * N * a.S;
     const float v = greedy ? 0.0f : stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(N));
 
     __shared__ float tile_sum[kMaxTiles];
@@ -205,7 +204,8 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(TreeArgs a) {
     const int chunk = int(g % a.S);
     const int64_t task = g / a.S;
     const int slot = int(task % (2 * N));
-    const int b = int(task / (2 * N));
+    const int tidx = int(task / (2 * N));                 // dispatch slot of the tree
+    const int b = sequence_for_slot(a.temperature, a.B, tidx);
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
     const bool draft_row = slot >= N;
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(TreeArgs a) {
     }
     if (threadIdx.x == 0) publish(a.slots + g, word);
     // The tree's last workgroup walks it.
-    if (slot == 2 * N - 1 && chunk == a.S - 1) tree_resolve<DT>(a, b, T);
+    if (slot == 2 * N - 1 && chunk == a.S - 1) tree_resolve<DT>(a, b, T, a.slots + int64_t(tidx) * 2 * N * a.S);
 }
 
 }  // namespace

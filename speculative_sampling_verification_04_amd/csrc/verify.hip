@@ -2,7 +2,8 @@
 // sec. 2.2, 2.7, 3.1; Speculative Decoding (dl-note), sec. 2.2-2.3 and
 // Appendix "Implementation Details"].
 //
-// One launch. Workgroup g streams one chunk of one row of one sequence:
+// One launch. Sequences are taken T > 0 first (sequence_for_slot), and
+// workgroup g streams one chunk of one row of one sequence:
 // target rows 0..gamma and (for T > 0) draft rows 0..gamma-1, each read once
 // from HBM with 16-byte loads, and publishes the chunk's statistics (online
 // max and sum of 2^(z*c - mc), or the greedy argmax) as one 64-bit atomic
@@ -28,13 +29,12 @@ __device__ __forceinline__ const void* row_ptr(const RowView& v, int esz, int64_
 __device__ __forceinline__ float log2e_over(float T) { return float(1.4426950408889634 / double(T)); }
 
 template <int DT>
-__device__ void chain_resolve(const ChainArgs& a, int b, float T) {
+__device__ void chain_resolve(const ChainArgs& a, int b, float T, uint64_t* slots) {
     constexpr int esz = ElemT<DT>::kBytes;
     const int gamma = a.gamma;
     const int R = 2 * gamma + 1;
     const bool greedy = !(T > 0.0f);
     const float c = greedy ? 0.0f : log2e_over(T);
-    uint64_t* slots = a.slots + int64_t(b) * R * a.S;
 
     __shared__ RowStats st[2 * 64 + 1];
     __shared__ int32_t s_k;
@@ -140,7 +140,8 @@ __global__ __launch_bounds__(kThreads) void chain_verify_kernel(ChainArgs a) {
     const int chunk = int(g % a.S);
     const int64_t task = g / a.S;
     const int slot = int(task % R);
-    const int b = int(task / R);
+    const int sidx = int(task / R);                      // dispatch slot of the sequence
+    const int b = sequence_for_slot(a.temperature, a.B, sidx);
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
     const bool draft_row = slot > a.gamma;
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void chain_verify_kernel(ChainArgs a) {
     }
     if (threadIdx.x == 0) publish(a.slots + g, word);
     // The sequence's last workgroup resolves it.
-    if (slot == R - 1 && chunk == a.S - 1) chain_resolve<DT>(a, b, T);
+    if (slot == R - 1 && chunk == a.S - 1) chain_resolve<DT>(a, b, T, a.slots + int64_t(sidx) * R * a.S);
 }
 
 }  // namespace
