@@ -4,14 +4,16 @@
 
 One step = the whole hot path on the headline workload (B = 256 sequences,
 gamma = 8 draft tokens, V = 128256 bf16 logits, half the sequences greedy and
-half at T = 1): specv_verify (accept prefix + bonus token) followed by
-specv_bonus_topk (F = 4 SSD bonus candidates per position). Inputs are seeded
-synthetic logits already resident in HBM when timing starts.
+half at T = 1): verification (accept prefix + bonus token) and the F = 4 SSD
+bonus candidates per position, as one specv_verify_topk call (one kernel that
+reads every target and draft row once). Inputs are seeded synthetic logits
+already resident in HBM when timing starts.
 
-Prints one JSON line: verified rows/s (B * (gamma + 1) per step), the verify
+Prints one JSON line: verified rows/s (B * (gamma + 1) per step), the step
 kernel's roofline (algorithmic HBM bytes / its average duration, measured with
-HIP events on the launch stream), and the oracle timed on the host cores on a
-bounded sample of the same workload.
+HIP events on the launch stream), the separate specv_verify and
+specv_bonus_topk kernels for reference, and the oracle timed on the host cores
+on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
@@ -34,15 +36,16 @@ CSRC = os.path.join(ROOT, "speculative_sampling_verification_04_amd", "csrc")
 
 
 def algorithmic_bytes(w):
-    """Bytes each call must read at least once: every target row; a draft row
-    only for T > 0 sequences (greedy rows never read the draft) -- verify;
-    every draft row -- top-F. Token ids, temperatures and outputs are added."""
+    """Logit bytes each call must read at least once (rows of V bf16):
+    verify: every target row, and a draft row only for T > 0 sequences
+    (greedy rows never read the draft); top-F: every draft row; the fused
+    step: every target row and every draft row."""
     row = w.V * 2
     n_sampled = int((w.temperature > 0).sum())
-    small = w.B * (w.gamma * 4 + 4) + w.B * (w.gamma + 1) * 4 + w.B * w.gamma * 8 + w.B * 8
     verify = w.B * (w.gamma + 1) * row + n_sampled * w.gamma * row
     topf = w.B * (w.gamma + 1) * row
-    return verify, verify + small, topf
+    step = 2 * w.B * (w.gamma + 1) * row
+    return verify, topf, step
 
 
 def kernel_source_hash():
@@ -125,42 +128,53 @@ def main():
     out = dict(tokens=torch.empty((B, gamma + 1), dtype=torch.int32, device=dev),
                num_accepted=torch.empty((B,), dtype=torch.int32, device=dev),
                probs=torch.empty((B, gamma, 2), dtype=torch.float32, device=dev),
-               bonus_mass=torch.empty((B,), dtype=torch.float32, device=dev))
-    topk = (torch.empty((B, gamma + 1, F), dtype=torch.int32, device=dev),
-            torch.empty((B, gamma + 1, F), dtype=torch.float32, device=dev))
-    ws = torch.zeros(binding.verify_workspace_bytes(B, gamma, w.V), dtype=torch.uint8, device=dev)
+               bonus_mass=torch.empty((B,), dtype=torch.float32, device=dev),
+               topk=torch.empty((B, gamma + 1, F), dtype=torch.int32, device=dev),
+               topk_logits=torch.empty((B, gamma + 1, F), dtype=torch.float32, device=dev))
+    ws = torch.zeros(binding.verify_topk_workspace_bytes(B, gamma, w.V), dtype=torch.uint8, device=dev)
 
-    def step(i, ev=None):
-        if ev is not None:
-            ev[0].record()
-        binding.verify(target, draft, tokens, temp, w.seed, i, workspace=ws, out=out)
-        if ev is not None:
-            ev[1].record()
-        binding.bonus_topk(draft, tokens, F, out=topk)
-        if ev is not None:
-            ev[2].record()
+    def step(i):
+        binding.verify_topk(target, draft, tokens, temp, F, w.seed, i, workspace=ws, out=out)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        events[i][0].record()
+        step(args.warmup + i)
+        events[i][1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_kernel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    mean_accepted = float(out["num_accepted"].float().mean().item())
 
-    verify_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    topf_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    # Reference: the two entry points run separately (not part of the step).
+    def timed(fn, n=20):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for i in range(3):
+            fn(i)
+        for i in range(n):
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+    vws = torch.zeros(binding.verify_workspace_bytes(B, gamma, w.V), dtype=torch.uint8, device=dev)
+    vout = {k: out[k] for k in ("tokens", "num_accepted", "probs", "bonus_mass")}
+    verify_ms = timed(lambda i: binding.verify(target, draft, tokens, temp, w.seed, i, workspace=vws, out=vout))
+    topf_ms = timed(lambda i: binding.bonus_topk(draft, tokens, F, out=(out["topk"], out["topk_logits"])))
+
     ms_per_step = elapsed * 1e3 / args.steps
     rows = B * (gamma + 1)
-    verify_bytes, verify_bytes_io, topf_bytes = algorithmic_bytes(w)
-    achieved = verify_bytes / (verify_ms * 1e-3) / 1e9
-    topf_gbps = topf_bytes / (topf_ms * 1e-3) / 1e9
-    step_gbps = (verify_bytes + topf_bytes) / (ms_per_step * 1e-3) / 1e9
-    traffic = measured_traffic("chain_verify_kernel")
+    verify_bytes, topf_bytes, step_bytes = algorithmic_bytes(w)
+    achieved = step_bytes / (step_kernel_ms * 1e-3) / 1e9
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    traffic = measured_traffic("verify_topf_kernel")
 
     line = {
         "metric": METRIC,
@@ -177,16 +191,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "B": B, "gamma": gamma, "V": w.V, "logits": "bf16",
                    "F": F, "greedy_sequences": int((w.temperature == 0).sum()),
-                   "step": "specv_verify + specv_bonus_topk", "parallelism": "none"},
+                   "step": "specv_verify_topk", "parallelism": "none"},
         "hbm_gbps": step_gbps,
         "hbm_pct_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
-        "roofline": {"bound": "hbm", "kernel": "chain_verify_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "verify_topf_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic, "algorithmic_bytes": verify_bytes, "avg_ms": verify_ms},
-        "roofline_topf": {"bound": "hbm", "kernel": "topf_kernel", "achieved": topf_gbps,
-                          "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": topf_gbps / HBM_PEAK_GBPS,
-                          "algorithmic_bytes": topf_bytes, "avg_ms": topf_ms},
-        "mean_accepted": float(out["num_accepted"].float().mean().item()),
+                     "traffic": traffic, "algorithmic_bytes": step_bytes, "avg_ms": step_kernel_ms},
+        "separate_kernels": {
+            "chain_verify_kernel": {"avg_ms": verify_ms, "algorithmic_bytes": verify_bytes,
+                                    "gbps": verify_bytes / (verify_ms * 1e-3) / 1e9},
+            "topf_kernel": {"avg_ms": topf_ms, "algorithmic_bytes": topf_bytes,
+                            "gbps": topf_bytes / (topf_ms * 1e-3) / 1e9}},
+        "mean_accepted": mean_accepted,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

@@ -139,6 +139,29 @@ specv_status specv_bonus_topk(specv_logits draft, const int32_t* draft_tokens,
                               int32_t F, int32_t* out_topk,
                               float* out_topk_logits, void* stream);
 
+/* Bytes of workspace specv_verify_topk needs for (batch, gamma, vocab). */
+specv_status specv_verify_topk_workspace_size(int32_t batch, int32_t gamma,
+                                              int32_t vocab, size_t* bytes);
+
+/*
+ * specv_verify and specv_bonus_topk(draft, draft_tokens, ...) in one call,
+ * with the same outputs as the two calls. When every row fits one workgroup
+ * (large batches) a single kernel streams every draft row once for both the
+ * softmax statistics and the top-F candidates; otherwise the two kernels run
+ * in turn. draft must have gamma + 1 rows per sequence. Arguments and outputs
+ * as for specv_verify and specv_bonus_topk (draft_tokens is required here and
+ * serves both); workspace as for specv_verify, sized by
+ * specv_verify_topk_workspace_size.
+ */
+specv_status specv_verify_topk(specv_logits target, specv_logits draft,
+                               const int32_t* draft_tokens, const float* temperature,
+                               int32_t batch, int32_t gamma, int32_t vocab, int32_t F,
+                               uint64_t seed, uint64_t offset,
+                               int32_t* out_tokens, int32_t* out_num_accepted,
+                               float* out_probs, float* out_bonus_mass,
+                               int32_t* out_topk, float* out_topk_logits,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace specv_tree_verify needs for (batch, nodes, vocab). */
 specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes,
                                               int32_t vocab, size_t* bytes);

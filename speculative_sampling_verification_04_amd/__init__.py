@@ -4,4 +4,4 @@ The work runs in hand-written HIP kernels behind the C ABI of libspecv.so
 (include/specv.h); `binding` marshals torch tensors into that ABI.
 """
 from .binding import (SpecvError, bonus_topk, load_library, tree_verify,  # noqa: F401
-                      uniforms, verify, version)
+                      uniforms, verify, verify_topk, version)

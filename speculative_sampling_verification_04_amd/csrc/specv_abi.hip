@@ -86,6 +86,21 @@ specv_status check_chain_sizes(int32_t batch, int32_t gamma, int32_t vocab) {
     return SPECV_OK;
 }
 
+// The fused kernel runs when every row fits one workgroup; its workspace has
+// 2*gamma + 2 slots per sequence. Otherwise the verify and top-F kernels run.
+bool fused_fits(int64_t batch, int64_t gamma, int64_t vocab) {
+    int32_t S;
+    int64_t chunk;
+    choose_split(batch * (2 * gamma + 2), vocab, &S, &chunk);
+    return S == 1;
+}
+
+size_t verify_topk_bytes(int64_t batch, int64_t gamma, int64_t vocab) {
+    const size_t plain = layout_for(batch, 2 * gamma + 1, vocab).total();
+    const size_t fused = round_up(size_t(batch) * (2 * gamma + 2) * sizeof(uint64_t));
+    return plain > fused ? plain : fused;
+}
+
 specv_status check_tree_sizes(int32_t batch, int32_t nodes, int32_t vocab) {
     if (batch < 1) return fail(SPECV_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
     if (nodes < 1 || nodes > SPECV_MAX_TREE_NODES)
@@ -130,6 +145,14 @@ specv_status specv_verify_workspace_size(int32_t batch, int32_t gamma, int32_t v
     return ok();
 }
 
+specv_status specv_verify_topk_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, size_t* bytes) {
+    if (bytes == nullptr) return fail(SPECV_ERR_INVALID_ARG, "bytes is NULL");
+    specv_status st = check_chain_sizes(batch, gamma, vocab);
+    if (st != SPECV_OK) return st;
+    *bytes = verify_topk_bytes(batch, gamma, vocab);
+    return ok();
+}
+
 specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes, int32_t vocab, size_t* bytes) {
     if (bytes == nullptr) return fail(SPECV_ERR_INVALID_ARG, "bytes is NULL");
     specv_status st = check_tree_sizes(batch, nodes, vocab);
@@ -155,7 +178,7 @@ specv_status specv_verify(specv_logits target, specv_logits draft, const int32_t
     if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch (%lld workgroups)", (long long)grid);
     if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
 
-    ChainArgs a;
+    ChainArgs a{};
     a.target = view(target);
     a.draft = view(draft);
     a.tokens = draft_tokens;
@@ -175,6 +198,73 @@ specv_status specv_verify(specv_logits target, specv_logits draft, const int32_t
     const hipError_t e = launch_chain(a, target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32,
                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_verify launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+specv_status specv_verify_topk(specv_logits target, specv_logits draft, const int32_t* draft_tokens,
+                               const float* temperature, int32_t batch, int32_t gamma, int32_t vocab, int32_t F,
+                               uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_num_accepted,
+                               float* out_probs, float* out_bonus_mass, int32_t* out_topk, float* out_topk_logits,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    specv_status st = check_chain_sizes(batch, gamma, vocab);
+    if (st != SPECV_OK) return st;
+    if ((st = check_logits("target", target)) != SPECV_OK) return st;
+    if ((st = check_logits("draft", draft)) != SPECV_OK) return st;
+    if (target.dtype != draft.dtype)
+        return fail(SPECV_ERR_UNSUPPORTED, "target and draft must have the same dtype");
+    if (F < 1 || F > SPECV_MAX_TOPF || F > vocab - 1)
+        return fail(SPECV_ERR_INVALID_ARG, "F must be in [1, min(%d, vocab - 1)] (got %d, vocab %d)", SPECV_MAX_TOPF,
+                    F, vocab);
+    if (!draft_tokens || !temperature || !out_tokens || !out_num_accepted || !out_topk)
+        return fail(SPECV_ERR_INVALID_ARG,
+                    "draft_tokens, temperature, out_tokens, out_num_accepted and out_topk are required");
+    const bool fused = fused_fits(batch, gamma, vocab);
+    const Layout L = layout_for(batch, 2 * int64_t(gamma) + 1, vocab);
+    const int64_t grid = fused ? int64_t(batch) * (2 * gamma + 2) : int64_t(batch) * (2 * gamma + 1) * L.S;
+    if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch");
+    if ((st = check_workspace(workspace, workspace_bytes, verify_topk_bytes(batch, gamma, vocab))) != SPECV_OK)
+        return st;
+
+    ChainArgs a{};
+    a.target = view(target);
+    a.draft = view(draft);
+    a.tokens = draft_tokens;
+    a.temperature = temperature;
+    a.B = batch;
+    a.gamma = gamma;
+    a.V = vocab;
+    a.S = fused ? 1 : L.S;
+    a.chunk = fused ? int64_t(vocab) : L.chunk;
+    a.seed = seed;
+    a.offset = offset;
+    a.out_tokens = out_tokens;
+    a.out_nacc = out_num_accepted;
+    a.out_probs = out_probs;
+    a.out_mass = out_bonus_mass;
+    a.slots = static_cast<uint64_t*>(workspace);
+    a.F = F;
+    a.out_topk = out_topk;
+    a.out_topk_logits = out_topk_logits;
+    const int dt = target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32;
+    hipError_t e;
+    if (fused) {
+        e = launch_verify_topf(a, dt, static_cast<hipStream_t>(stream));
+    } else {
+        e = launch_chain(a, dt, static_cast<hipStream_t>(stream));
+        if (e == hipSuccess) {
+            TopFArgs t;
+            t.draft = view(draft);
+            t.tokens = draft_tokens;
+            t.B = batch;
+            t.gamma = gamma;
+            t.V = vocab;
+            t.F = F;
+            t.out_topk = out_topk;
+            t.out_logits = out_topk_logits;
+            e = launch_topf(t, dt, static_cast<hipStream_t>(stream));
+        }
+    }
+    if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_verify_topk launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -30,6 +30,10 @@ struct ChainArgs {
     float* out_probs;
     float* out_mass;
     uint64_t* slots;
+    // Fused top-F (verify_topf_kernel only).
+    int32_t F;
+    int32_t* out_topk;
+    float* out_topk_logits;
 };
 
 // Tree verification. Per tree there are 2N row tasks (target rows of every
@@ -73,6 +77,7 @@ inline void choose_split(int64_t row_tasks, int64_t V, int32_t* S, int64_t* chun
 }
 
 hipError_t launch_chain(const ChainArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_verify_topf(const ChainArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_tree(const TreeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_topf(const TopFArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_uniforms(uint64_t seed, uint64_t offset, int32_t tag, int32_t B,

@@ -16,7 +16,7 @@
 
 namespace specv {
 
-constexpr int kTilesInFlight = 8;      // residual pass: tiles per wave per iteration
+constexpr int kTilesInFlight = 4;      // residual pass: tiles per wave per iteration
 constexpr int kMaxSpin = 1 << 24;      // bound on the resolver's wait (about a second)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWaveSize - 1); }

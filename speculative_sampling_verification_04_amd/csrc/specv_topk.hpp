@@ -8,11 +8,12 @@
 // wave forms a lower bound theta on the K-th largest key seen so far: the
 // minimum, over K groups of lanes, of each group's largest lane maximum (K
 // distinct elements are >= theta). An 8-element group whose maximum reaches
-// theta is recorded as a candidate (its start index) in the wave's LDS list;
-// every other group cannot hold one of the K largest keys. When the list runs
-// full, and at the end of the chunk, it is compacted exactly: the K groups
-// with the largest maxima are kept and theta becomes the K-th of those maxima.
-// The K largest keys of the chunk then lie in the kept groups.
+// theta is recorded as a candidate (its start index and its largest key) in
+// the wave's LDS list; every other group cannot hold one of the K largest
+// keys. When the list runs full, and at the end of the chunk, it is compacted
+// exactly from LDS: the K groups with the largest maxima are kept and theta
+// becomes the K-th of those maxima. The K largest keys of the chunk then lie
+// in the kept groups.
 #pragma once
 
 #include <limits.h>
@@ -21,7 +22,7 @@
 
 namespace specv {
 
-constexpr int kCandCap = 512;                  // candidate groups per wave
+constexpr int kCandCap = 256;                  // candidate groups per wave
 constexpr int32_t kSingle = 0x40000000;       // candidate holds one element, not 8
 
 __device__ __forceinline__ int lanes_below(uint64_t m) {
@@ -31,17 +32,6 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
-// Largest key of a candidate's elements (8 from its start, or one), < hi.
-template <int DT>
-__device__ uint64_t candidate_max_key(const void* row, int32_t ent, int64_t hi) {
-    const int64_t j0 = ent & ~kSingle;
-    const int n = (ent & kSingle) ? 1 : kLaneElems;
-    uint64_t best = 0;
-    for (int e = 0; e < n; ++e)
-        if (j0 + e < hi) best = umax64(best, full_key(load_elem<DT>(row, j0 + e), j0 + e));
-    return best;
-}
-
 template <int DT, int K>
 struct TopKAcc {
     static_assert(K >= 1 && K <= 32 && (K & (K - 1)) == 0, "K is a power of two <= 32");
@@ -49,7 +39,8 @@ struct TopKAcc {
 
     const void* row;
     int64_t hi;          // elements at or past hi are not part of the chunk
-    int32_t* buf;        // this wave's candidate list (LDS, kCandCap entries)
+    int32_t* ent;        // this wave's candidates (LDS, kCandCap each): start
+    uint64_t* mkey;      //   index (| kSingle for one element) and largest key
     int count;           // wave-uniform
     float lm;            // lane maximum and its lowest index (-1: none yet)
     int32_t li;
@@ -57,8 +48,8 @@ struct TopKAcc {
     float th_val;
     int32_t th_idx;
 
-    __device__ void init(const void* r, int64_t h, int32_t* b) {
-        row = r; hi = h; buf = b; count = 0;
+    __device__ void init(const void* r, int64_t h, int32_t* e, uint64_t* k) {
+        row = r; hi = h; ent = e; mkey = k; count = 0;
         lm = -INFINITY; li = -1;
         theta = 0; th_val = -INFINITY; th_idx = INT_MAX;
     }
@@ -90,46 +81,44 @@ struct TopKAcc {
         return vm > th_val || (vm == th_val && start <= th_idx);
     }
 
-    __device__ __forceinline__ void push(bool pass, int32_t ent) {
+    __device__ __forceinline__ void push(bool pass, int32_t e, uint64_t key) {
         const uint64_t m = __ballot(pass);
-        if (pass) buf[count + lanes_below(m)] = ent;
+        if (pass) {
+            const int pos = count + lanes_below(m);
+            ent[pos] = e;
+            mkey[pos] = key;
+        }
         count += __popcll(m);
     }
 
-    // Exact compaction: keep the K candidates with the largest maxima and
-    // raise theta to the K-th of them (only when at least K candidates exist).
+    // Exact compaction from LDS: the K-th largest recorded group maximum
+    // becomes theta and only the groups whose maximum reaches it are kept
+    // (nothing changes while fewer than K candidates exist).
     __device__ void compact() {
-        constexpr int R = kCandCap / kWaveSize;
-        int32_t ent[R];
-        uint64_t mk[R], tmp[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int e = lane_id() + r * kWaveSize;
-            ent[r] = e < count ? buf[e] : -1;
-            mk[r] = ent[r] >= 0 ? candidate_max_key<DT>(row, ent[r], hi) : 0;
-            tmp[r] = mk[r];
-        }
-        uint64_t kth = 0;
-        int got = 0;
+        if (count < K) return;
+        // Keys are unique: round k finds the largest key below round k-1's.
+        uint64_t kth = ~0ull;
         for (int k = 0; k < K; ++k) {
             uint64_t l = 0;
-#pragma unroll
-            for (int r = 0; r < R; ++r) l = umax64(l, tmp[r]);
-            const uint64_t w = wave_max_u64(l);
-            if (w == 0) break;
-            kth = w;
-            ++got;
-#pragma unroll
-            for (int r = 0; r < R; ++r) tmp[r] = (tmp[r] == w) ? 0 : tmp[r];
+            for (int i = lane_id(); i < count; i += kWaveSize) {
+                const uint64_t x = mkey[i];
+                if (x < kth && x > l) l = x;
+            }
+            kth = wave_max_u64(l);
         }
-        if (got < K) return;  // fewer than K candidates: nothing to drop
         raise_theta(kth);
         int n = 0;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const bool keep = ent[r] >= 0 && mk[r] >= kth;
+        for (int base = 0; base < count; base += kWaveSize) {
+            const int i = base + lane_id();
+            const bool keep = i < count && mkey[i] >= kth;
+            const int32_t e = keep ? ent[i] : 0;
+            const uint64_t x = keep ? mkey[i] : 0;
             const uint64_t m = __ballot(keep);
-            if (keep) buf[n + lanes_below(m)] = ent[r];
+            if (keep) {
+                const int pos = n + lanes_below(m);
+                ent[pos] = e;
+                mkey[pos] = x;
+            }
             n += __popcll(m);
         }
         count = n;
@@ -138,13 +127,15 @@ struct TopKAcc {
     template <int U>
     __device__ __forceinline__ void block(const float (&v)[U][kLaneElems], const int64_t* base, const bool* valid) {
         float vm[U];
+        int fe[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             vm[u] = max8(v[u]);
-            if (valid[u] && (vm[u] > lm || li < 0)) {
-                int e = kLaneElems - 1;
+            int e = kLaneElems - 1;
 #pragma unroll
-                for (int k = kLaneElems - 2; k >= 0; --k) e = (v[u][k] == vm[u]) ? k : e;
+            for (int k = kLaneElems - 2; k >= 0; --k) e = (v[u][k] == vm[u]) ? k : e;
+            fe[u] = e;
+            if (valid[u] && (vm[u] > lm || li < 0)) {
                 lm = vm[u];
                 li = int32_t(base[u] + e);
             }
@@ -152,15 +143,85 @@ struct TopKAcc {
         refresh();
         if (count > kCandCap - kWaveSize * U) compact();
 #pragma unroll
-        for (int u = 0; u < U; ++u) push(valid[u] && reaches(vm[u], base[u]), int32_t(base[u]));
+        for (int u = 0; u < U; ++u) {
+            const bool pass = valid[u] && reaches(vm[u], base[u]);
+            push(pass, int32_t(base[u]), pass ? full_key(vm[u], base[u] + fe[u]) : 0);
+        }
     }
 
     __device__ __forceinline__ void one(float z, int64_t j, bool ok) {
         if (ok && (z > lm || li < 0)) { lm = z; li = int32_t(j); }
         refresh();
         if (count > kCandCap - kWaveSize) compact();
-        push(ok && reaches(z, j), int32_t(j) | kSingle);
+        const bool pass = ok && reaches(z, j);
+        push(pass, int32_t(j) | kSingle, pass ? full_key(z, j) : 0);
     }
 };
+
+// Ends a row's selection (whole workgroup, after streaming): every wave
+// compacts its candidates to at most K groups, the keys that reach the largest
+// wave threshold are gathered, wave 0 pops the F + 1 largest, and thread 0
+// writes the first F ids (and logits) that are not `excl`.
+template <int DT, int K>
+__device__ void topf_finish(TopKAcc<DT, K>& acc, const void* rp, int64_t V, int F, int32_t excl,
+                            int32_t* out_ids, float* out_logits) {
+    __shared__ uint64_t keys[kWaves * kLaneElems * K];
+    __shared__ uint64_t s_theta[kWaves];
+    __shared__ uint64_t s_pick[K];
+    __shared__ int s_nkeys;
+
+    acc.compact();
+    if (lane_id() == 0) s_theta[wave_id()] = acc.theta;
+    if (threadIdx.x == 0) s_nkeys = 0;
+    __syncthreads();
+    uint64_t th = s_theta[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) th = umax64(th, s_theta[w]);
+
+    // Keys that reach the workgroup threshold: at most 8 per kept group.
+    for (int e = lane_id(); e < acc.count; e += kWaveSize) {
+        const int32_t ent = acc.ent[e];
+        const int64_t j0 = ent & ~kSingle;
+        const int n = (ent & kSingle) ? 1 : kLaneElems;
+        for (int q = 0; q < n; ++q) {
+            if (j0 + q >= V) break;
+            const uint64_t key = full_key(load_elem<DT>(rp, j0 + q), j0 + q);
+            if (key >= th) keys[atomicAdd(&s_nkeys, 1)] = key;
+        }
+    }
+    __syncthreads();
+
+    const int need = F + 1;
+    if (wave_id() == 0) {
+        const int n = s_nkeys;
+        for (int r = 0; r < need; ++r) {
+            uint64_t l = 0;
+            for (int i = lane_id(); i < n; i += kWaveSize) l = umax64(l, keys[i]);
+            const uint64_t w = wave_max_u64(l);
+            for (int i = lane_id(); i < n; i += kWaveSize)
+                if (keys[i] == w) keys[i] = 0;   // keys are unique: one owner
+            if (lane_id() == 0) s_pick[r] = w;
+        }
+    }
+    __syncthreads();
+
+    if (threadIdx.x == 0) {
+        int n = 0;
+        for (int r = 0; r < need && n < F; ++r) {
+            const uint64_t key = s_pick[r];
+            if (key == 0) break;
+            const int32_t idx = int32_t(~uint32_t(key));
+            if (idx == excl) continue;
+            out_ids[n] = idx;
+            if (out_logits) out_logits[n] = key_logit(uint32_t(key >> 32));
+            ++n;
+        }
+        for (; n < F; ++n) {  // fewer candidates than F (only when vocab <= F)
+            out_ids[n] = -1;
+            if (out_logits) out_logits[n] = -INFINITY;
+        }
+    }
+    __syncthreads();
+}
 
 }  // namespace specv

@@ -28,67 +28,13 @@ __global__ __launch_bounds__(kThreads) void topf_kernel(TopFArgs a) {
                      (int64_t(b) * a.draft.stride_seq + int64_t(k) * a.draft.stride_row) * esz;
 
     __shared__ int32_t cand[kWaves][kCandCap];
-    __shared__ uint64_t keys[kWaves * kLaneElems * K];
-    __shared__ uint64_t s_theta[kWaves];
-    __shared__ uint64_t s_pick[K];
-    __shared__ int s_nkeys;
-
+    __shared__ uint64_t cand_key[kWaves][kCandCap];
     TopKAcc<DT, K> acc;
-    acc.init(rp, a.V, cand[wave_id()]);
+    acc.init(rp, a.V, cand[wave_id()], cand_key[wave_id()]);
     stream_chunk<DT, kUnroll>(rp, 0, a.V, acc);
-    acc.compact();
-    if (lane_id() == 0) s_theta[wave_id()] = acc.theta;
-    if (threadIdx.x == 0) s_nkeys = 0;
-    __syncthreads();
-    uint64_t th = s_theta[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) th = umax64(th, s_theta[w]);
-
-    // Keys that reach the workgroup threshold: at most 8 per kept group.
-    for (int e = lane_id(); e < acc.count; e += kWaveSize) {
-        const int32_t ent = acc.buf[e];
-        const int64_t j0 = ent & ~kSingle;
-        const int n = (ent & kSingle) ? 1 : kLaneElems;
-        for (int q = 0; q < n; ++q) {
-            if (j0 + q >= a.V) break;
-            const uint64_t key = full_key(load_elem<DT>(rp, j0 + q), j0 + q);
-            if (key >= th) keys[atomicAdd(&s_nkeys, 1)] = key;
-        }
-    }
-    __syncthreads();
-
-    const int need = a.F + 1;
-    if (wave_id() == 0) {
-        const int n = s_nkeys;
-        for (int r = 0; r < need; ++r) {
-            uint64_t l = 0;
-            for (int i = lane_id(); i < n; i += kWaveSize) l = umax64(l, keys[i]);
-            const uint64_t w = wave_max_u64(l);
-            for (int i = lane_id(); i < n; i += kWaveSize)
-                if (keys[i] == w) keys[i] = 0;   // keys are unique: one owner
-            if (lane_id() == 0) s_pick[r] = w;
-        }
-    }
-    __syncthreads();
-
-    if (threadIdx.x == 0) {
-        const int32_t excl = (a.tokens != nullptr && k < a.gamma) ? a.tokens[int64_t(b) * a.gamma + k] : -1;
-        const int64_t out = (int64_t(b) * rows + k) * a.F;
-        int n = 0;
-        for (int r = 0; r < need && n < a.F; ++r) {
-            const uint64_t key = s_pick[r];
-            if (key == 0) break;
-            const int32_t idx = int32_t(~uint32_t(key));
-            if (idx == excl) continue;
-            a.out_topk[out + n] = idx;
-            if (a.out_logits) a.out_logits[out + n] = key_logit(uint32_t(key >> 32));
-            ++n;
-        }
-        for (; n < a.F; ++n) {  // fewer candidates than F (only when vocab <= F)
-            a.out_topk[out + n] = -1;
-            if (a.out_logits) a.out_logits[out + n] = -INFINITY;
-        }
-    }
+    const int32_t excl = (a.tokens != nullptr && k < a.gamma) ? a.tokens[int64_t(b) * a.gamma + k] : -1;
+    const int64_t out = (int64_t(b) * rows + k) * a.F;
+    topf_finish<DT, K>(acc, rp, a.V, a.F, excl, a.out_topk + out, a.out_logits ? a.out_logits + out : nullptr);
 }
 
 template <int DT>

@@ -1,0 +1,108 @@
+// Fused chain verification + SSD bonus-token candidates in one pass over the
+// logits [Lecture 5: Speculative Decoding and SpecInfer, sec. 2.2, 3.1;
+// Speculative Speculative Decoding, sec. 4.1.1].
+//
+// specv_verify reads draft rows 0..gamma-1 of the T > 0 sequences and
+// specv_bonus_topk reads all draft rows 0..gamma; run separately, the shared
+// rows cross HBM twice. Here each draft row is streamed once by one workgroup
+// that feeds both the softmax statistics (T > 0, row < gamma) and the top-F
+// selection, writes that row's candidates directly, and publishes its
+// statistics; target rows are as in the verify kernel. Per sequence the
+// slots are target rows 0..gamma, then draft rows 0..gamma; the last one
+// (draft row gamma) resolves the sequence. Used when every row fits one
+// workgroup (S = 1); otherwise the library runs the two kernels.
+#include "specv_chain.hpp"
+#include "specv_topk.hpp"
+
+namespace specv {
+
+namespace {
+
+template <int DT, int K>
+struct SoftmaxTopK {
+    SoftmaxAcc sm;
+    TopKAcc<DT, K> tk;
+    __device__ explicit SoftmaxTopK(float c) : sm(c) {}
+    template <int U>
+    __device__ __forceinline__ void block(const float (&v)[U][kLaneElems], const int64_t* base, const bool* valid) {
+        sm.template block<U>(v, base, valid);
+        tk.template block<U>(v, base, valid);
+    }
+    __device__ __forceinline__ void one(float z, int64_t j, bool ok) {
+        sm.one(z, j, ok);
+        tk.one(z, j, ok);
+    }
+};
+
+template <int DT, int K>
+__global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
+    constexpr int esz = ElemT<DT>::kBytes;
+    const int R1 = 2 * a.gamma + 2;
+    const int64_t g = blockIdx.x;
+    const int slot = int(g % R1);
+    const int sidx = int(g / R1);
+    const int b = sequence_for_slot(a.temperature, a.B, sidx);
+    const float T = a.temperature[b];
+    const bool greedy = !(T > 0.0f);
+    const bool draft_row = slot > a.gamma;
+    const int row = draft_row ? slot - (a.gamma + 1) : slot;
+    const int64_t V = a.V;
+
+    uint64_t word = pack_skipped();
+    if (!draft_row) {
+        const void* rp = row_ptr(a.target, esz, b, row);
+        if (greedy) {
+            ArgmaxAcc acc;
+            stream_chunk<DT, 4>(rp, 0, V, acc);
+            block_merge_argmax(acc.best, acc.idx);
+            word = pack_argmax(acc.best, acc.idx);
+        } else {
+            SoftmaxAcc acc(log2e_over(T));
+            stream_chunk<DT, 4>(rp, 0, V, acc);
+            block_merge_softmax(acc.m, acc.mc, acc.s);
+            word = pack_softmax(acc.m, acc.s);
+        }
+    } else {
+        __shared__ int32_t cand[kWaves][kCandCap];
+        __shared__ uint64_t cand_key[kWaves][kCandCap];
+        const void* rp = row_ptr(a.draft, esz, b, row);
+        const int32_t excl = row < a.gamma ? a.tokens[int64_t(b) * a.gamma + row] : -1;
+        int32_t* ids = a.out_topk + (int64_t(b) * (a.gamma + 1) + row) * a.F;
+        float* vals = a.out_topk_logits ? a.out_topk_logits + (int64_t(b) * (a.gamma + 1) + row) * a.F : nullptr;
+        if (!greedy && row < a.gamma) {
+            SoftmaxTopK<DT, K> acc(log2e_over(T));
+            acc.tk.init(rp, V, cand[wave_id()], cand_key[wave_id()]);
+            stream_chunk<DT, 2>(rp, 0, V, acc);
+            block_merge_softmax(acc.sm.m, acc.sm.mc, acc.sm.s);
+            word = pack_softmax(acc.sm.m, acc.sm.s);
+            topf_finish<DT, K>(acc.tk, rp, V, a.F, excl, ids, vals);
+        } else {
+            TopKAcc<DT, K> acc;
+            acc.init(rp, V, cand[wave_id()], cand_key[wave_id()]);
+            stream_chunk<DT, 2>(rp, 0, V, acc);
+            topf_finish<DT, K>(acc, rp, V, a.F, excl, ids, vals);
+        }
+    }
+    if (threadIdx.x == 0) publish(a.slots + g, word);
+    if (slot == R1 - 1) chain_resolve<DT>(a, b, T, a.slots + int64_t(sidx) * R1, R1);
+}
+
+template <int DT>
+hipError_t launch_dt(const ChainArgs& a, hipStream_t stream) {
+    const dim3 grid(unsigned(int64_t(a.B) * (2 * a.gamma + 2)));
+    const int K = a.F + 1;
+    if (K <= 2) hipLaunchKernelGGL((verify_topf_kernel<DT, 2>), grid, dim3(kThreads), 0, stream, a);
+    else if (K <= 4) hipLaunchKernelGGL((verify_topf_kernel<DT, 4>), grid, dim3(kThreads), 0, stream, a);
+    else if (K <= 8) hipLaunchKernelGGL((verify_topf_kernel<DT, 8>), grid, dim3(kThreads), 0, stream, a);
+    else if (K <= 16) hipLaunchKernelGGL((verify_topf_kernel<DT, 16>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((verify_topf_kernel<DT, 32>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_verify_topf(const ChainArgs& a, int dtype, hipStream_t stream) {
+    return dtype == DT_BF16 ? launch_dt<DT_BF16>(a, stream) : launch_dt<DT_F32>(a, stream);
+}
+
+}  // namespace specv

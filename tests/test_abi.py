@@ -32,8 +32,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("specv_verify", "specv_bonus_topk", "specv_tree_verify",
+    for n in ("specv_verify", "specv_bonus_topk", "specv_tree_verify", "specv_verify_topk",
               "specv_verify_workspace_size", "specv_tree_verify_workspace_size",
+              "specv_verify_topk_workspace_size",
               "specv_uniforms", "specv_last_error", "specv_version"):
         assert n in names
 
@@ -101,6 +102,24 @@ def test_verify_validation(lib):
     assert call_verify(lib, ws=FAKE + 16, ws_bytes=1 << 20) == WORKSPACE     # misaligned
     assert call_verify(lib, ws=FAKE, ws_bytes=8) == WORKSPACE               # too small
     assert b"workspace" in lib.specv_last_error()
+
+
+def test_verify_topk_validation(lib):
+    st, n = ws_size(lib, "specv_verify_topk_workspace_size", 256, 8, 128256)
+    assert st == 0 and n == 256 * 18 * 8            # fused: 2*gamma + 2 slots per sequence
+    st, m = ws_size(lib, "specv_verify_topk_workspace_size", 8, 4, 32000)
+    assert st == 0 and m == ws_size(lib, "specv_verify_workspace_size", 8, 4, 32000)[1]
+
+    def call(F=2, B=2, topk=FAKE, tokens=FAKE, ws_bytes=1 << 20, ws=FAKE):
+        return lib.specv_verify_topk(L(), L(), tokens, FAKE, B, 3, 10, F, 1, 0, FAKE, FAKE, None, None,
+                                     topk, None, ws, ws_bytes, None)
+    assert call(F=0) == INVALID
+    assert call(F=10) == INVALID
+    assert call(B=0) == INVALID
+    assert call(topk=None) == INVALID
+    assert call(tokens=None) == INVALID
+    assert call(ws_bytes=8) == WORKSPACE
+    assert call(ws=None, ws_bytes=0) == WORKSPACE
 
 
 def test_topk_validation(lib):
