@@ -33,6 +33,7 @@ METRIC = "verified vocab rows/sec + achieved HBM GB/s (% peak) at V=128256, B=25
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "speculative_sampling_verification_04_amd", "csrc")
+COPY_BYTES = 1 << 30
 
 
 def algorithmic_bytes(w):
@@ -169,6 +170,14 @@ def main():
     verify_ms = timed(lambda i: binding.verify(target, draft, tokens, temp, w.seed, i, workspace=vws, out=vout))
     topf_ms = timed(lambda i: binding.bonus_topk(draft, tokens, F, out=(out["topk"], out["topk_logits"])))
 
+    # Yardstick for the memory counters and for what a plain streaming kernel
+    # reaches: torch's elementwise negation of 1 GiB of int32 (reads 1 GiB, writes
+    # 1 GiB; larger than the 256 MB last-level cache), outside the timed region.
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = timed(lambda i: torch.neg(src, out=dst))
+    del src, dst
+
     ms_per_step = elapsed * 1e3 / args.steps
     rows = B * (gamma + 1)
     verify_bytes, topf_bytes, step_bytes = algorithmic_bytes(w)
@@ -202,6 +211,8 @@ def main():
                                     "gbps": verify_bytes / (verify_ms * 1e-3) / 1e9},
             "topf_kernel": {"avg_ms": topf_ms, "algorithmic_bytes": topf_bytes,
                             "gbps": topf_bytes / (topf_ms * 1e-3) / 1e9}},
+        "copy_yardstick": {"kernel": "torch.neg int32", "read_bytes": COPY_BYTES, "write_bytes": COPY_BYTES,
+                           "avg_ms": copy_ms, "gbps": 2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9},
         "mean_accepted": mean_accepted,
     }
     if not args.no_cpu_baseline:

@@ -19,7 +19,7 @@ __device__ __forceinline__ float log2e_over(float T) { return float(1.4426950408
 // holds target row r (r <= gamma) and draft row r - gamma - 1 (after that);
 // nslots = all slots of the sequence (waited for, then zeroed).
 template <int DT>
-__device__ void chain_resolve(const ChainArgs& a, int b, float T, uint64_t* slots, int64_t nslots) {
+__device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T, uint64_t* slots, int64_t nslots) {
     constexpr int esz = ElemT<DT>::kBytes;
     const int gamma = a.gamma;
     const int R = 2 * gamma + 1;

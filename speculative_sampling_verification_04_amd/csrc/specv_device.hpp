@@ -49,11 +49,19 @@ __device__ __forceinline__ float load_elem(const void* row, int64_t j) {
 // two for fp32.
 template <int DT> struct Raw8 { uint4 w[ElemT<DT>::kBytes / 2]; };
 
+// Logit rows are read exactly once by the streaming pass, so the loads carry
+// the nontemporal hint: on gfx950 this streams at ~6.9 TB/s against ~6.0 TB/s
+// for ordinary loads of the same rows.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 template <int DT>
 __device__ __forceinline__ void load_raw8(Raw8<DT>& r, const char* p) {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
+    const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
 #pragma unroll
-    for (int i = 0; i < ElemT<DT>::kBytes / 2; ++i) r.w[i] = q[i];
+    for (int i = 0; i < ElemT<DT>::kBytes / 2; ++i) {
+        const u32x4_t x = __builtin_nontemporal_load(q + i);
+        r.w[i] = make_uint4(x.x, x.y, x.z, x.w);
+    }
 }
 
 template <int DT>
@@ -79,54 +87,98 @@ __device__ __forceinline__ float max8(const float v[kLaneElems]) {
 // ------------------------------------------------------------- streaming
 //
 // Visits elements [lo, hi) of `row`. When the chunk start is 16-byte aligned
-// the body is read in steps of kLaneElems elements per lane, U steps in flight
-// per lane per iteration (lane t takes steps t, t + kThreads, ...), and the
-// remainder element by element; otherwise every element is read singly.
-// Both loop bounds are uniform over the workgroup, so every lane calls the
-// visitor's block() and one() on every iteration (visitors may use wave-wide
-// operations); steps or elements past the end arrive as -inf with valid = false.
+// the body is read in steps of kLaneElems elements per lane, U steps per lane
+// per iteration (lane t takes steps t, t + kThreads, ...), and the remainder
+// element by element; otherwise every element is read singly. Both loop
+// bounds are uniform over the workgroup, so every lane calls the visitor's
+// block() and one() on every iteration (visitors may use wave-wide
+// operations); steps or elements past the end arrive as -inf with
+// valid = false.
+//
+// Software pipelined through a ring of D buffers of U steps: while iteration
+// i is processed, the loads of iterations i + 1 .. i + D - 1 are in flight,
+// so D * U 16-byte loads per lane overlap the arithmetic while only U steps
+// are unpacked at a time. Every load in the loop is issued unconditionally
+// (a load under a per-lane or per-iteration branch makes the compiler wait
+// for every outstanding load before the processing, which would serialise
+// the ring); refills past the last iteration are clamped and never visited.
+// Per-lane validity is tested only in the last iteration.
 template <int DT, int U, class Acc>
+__device__ __forceinline__ void visit_steps(const Raw8<DT> (&r)[U], int64_t lo, int64_t s0, int64_t nstep,
+                                            bool full, Acc& acc) {
+    float v[U][kLaneElems];
+    int64_t idx[U];
+    bool valid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t s = s0 + threadIdx.x + int64_t(u) * kThreads;
+        valid[u] = full || s < nstep;
+        idx[u] = lo + s * kLaneElems;
+        unpack8<DT>(r[u], v[u]);
+        if (!valid[u]) {
+#pragma unroll
+            for (int e = 0; e < kLaneElems; ++e) v[u][e] = -INFINITY;
+        }
+    }
+    acc.template block<U>(v, idx, valid);
+}
+
+template <int DT, int U, int D, class Acc>
 __device__ __forceinline__ void stream_chunk(const void* row, int64_t lo, int64_t hi, Acc& acc) {
+    static_assert(U >= 1 && D >= 0, "U >= 1 steps per iteration; D = 0 (prefetch) or a ring of D >= 1");
     constexpr int kB = ElemT<DT>::kBytes;
     constexpr int64_t kStride = int64_t(kThreads) * U;
     const char* base = static_cast<const char*>(row) + lo * kB;
     const int64_t n = hi - lo;
     const bool aligned = (reinterpret_cast<uintptr_t>(base) & 15u) == 0;
     const int64_t nstep = aligned ? n / kLaneElems : 0;
-    // Software pipelined: the next iteration's U loads are issued before the
-    // current iteration's data is processed.
-    Raw8<DT> cur[U], nxt[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t s = threadIdx.x + int64_t(u) * kThreads;
-        if (s < nstep) load_raw8<DT>(cur[u], base + s * (kLaneElems * kB));
-    }
-    for (int64_t base0 = 0; base0 < nstep; base0 += kStride) {
-        if (base0 + kStride < nstep) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t s = base0 + kStride + threadIdx.x + int64_t(u) * kThreads;
-                if (s < nstep) load_raw8<DT>(nxt[u], base + s * (kLaneElems * kB));
-            }
-        }
-        float v[U][kLaneElems];
-        int64_t idx[U];
-        bool valid[U];
+    const int64_t nit = (nstep + kStride - 1) / kStride;
+    const int64_t last = nstep - 1;
+    // Loads of steps past the end are clamped to the last step (in bounds,
+    // and the same line for every such lane); their data is never used.
+    auto load_it = [&](Raw8<DT> (&r)[U], int64_t it) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t s = base0 + threadIdx.x + int64_t(u) * kThreads;
-            valid[u] = s < nstep;
-            idx[u] = lo + s * kLaneElems;
-            if (valid[u]) {
-                unpack8<DT>(cur[u], v[u]);
-            } else {
+            const int64_t s = it * kStride + threadIdx.x + int64_t(u) * kThreads;
+            load_raw8<DT>(r[u], base + (s < last ? s : last) * (kLaneElems * kB));
+        }
+    };
+
+    if constexpr (D == 0) {
+        // Prefetch form: one buffer in flight, issued before the current
+        // iteration is processed and moved into place after it (fewer live
+        // registers than a ring of two when the visitor is heavy).
+        if (nstep > 0) {
+            const int64_t nfull = nstep - nstep % kStride;
+            Raw8<DT> cur[U];
+            load_it(cur, 0);
+            int64_t base0 = 0;
+            for (; base0 < nfull; base0 += kStride) {
+                Raw8<DT> nxt[U];
+                load_it(nxt, base0 / kStride + 1);
+                visit_steps<DT, U>(cur, lo, base0, nstep, true, acc);
 #pragma unroll
-                for (int e = 0; e < kLaneElems; ++e) v[u][e] = -INFINITY;
+                for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+            }
+            if (base0 < nstep) visit_steps<DT, U>(cur, lo, base0, nstep, false, acc);
+        }
+    } else if (nstep > 0) {
+        Raw8<DT> ring[D][U];
+#pragma unroll
+        for (int d = 0; d < D; ++d) load_it(ring[d], d);
+        int64_t it0 = 0;
+        for (; it0 + D <= nit; it0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                visit_steps<DT, U>(ring[d], lo, (it0 + d) * kStride, nstep, it0 + d + 1 < nit, acc);
+                load_it(ring[d], it0 + D + d);
             }
         }
-        acc.template block<U>(v, idx, valid);
+        // Drain: iterations it0 .. nit - 1 (fewer than D) are in the ring.
 #pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        for (int d = 0; d + 1 < D; ++d) {
+            if (it0 + d < nit) visit_steps<DT, U>(ring[d], lo, (it0 + d) * kStride, nstep, false, acc);
+        }
     }
     for (int64_t j0 = nstep * kLaneElems; j0 < n; j0 += kThreads) {
         const int64_t j = j0 + threadIdx.x;

@@ -221,7 +221,7 @@ struct ResidualWeights {
 // Pass A: per-tile sums of the weights into `tile_sum` (fp32) and their total
 // (fp64). Every wave keeps kTilesInFlight tiles' loads in flight.
 template <class WFn>
-__device__ double weight_tiles(const WFn& f, int64_t V, float* tile_sum) {
+__device__ __forceinline__ double weight_tiles(const WFn& f, int64_t V, float* tile_sum) {
     const int ntiles = int((V + kTileElems - 1) / kTileElems);
     for (int t0 = wave_id() * kTilesInFlight; t0 < ntiles; t0 += kWaves * kTilesInFlight) {
         typename WFn::Raw raw[kTilesInFlight];
@@ -252,7 +252,7 @@ __device__ double weight_tiles(const WFn& f, int64_t V, float* tile_sum) {
 // Pass B: given the tile sums of pass A, the smallest j with S_j >= v * W.
 // Returns -1 when the total is 0.
 template <class WFn>
-__device__ int32_t sample_from_tiles(const WFn& f, int64_t V, float v, const float* tile_sum) {
+__device__ __forceinline__ int32_t sample_from_tiles(const WFn& f, int64_t V, float v, const float* tile_sum) {
     const int ntiles = int((V + kTileElems - 1) / kTileElems);
     const int lane = lane_id();
     __shared__ int32_t s_tile;

@@ -4,8 +4,8 @@
 //
 // Keys: (order-preserving logit key << 32) | ~index, so a larger key is a
 // larger logit, or an equal logit at a lower index. Each lane tracks only its
-// running maximum (value and lowest index). Once per streaming iteration the
-// wave forms a lower bound theta on the K-th largest key seen so far: the
+// running maximum value. Every other streaming iteration the wave forms a
+// lower bound theta on the K-th largest key seen so far: the
 // minimum, over K groups of lanes, of each group's largest lane maximum (K
 // distinct elements are >= theta). An 8-element group whose maximum reaches
 // theta is recorded as a candidate (its start index and its largest key) in
@@ -42,16 +42,18 @@ struct TopKAcc {
     int32_t* ent;        // this wave's candidates (LDS, kCandCap each): start
     uint64_t* mkey;      //   index (| kSingle for one element) and largest key
     int count;           // wave-uniform
-    float lm;            // lane maximum and its lowest index (-1: none yet)
+    float lm;            // lane maximum (li < 0: the lane has seen no element yet)
     int32_t li;
     uint64_t theta;      // wave-uniform lower bound on the K-th largest key (0: none)
     float th_val;
     int32_t th_idx;
+    int iter;            // block() calls so far
 
     __device__ void init(const void* r, int64_t h, int32_t* e, uint64_t* k) {
         row = r; hi = h; ent = e; mkey = k; count = 0;
         lm = -INFINITY; li = -1;
         theta = 0; th_val = -INFINITY; th_idx = INT_MAX;
+        iter = 0;
     }
 
     // theta's logit and index; an index part of 0 (key lo) stands for "any
@@ -127,25 +129,27 @@ struct TopKAcc {
     template <int U>
     __device__ __forceinline__ void block(const float (&v)[U][kLaneElems], const int64_t* base, const bool* valid) {
         float vm[U];
-        int fe[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             vm[u] = max8(v[u]);
-            int e = kLaneElems - 1;
-#pragma unroll
-            for (int k = kLaneElems - 2; k >= 0; --k) e = (v[u][k] == vm[u]) ? k : e;
-            fe[u] = e;
             if (valid[u] && (vm[u] > lm || li < 0)) {
                 lm = vm[u];
-                li = int32_t(base[u] + e);
+                li = int32_t(base[u]);
             }
         }
-        refresh();
+        if ((++iter & 1) == 0) refresh();  // every other iteration: theta only lags
         if (count > kCandCap - kWaveSize * U) compact();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool pass = valid[u] && reaches(vm[u], base[u]);
-            push(pass, int32_t(base[u]), pass ? full_key(vm[u], base[u] + fe[u]) : 0);
+            uint64_t key = 0;
+            if (pass) {  // rare once theta has settled: locate the group maximum
+                int e = kLaneElems - 1;
+#pragma unroll
+                for (int k = kLaneElems - 2; k >= 0; --k) e = (v[u][k] == vm[u]) ? k : e;
+                key = full_key(vm[u], base[u] + e);
+            }
+            push(pass, int32_t(base[u]), key);
         }
     }
 
@@ -163,7 +167,7 @@ struct TopKAcc {
 // wave threshold are gathered, wave 0 pops the F + 1 largest, and thread 0
 // writes the first F ids (and logits) that are not `excl`.
 template <int DT, int K>
-__device__ void topf_finish(TopKAcc<DT, K>& acc, const void* rp, int64_t V, int F, int32_t excl,
+__device__ __forceinline__ void topf_finish(TopKAcc<DT, K>& acc, const void* rp, int64_t V, int F, int32_t excl,
                             int32_t* out_ids, float* out_logits) {
     __shared__ uint64_t keys[kWaves * kLaneElems * K];
     __shared__ uint64_t s_theta[kWaves];

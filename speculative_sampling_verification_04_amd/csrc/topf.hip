@@ -16,7 +16,8 @@ namespace specv {
 
 namespace {
 
-constexpr int kUnroll = 2;
+constexpr int kU = 2;  // 16-byte steps per lane per iteration
+constexpr int kD = 2;  // ring of two buffers (see stream_chunk)
 
 template <int DT, int K>
 __global__ __launch_bounds__(kThreads) void topf_kernel(TopFArgs a) {
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(kThreads) void topf_kernel(TopFArgs a) {
     __shared__ uint64_t cand_key[kWaves][kCandCap];
     TopKAcc<DT, K> acc;
     acc.init(rp, a.V, cand[wave_id()], cand_key[wave_id()]);
-    stream_chunk<DT, kUnroll>(rp, 0, a.V, acc);
+    stream_chunk<DT, kU, kD>(rp, 0, a.V, acc);
     const int32_t excl = (a.tokens != nullptr && k < a.gamma) ? a.tokens[int64_t(b) * a.gamma + k] : -1;
     const int64_t out = (int64_t(b) * rows + k) * a.F;
     topf_finish<DT, K>(acc, rp, a.V, a.F, excl, a.out_topk + out, a.out_logits ? a.out_logits + out : nullptr);

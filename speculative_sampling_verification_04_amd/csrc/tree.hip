@@ -24,7 +24,8 @@ namespace specv {
 
 namespace {
 
-constexpr int kUnroll = 4;
+constexpr int kU = 4;  // 16-byte steps per lane per iteration
+constexpr int kD = 1;  // ring of one buffer (see stream_chunk)
 
 __device__ __forceinline__ const void* row_ptr(const RowView& v, int esz, int64_t b, int64_t r) {
     return static_cast<const char*>(v.data) + (b * v.stride_seq + r * v.stride_row) * esz;
@@ -53,7 +54,7 @@ __device__ int child_with_token(const int32_t* par, const int32_t* tok, int N, i
 }
 
 template <int DT>
-__device__ void tree_resolve(const TreeArgs& a, int b, float T, uint64_t* slots) {
+__device__ __forceinline__ void tree_resolve(const TreeArgs& a, int b, float T, uint64_t* slots) {
     constexpr int esz = ElemT<DT>::kBytes;
     const int N = a.N;
     const bool greedy = !(T > 0.0f);
@@ -226,12 +227,12 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(TreeArgs a) {
         const void* rp = row_ptr(draft_row ? a.draft : a.target, esz, b, node);
         if (greedy) {
             ArgmaxAcc acc;
-            stream_chunk<DT, kUnroll>(rp, lo, hi, acc);
+            stream_chunk<DT, kU, kD>(rp, lo, hi, acc);
             block_merge_argmax(acc.best, acc.idx);
             word = pack_argmax(acc.best, acc.idx);
         } else {
             SoftmaxAcc acc(log2e_over(T));
-            stream_chunk<DT, kUnroll>(rp, lo, hi, acc);
+            stream_chunk<DT, kU, kD>(rp, lo, hi, acc);
             block_merge_softmax(acc.m, acc.mc, acc.s);
             word = pack_softmax(acc.m, acc.s);
         }

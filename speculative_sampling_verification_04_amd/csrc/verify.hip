@@ -19,7 +19,8 @@ namespace specv {
 
 namespace {
 
-constexpr int kUnroll = 4;
+constexpr int kU = 8;  // 16-byte steps per lane per iteration
+constexpr int kD = 0;  // prefetch form (see stream_chunk)
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void chain_verify_kernel(ChainArgs a) {
@@ -43,12 +44,12 @@ __global__ __launch_bounds__(kThreads) void chain_verify_kernel(ChainArgs a) {
         const void* rp = row_ptr(draft_row ? a.draft : a.target, esz, b, row);
         if (greedy) {
             ArgmaxAcc acc;
-            stream_chunk<DT, kUnroll>(rp, lo, hi, acc);
+            stream_chunk<DT, kU, kD>(rp, lo, hi, acc);
             block_merge_argmax(acc.best, acc.idx);
             word = pack_argmax(acc.best, acc.idx);
         } else {
             SoftmaxAcc acc(log2e_over(T));
-            stream_chunk<DT, kUnroll>(rp, lo, hi, acc);
+            stream_chunk<DT, kU, kD>(rp, lo, hi, acc);
             block_merge_softmax(acc.m, acc.mc, acc.s);
             word = pack_softmax(acc.m, acc.s);
         }

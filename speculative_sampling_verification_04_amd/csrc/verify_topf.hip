@@ -18,6 +18,11 @@ namespace specv {
 
 namespace {
 
+// Streaming shapes (16-byte steps per lane per iteration; 0 = prefetch form):
+// target rows carry only the softmax or argmax, draft rows also the top-K.
+constexpr int kTargetU = 4, kTargetD = 0;
+constexpr int kDraftU = 2, kDraftD = 0;
+
 template <int DT, int K>
 struct SoftmaxTopK {
     SoftmaxAcc sm;
@@ -53,12 +58,12 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
         const void* rp = row_ptr(a.target, esz, b, row);
         if (greedy) {
             ArgmaxAcc acc;
-            stream_chunk<DT, 4>(rp, 0, V, acc);
+            stream_chunk<DT, kTargetU, kTargetD>(rp, 0, V, acc);
             block_merge_argmax(acc.best, acc.idx);
             word = pack_argmax(acc.best, acc.idx);
         } else {
             SoftmaxAcc acc(log2e_over(T));
-            stream_chunk<DT, 4>(rp, 0, V, acc);
+            stream_chunk<DT, kTargetU, kTargetD>(rp, 0, V, acc);
             block_merge_softmax(acc.m, acc.mc, acc.s);
             word = pack_softmax(acc.m, acc.s);
         }
@@ -72,14 +77,14 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
         if (!greedy && row < a.gamma) {
             SoftmaxTopK<DT, K> acc(log2e_over(T));
             acc.tk.init(rp, V, cand[wave_id()], cand_key[wave_id()]);
-            stream_chunk<DT, 2>(rp, 0, V, acc);
+            stream_chunk<DT, kDraftU, kDraftD>(rp, 0, V, acc);
             block_merge_softmax(acc.sm.m, acc.sm.mc, acc.sm.s);
             word = pack_softmax(acc.sm.m, acc.sm.s);
             topf_finish<DT, K>(acc.tk, rp, V, a.F, excl, ids, vals);
         } else {
             TopKAcc<DT, K> acc;
             acc.init(rp, V, cand[wave_id()], cand_key[wave_id()]);
-            stream_chunk<DT, 2>(rp, 0, V, acc);
+            stream_chunk<DT, kDraftU, kDraftD>(rp, 0, V, acc);
             topf_finish<DT, K>(acc, rp, V, a.F, excl, ids, vals);
         }
     }
