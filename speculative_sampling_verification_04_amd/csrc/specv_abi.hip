@@ -62,19 +62,46 @@ specv_status check_workspace(void* ws, size_t have, size_t need) {
 
 RowView view(const specv_logits& l) { return RowView{l.data, l.stride_seq, l.stride_row}; }
 
-// Workspace: one 64-bit slot per workgroup (row chunk).
+// Workspace: one 64-bit word per row chunk (its statistics), then, when the
+// bonus draw is shared by H > 1 workgroups, one word per residual tile of
+// every sequence.
 struct Layout {
     int32_t S;
     int64_t chunk;
+    int32_t H;
+    int32_t ntiles;
     size_t slot_bytes;
-    size_t total() const { return slot_bytes; }
+    size_t tile_bytes;
+    size_t total() const { return slot_bytes + tile_bytes; }
 };
 
 Layout layout_for(int64_t batch, int64_t row_tasks_per_seq, int64_t vocab) {
     Layout L;
     choose_split(batch * row_tasks_per_seq, vocab, &L.S, &L.chunk);
+    L.H = bonus_helpers(vocab);
+    L.ntiles = int32_t((vocab + kTileElems - 1) / kTileElems);
     L.slot_bytes = round_up(size_t(batch) * row_tasks_per_seq * L.S * sizeof(uint64_t));
+    L.tile_bytes = L.H > 1 ? round_up(size_t(batch) * L.ntiles * sizeof(uint64_t)) : 0;
     return L;
+}
+
+// Layout of the fused kernel: 2*gamma + 2 unsplit rows per sequence.
+Layout fused_layout(int64_t batch, int64_t gamma, int64_t vocab) {
+    Layout L = layout_for(batch, 2 * gamma + 2, vocab);
+    L.S = 1;
+    L.chunk = vocab;
+    L.slot_bytes = round_up(size_t(batch) * (2 * gamma + 2) * sizeof(uint64_t));
+    return L;
+}
+
+void set_bonus(ChainArgs& a, const Layout& L, int64_t row_words, void* workspace) {
+    a.D = bonus_delay(a.B, row_words);
+    a.S = L.S;
+    a.chunk = L.chunk;
+    a.H = L.H;
+    a.ntiles = L.ntiles;
+    a.slots = static_cast<uint64_t*>(workspace);
+    a.tiles = L.H > 1 ? reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.slot_bytes) : nullptr;
 }
 
 specv_status check_chain_sizes(int32_t batch, int32_t gamma, int32_t vocab) {
@@ -97,7 +124,7 @@ bool fused_fits(int64_t batch, int64_t gamma, int64_t vocab) {
 
 size_t verify_topk_bytes(int64_t batch, int64_t gamma, int64_t vocab) {
     const size_t plain = layout_for(batch, 2 * gamma + 1, vocab).total();
-    const size_t fused = round_up(size_t(batch) * (2 * gamma + 2) * sizeof(uint64_t));
+    const size_t fused = fused_layout(batch, gamma, vocab).total();
     return plain > fused ? plain : fused;
 }
 
@@ -157,7 +184,7 @@ specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes, int3
     if (bytes == nullptr) return fail(SPECV_ERR_INVALID_ARG, "bytes is NULL");
     specv_status st = check_tree_sizes(batch, nodes, vocab);
     if (st != SPECV_OK) return st;
-    *bytes = layout_for(batch, 2 * int64_t(nodes), vocab).total();
+    *bytes = layout_for(batch, 2 * int64_t(nodes), vocab).slot_bytes;  // row words only
     return ok();
 }
 
@@ -174,7 +201,7 @@ specv_status specv_verify(specv_logits target, specv_logits draft, const int32_t
     if (!draft_tokens || !temperature || !out_tokens || !out_num_accepted)
         return fail(SPECV_ERR_INVALID_ARG, "draft_tokens, temperature, out_tokens and out_num_accepted are required");
     const Layout L = layout_for(batch, 2 * int64_t(gamma) + 1, vocab);
-    const int64_t grid = int64_t(batch) * (2 * gamma + 1) * L.S;
+    const int64_t grid = int64_t(batch) * ((2 * gamma + 1) * int64_t(L.S) + L.H);
     if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch (%lld workgroups)", (long long)grid);
     if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
 
@@ -186,15 +213,13 @@ specv_status specv_verify(specv_logits target, specv_logits draft, const int32_t
     a.B = batch;
     a.gamma = gamma;
     a.V = vocab;
-    a.S = L.S;
-    a.chunk = L.chunk;
+    set_bonus(a, L, (2 * int64_t(gamma) + 1) * L.S, workspace);
     a.seed = seed;
     a.offset = offset;
     a.out_tokens = out_tokens;
     a.out_nacc = out_num_accepted;
     a.out_probs = out_probs;
     a.out_mass = out_bonus_mass;
-    a.slots = static_cast<uint64_t*>(workspace);
     const hipError_t e = launch_chain(a, target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32,
                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_verify launch failed: %s", hipGetErrorString(e));
@@ -219,8 +244,9 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
         return fail(SPECV_ERR_INVALID_ARG,
                     "draft_tokens, temperature, out_tokens, out_num_accepted and out_topk are required");
     const bool fused = fused_fits(batch, gamma, vocab);
-    const Layout L = layout_for(batch, 2 * int64_t(gamma) + 1, vocab);
-    const int64_t grid = fused ? int64_t(batch) * (2 * gamma + 2) : int64_t(batch) * (2 * gamma + 1) * L.S;
+    const Layout L = fused ? fused_layout(batch, gamma, vocab) : layout_for(batch, 2 * int64_t(gamma) + 1, vocab);
+    const int64_t grid = fused ? int64_t(batch) * (2 * gamma + 2 + L.H)
+                               : int64_t(batch) * ((2 * gamma + 1) * int64_t(L.S) + L.H);
     if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch");
     if ((st = check_workspace(workspace, workspace_bytes, verify_topk_bytes(batch, gamma, vocab))) != SPECV_OK)
         return st;
@@ -233,15 +259,13 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
     a.B = batch;
     a.gamma = gamma;
     a.V = vocab;
-    a.S = fused ? 1 : L.S;
-    a.chunk = fused ? int64_t(vocab) : L.chunk;
+    set_bonus(a, L, fused ? 2 * int64_t(gamma) + 2 : (2 * int64_t(gamma) + 1) * L.S, workspace);
     a.seed = seed;
     a.offset = offset;
     a.out_tokens = out_tokens;
     a.out_nacc = out_num_accepted;
     a.out_probs = out_probs;
     a.out_mass = out_bonus_mass;
-    a.slots = static_cast<uint64_t*>(workspace);
     a.F = F;
     a.out_topk = out_topk;
     a.out_topk_logits = out_topk_logits;
@@ -308,7 +332,7 @@ specv_status specv_tree_verify(specv_logits target, specv_logits draft, const in
     const Layout L = layout_for(batch, 2 * int64_t(nodes), vocab);
     const int64_t grid = int64_t(batch) * 2 * nodes * L.S;
     if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch");
-    if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
+    if ((st = check_workspace(workspace, workspace_bytes, L.slot_bytes)) != SPECV_OK) return st;
 
     TreeArgs a;
     a.target = view(target);

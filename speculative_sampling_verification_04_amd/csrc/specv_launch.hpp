@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "specv_device.hpp"
+
 namespace specv {
 
 struct RowView {
@@ -16,8 +18,9 @@ struct RowView {
 
 // Chain verification. Per sequence there are R = 2*gamma + 1 row tasks
 // (target rows 0..gamma, then draft rows 0..gamma-1), each split into S
-// chunks of `chunk` elements; workgroup g publishes its chunk's statistics in
-// slots[g] (one 64-bit word).
+// chunks of `chunk` elements, then H bonus workgroups; row chunk j of the
+// sequence in dispatch slot s publishes its statistics in slots[s * R * S + j]
+// (one 64-bit word).
 struct ChainArgs {
     RowView target, draft;
     const int32_t* tokens;
@@ -30,6 +33,12 @@ struct ChainArgs {
     float* out_probs;
     float* out_mass;
     uint64_t* slots;
+    // Bonus draw of T > 0 sequences: H workgroups per sequence (dispatched
+    // after its rows) share the tile sums of the weights; the last of them
+    // resolves. With H > 1 they meet in `tiles` (ntiles words per sequence).
+    int32_t H, ntiles;
+    uint64_t* tiles;
+    int32_t D;               // bonus workgroups trail their rows by D sequences (see decode_chain)
     // Fused top-F (verify_topf_kernel only).
     int32_t F;
     int32_t* out_topk;
@@ -74,6 +83,46 @@ inline void choose_split(int64_t row_tasks, int64_t V, int32_t* S, int64_t* chun
     s = (V + c - 1) / c;
     *S = int32_t(s);
     *chunk = c;
+}
+
+// Workgroups that share the bonus draw of one T > 0 sequence: about 32 tiles
+// (16K elements of the row pair) each, at most 16.
+inline int32_t bonus_helpers(int64_t V) {
+    const int64_t ntiles = (V + kTileElems - 1) / kTileElems;
+    const int64_t h = (ntiles + 31) / 32;
+    return int32_t(h < 1 ? 1 : h > 16 ? 16 : h);
+}
+
+// How many sequences the bonus workgroups of a sequence trail its rows by in
+// dispatch order: about one GPU-full of row workgroups (RS per sequence), so
+// that when they start their rows are (nearly) done and they do not hold CU
+// slots waiting.
+inline int32_t bonus_delay(int64_t B, int64_t RS) {
+    const int64_t d = (1536 + RS - 1) / RS;
+    return int32_t(d < B ? d : B);
+}
+
+// Dispatch order of a chain launch: unit u = the RS row workgroups of the
+// sequence in dispatch slot u (u < B), then the H bonus workgroups of
+// sequence u - D (u >= D). Maps workgroup g to its sequence slot and its
+// index w in that sequence (w < RS: row chunk w; else bonus workgroup w - RS).
+__device__ __forceinline__ void decode_chain(int64_t g, int64_t B, int64_t RS, int64_t H, int64_t D, int& sidx,
+                                             int64_t& w) {
+    const int64_t a_end = D * RS;                      // units 0..D-1: rows only
+    const int64_t b_end = a_end + (B - D) * (RS + H);  // units D..B-1: rows, then bonus of u - D
+    if (g < a_end) {
+        sidx = int(g / RS);
+        w = g % RS;
+    } else if (g < b_end) {
+        const int64_t u = D + (g - a_end) / (RS + H);
+        const int64_t o = (g - a_end) % (RS + H);
+        sidx = int(o < RS ? u : u - D);
+        w = o;
+    } else {                                           // units B..B+D-1: bonus only
+        const int64_t i = g - b_end;
+        sidx = int(B - D + i / H);
+        w = RS + i % H;
+    }
 }
 
 hipError_t launch_chain(const ChainArgs& a, int dtype, hipStream_t stream);

@@ -218,27 +218,33 @@ struct ResidualWeights {
     }
 };
 
-// Pass A: per-tile sums of the weights into `tile_sum` (fp32) and their total
-// (fp64). Every wave keeps kTilesInFlight tiles' loads in flight.
-template <class WFn>
-__device__ __forceinline__ double weight_tiles(const WFn& f, int64_t V, float* tile_sum) {
-    const int ntiles = int((V + kTileElems - 1) / kTileElems);
-    for (int t0 = wave_id() * kTilesInFlight; t0 < ntiles; t0 += kWaves * kTilesInFlight) {
-        typename WFn::Raw raw[kTilesInFlight];
+// Pass A over tiles [t_lo, t_hi): per-tile sums of the weights (fp32), handed
+// to sink(t, sum) by lane 0 of the wave that summed the tile. Every wave keeps
+// TIF tiles' loads in flight (more is faster for a lone workgroup; fewer keeps
+// the registers of a kernel that also streams rows low).
+template <int TIF = kTilesInFlight, class WFn, class Sink>
+__device__ __forceinline__ void weight_tile_range(const WFn& f, int t_lo, int t_hi, Sink sink) {
+    for (int t0 = t_lo + wave_id() * TIF; t0 < t_hi; t0 += kWaves * TIF) {
+        typename WFn::Raw raw[TIF];
 #pragma unroll
-        for (int u = 0; u < kTilesInFlight; ++u)
-            f.load(int64_t(t0 + u) * kTileElems + lane_id() * kLaneElems, raw[u]);
+        for (int u = 0; u < TIF; ++u)
+            if (t0 + u < t_hi) f.load(int64_t(t0 + u) * kTileElems + lane_id() * kLaneElems, raw[u]);
 #pragma unroll
-        for (int u = 0; u < kTilesInFlight; ++u) {
+        for (int u = 0; u < TIF; ++u) {
+            if (t0 + u >= t_hi) break;
             float w[kLaneElems];
             f.weights(raw[u], w);
             const float ls = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
             const float ts = wave_sum(ls);
-            if (lane_id() == 0 && t0 + u < ntiles) tile_sum[t0 + u] = ts;
+            if (lane_id() == 0) sink(t0 + u, ts);
         }
     }
-    __syncthreads();
+}
+
+// Total of the tile sums in fp64 (whole workgroup; tile_sum in LDS).
+__device__ __forceinline__ double tiles_total(const float* tile_sum, int ntiles) {
     __shared__ double s_total;
+    __syncthreads();
     if (wave_id() == 0) {
         double ps = 0.0;
         for (int t = lane_id(); t < ntiles; t += kWaveSize) ps += tile_sum[t];
@@ -248,6 +254,20 @@ __device__ __forceinline__ double weight_tiles(const WFn& f, int64_t V, float* t
     __syncthreads();
     return s_total;
 }
+
+// Pass A over the whole row by one workgroup: tile sums into LDS, and their
+// total.
+template <int TIF = kTilesInFlight, class WFn>
+__device__ __forceinline__ double weight_tiles(const WFn& f, int64_t V, float* tile_sum) {
+    const int ntiles = int((V + kTileElems - 1) / kTileElems);
+    weight_tile_range<TIF>(f, 0, ntiles, [&](int t, float ts) { tile_sum[t] = ts; });
+    return tiles_total(tile_sum, ntiles);
+}
+
+// A tile sum published to another workgroup: one 64-bit word, hi = 1 so that
+// a published word is never 0 (0 = not yet written), lo = the fp32 bits.
+__device__ __forceinline__ uint64_t pack_tile(float ts) { return (1ull << 32) | uint64_t(__float_as_uint(ts)); }
+__device__ __forceinline__ float tile_of(uint64_t w) { return __uint_as_float(uint32_t(w)); }
 
 // Pass B: given the tile sums of pass A, the smallest j with S_j >= v * W.
 // Returns -1 when the total is 0.

@@ -2,38 +2,44 @@
 // sec. 2.2, 2.7, 3.1; Speculative Decoding (dl-note), sec. 2.2-2.3 and
 // Appendix "Implementation Details"].
 //
-// One launch. Sequences are taken T > 0 first (sequence_for_slot), and
-// workgroup g streams one chunk of one row of one sequence:
-// target rows 0..gamma and (for T > 0) draft rows 0..gamma-1, each read once
-// from HBM with 16-byte loads, and publishes the chunk's statistics (online
-// max and sum of 2^(z*c - mc), or the greedy argmax) as one 64-bit atomic
-// word. The sequence's highest-numbered workgroup then waits for its other
-// words (their writers were dispatched before it), and resolves the sequence:
+// One launch. Sequences are taken T > 0 first (sequence_for_slot). Per
+// sequence, row workgroups stream one chunk of one row each: target rows
+// 0..gamma and (for T > 0) draft rows 0..gamma-1, each read once from HBM
+// with 16-byte loads, and publish the chunk's statistics (online max and sum
+// of 2^(z*c - mc), or the greedy argmax) as one 64-bit atomic word. Then the
+// sequence's H bonus workgroups wait for those words (their writers were
+// dispatched before them) and resolve the sequence (chain_resolve):
 //   accept tests u_i <= p_t(x_i)/p_d(x_i) in fp64 (one lane per position),
 //   k = first rejection by wave ballot,
 //   bonus by inverse CDF over max(p_t - p_d, 0) of row k, or p_t of row gamma,
-// then writes the outcome and zeroes the words for the next call.
+// then the last one writes the outcome and zeroes the words for the next call.
 #include "specv_chain.hpp"
 
 namespace specv {
 
 namespace {
 
-constexpr int kU = 8;  // 16-byte steps per lane per iteration
+constexpr int kU = 4;  // 16-byte steps per lane per iteration
 constexpr int kD = 0;  // prefetch form (see stream_chunk)
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void chain_verify_kernel(ChainArgs a) {
     constexpr int esz = ElemT<DT>::kBytes;
     const int R = 2 * a.gamma + 1;
-    const int64_t g = blockIdx.x;
-    const int chunk = int(g % a.S);
-    const int64_t task = g / a.S;
-    const int slot = int(task % R);
-    const int sidx = int(task / R);                      // dispatch slot of the sequence
+    const int64_t RS = int64_t(R) * a.S;                 // row workgroups per sequence
+    int sidx;                                            // dispatch slot of the sequence
+    int64_t w;
+    decode_chain(blockIdx.x, a.B, RS, a.H, a.D, sidx, w);
     const int b = sequence_for_slot(a.temperature, a.B, sidx);
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
+    uint64_t* slots = a.slots + int64_t(sidx) * RS;
+    if (w >= RS) {  // bonus workgroup: dispatched after every row of the sequence
+        chain_resolve<DT>(a, b, T, slots, RS, a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, int(w - RS));
+        return;
+    }
+    const int chunk = int(w % a.S);
+    const int slot = int(w / a.S);
     const bool draft_row = slot > a.gamma;
     const int row = draft_row ? slot - (a.gamma + 1) : slot;
     const int64_t lo = int64_t(chunk) * a.chunk;
@@ -54,16 +60,13 @@ __global__ __launch_bounds__(kThreads) void chain_verify_kernel(ChainArgs a) {
             word = pack_softmax(acc.m, acc.s);
         }
     }
-    if (threadIdx.x == 0) publish(a.slots + g, word);
-    // The sequence's last workgroup resolves it.
-    if (slot == R - 1 && chunk == a.S - 1)
-        chain_resolve<DT>(a, b, T, a.slots + int64_t(sidx) * R * a.S, int64_t(R) * a.S);
+    if (threadIdx.x == 0) publish(slots + w, word);
 }
 
 }  // namespace
 
 hipError_t launch_chain(const ChainArgs& a, int dtype, hipStream_t stream) {
-    const int64_t grid = int64_t(a.B) * (2 * a.gamma + 1) * a.S;
+    const int64_t grid = int64_t(a.B) * ((2 * a.gamma + 1) * int64_t(a.S) + a.H);
     if (dtype == DT_BF16)
         hipLaunchKernelGGL(chain_verify_kernel<DT_BF16>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
     else

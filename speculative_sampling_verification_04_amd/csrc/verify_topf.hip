@@ -8,9 +8,9 @@
 // that feeds both the softmax statistics (T > 0, row < gamma) and the top-F
 // selection, writes that row's candidates directly, and publishes its
 // statistics; target rows are as in the verify kernel. Per sequence the
-// slots are target rows 0..gamma, then draft rows 0..gamma; the last one
-// (draft row gamma) resolves the sequence. Used when every row fits one
-// workgroup (S = 1); otherwise the library runs the two kernels.
+// slots are target rows 0..gamma, then draft rows 0..gamma; the sequence's H
+// bonus workgroups follow and resolve it (chain_resolve). Used when every row
+// fits one workgroup (S = 1); otherwise the library runs the two kernels.
 #include "specv_chain.hpp"
 #include "specv_topk.hpp"
 
@@ -43,12 +43,18 @@ template <int DT, int K>
 __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     constexpr int esz = ElemT<DT>::kBytes;
     const int R1 = 2 * a.gamma + 2;
-    const int64_t g = blockIdx.x;
-    const int slot = int(g % R1);
-    const int sidx = int(g / R1);
+    int sidx;
+    int64_t w;
+    decode_chain(blockIdx.x, a.B, R1, a.H, a.D, sidx, w);
+    const int slot = int(w);
     const int b = sequence_for_slot(a.temperature, a.B, sidx);
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
+    uint64_t* slots = a.slots + int64_t(sidx) * R1;
+    if (slot >= R1) {  // bonus workgroup: dispatched after every row of the sequence
+        chain_resolve<DT>(a, b, T, slots, R1, a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, slot - R1);
+        return;
+    }
     const bool draft_row = slot > a.gamma;
     const int row = draft_row ? slot - (a.gamma + 1) : slot;
     const int64_t V = a.V;
@@ -88,13 +94,12 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
             topf_finish<DT, K>(acc, rp, V, a.F, excl, ids, vals);
         }
     }
-    if (threadIdx.x == 0) publish(a.slots + g, word);
-    if (slot == R1 - 1) chain_resolve<DT>(a, b, T, a.slots + int64_t(sidx) * R1, R1);
+    if (threadIdx.x == 0) publish(slots + slot, word);
 }
 
 template <int DT>
 hipError_t launch_dt(const ChainArgs& a, hipStream_t stream) {
-    const dim3 grid(unsigned(int64_t(a.B) * (2 * a.gamma + 2)));
+    const dim3 grid(unsigned(int64_t(a.B) * (2 * a.gamma + 2 + a.H)));
     const int K = a.F + 1;
     if (K <= 2) hipLaunchKernelGGL((verify_topf_kernel<DT, 2>), grid, dim3(kThreads), 0, stream, a);
     else if (K <= 4) hipLaunchKernelGGL((verify_topf_kernel<DT, 4>), grid, dim3(kThreads), 0, stream, a);

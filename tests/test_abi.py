@@ -59,12 +59,16 @@ def test_workspace_sizes(lib):
     st, a = ws_size(lib, "specv_verify_workspace_size", 256, 8, 128256)
     assert st == 0 and a > 0 and a % 256 == 0
     assert ws_size(lib, "specv_verify_workspace_size", 256, 8, 128256) == (0, a)
-    # one 8-byte slot per workgroup: 256 sequences x 17 rows x 1 chunk
-    assert a == 256 * 17 * 8
+    # one 8-byte word per row (256 sequences x 17 rows x 1 chunk), then one per
+    # 512-element residual tile of every sequence (251 tiles at V = 128256,
+    # shared by ceil(251 / 32) = 8 bonus workgroups)
+    assert a == 256 * 17 * 8 + 256 * 251 * 8
     st, b = ws_size(lib, "specv_verify_workspace_size", 8, 4, 32000)
     assert st == 0 and b >= 8 * 9 * 8 and b % 256 == 0      # rows split into chunks
     st, t = ws_size(lib, "specv_tree_verify_workspace_size", 32, 64, 152064)
     assert st == 0 and t == 32 * 128 * 8
+    st, c = ws_size(lib, "specv_verify_workspace_size", 4, 2, 16000)   # 32 tiles: one bonus workgroup
+    assert st == 0 and c % 256 == 0 and c < 4 * 5 * 64 * 8
     assert ws_size(lib, "specv_verify_workspace_size", 0, 8, 10)[0] == INVALID
     assert ws_size(lib, "specv_verify_workspace_size", 1, 65, 10)[0] == INVALID
     assert ws_size(lib, "specv_verify_workspace_size", 1, 0, 10)[0] == INVALID
@@ -106,7 +110,7 @@ def test_verify_validation(lib):
 
 def test_verify_topk_validation(lib):
     st, n = ws_size(lib, "specv_verify_topk_workspace_size", 256, 8, 128256)
-    assert st == 0 and n == 256 * 18 * 8            # fused: 2*gamma + 2 slots per sequence
+    assert st == 0 and n == 256 * 18 * 8 + 256 * 251 * 8   # fused: 2*gamma + 2 row words per sequence
     st, m = ws_size(lib, "specv_verify_topk_workspace_size", 8, 4, 32000)
     assert st == 0 and m == ws_size(lib, "specv_verify_workspace_size", 8, 4, 32000)[1]
 

@@ -98,6 +98,11 @@ EDGE = [
     (16, 8, 513, "bf16", "all0", 4.0, 1.5, 8),
     (2, 64, 1000, "f32", "all1", 0.5, 0.2, 9),
     (300, 2, 300, "bf16", "all0.7", 4.0, 1.0, 10),
+    # the bonus pass shared by H = ceil(tiles / 32) workgroups (at most 16)
+    (3, 3, 16385, "bf16", "all1", 3.0, 1.0, 11),          # 33 tiles: H = 2, uneven split
+    (5, 6, 70000, "bf16", "half0_half1", 4.0, 1.5, 12),   # H = 5
+    (2, 4, 300000, "f32", "all0.8", 3.0, 1.0, 13),        # 586 tiles: H = 16
+    (4, 3, 40000, "bf16", "all1", 3.0, 0.02, 14),         # nearly all accepted: p_t of row gamma
 ]
 
 
@@ -184,7 +189,9 @@ def test_one_workspace_across_shapes():
     # Calls of different shapes sharing one workspace: each call must leave it
     # zero-filled, whatever region the previous layout used.
     ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
-    shapes = [(16, 8, 513), (300, 2, 300), (3, 16, 4097), (257, 1, 64), (40, 4, 1000)]
+    shapes = [(16, 8, 513), (300, 2, 300), (3, 16, 4097), (257, 1, 64), (40, 4, 1000), (6, 3, 70000),
+              (2, 2, 300000)]
+    assert max(binding.verify_workspace_bytes(B, g, V) for B, g, V in shapes) <= ws.numel()
     for i, (B, gamma, V) in enumerate(shapes * 2):
         w = workloads.make_chain(B, gamma, V, dtype="bf16", sigma=3, noise=1, temps="half0_half1",
                                  gen_seed=100 + i, philox_seed=i)

@@ -68,7 +68,7 @@ def test_fused_equals_separate_and_oracle(name, B, gamma, V, dtype, temps, F):
 
 def test_fused_leaves_workspace_zero():
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
-    for i, (B, gamma, V) in enumerate([(300, 3, 5000), (8, 2, 9000), (260, 7, 3000)]):
+    for i, (B, gamma, V) in enumerate([(300, 3, 5000), (8, 2, 9000), (260, 3, 20000), (260, 7, 3000)]):
         w = workloads.make_chain(B, gamma, V, dtype="bf16", temps="half0_half1", gen_seed=50 + i, philox_seed=i)
         log(f"fused shared workspace {i}: B={B} gamma={gamma} V={V}")
         d = chain_to_dev(w)
