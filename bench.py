@@ -13,7 +13,8 @@ Prints one JSON line: verified rows/s (B * (gamma + 1) per step), the step
 kernel's roofline (algorithmic HBM bytes / its average duration, measured with
 HIP events on the launch stream), the separate specv_verify and
 specv_bonus_topk kernels for reference, and the oracle timed on the host cores
-on a bounded sample of the same workload.
+on a bounded sample of the same workload. A `tree` field times token-tree
+verification (MSS) on 32 trees of 64 nodes over V = 152064 (--no-tree skips).
 """
 import argparse
 import hashlib
@@ -29,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 WORKLOAD = "v128256_bf16_b256_g8"
+TREE_WORKLOAD = "tree_v152064_n64"
 METRIC = "verified vocab rows/sec + achieved HBM GB/s (% peak) at V=128256, B=256, γ=8"
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
@@ -47,6 +49,17 @@ def algorithmic_bytes(w):
     topf = w.B * (w.gamma + 1) * row
     step = 2 * w.B * (w.gamma + 1) * row
     return verify, topf, step
+
+
+def tree_algorithmic_bytes(tw):
+    """Logit bytes of one tree call: every node's target row, plus the draft
+    row of every node that has children when T > 0 (greedy trees read none)."""
+    row = tw.V * 2
+    total = 0
+    for b in range(tw.B):
+        internal = len(set(int(p) for p in tw.parent[b, 1:]))
+        total += tw.N * row + (internal * row if tw.temperature[b] > 0 else 0)
+    return total
 
 
 def kernel_source_hash():
@@ -106,6 +119,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-tree", action="store_true", help="skip the token-tree measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verification library has no "
@@ -170,6 +184,26 @@ def main():
     verify_ms = timed(lambda i: binding.verify(target, draft, tokens, temp, w.seed, i, workspace=vws, out=vout))
     topf_ms = timed(lambda i: binding.bonus_topk(draft, tokens, F, out=(out["topk"], out["topk_logits"])))
 
+    # Token-tree verification (MSS, T = 1) on its own workload: B = 32 trees of
+    # N = 64 nodes over V = 152064 bf16 logits (not part of the step).
+    tree = None
+    if not args.no_tree:
+        tw = workloads.make_workload(TREE_WORKLOAD)
+        tt = torch.from_numpy(tw.target).to(dev).to(torch.bfloat16)
+        td = torch.from_numpy(tw.draft).to(dev).to(torch.bfloat16)
+        tpar = torch.from_numpy(tw.parent).to(dev)
+        ttok = torch.from_numpy(tw.tokens).to(dev)
+        ttemp = torch.from_numpy(tw.temperature).to(dev)
+        tws = torch.zeros(binding.tree_workspace_bytes(tw.B, tw.N, tw.V), dtype=torch.uint8, device=dev)
+        tout = binding.tree_verify(tt, td, tpar, ttok, ttemp, tw.seed, 0, workspace=tws)
+        tree_ms = timed(lambda i: binding.tree_verify(tt, td, tpar, ttok, ttemp, tw.seed, i, workspace=tws, out=tout))
+        tree_bytes = tree_algorithmic_bytes(tw)
+        tree = {"workload": TREE_WORKLOAD, "kernel": "tree_verify_kernel", "B": tw.B, "N": tw.N, "V": tw.V,
+                "avg_ms": tree_ms, "algorithmic_bytes": tree_bytes, "gbps": tree_bytes / (tree_ms * 1e-3) / 1e9,
+                "trees_per_s": tw.B / (tree_ms * 1e-3),
+                "mean_accepted": float(tout["num_accepted"].float().mean().item())}
+        del tt, td, tws
+
     # Yardstick for the memory counters and for what a plain streaming kernel
     # reaches: torch's elementwise negation of 1 GiB of int32 (reads 1 GiB, writes
     # 1 GiB; larger than the 256 MB last-level cache), outside the timed region.
@@ -214,6 +248,7 @@ def main():
         "copy_yardstick": {"kernel": "torch.neg int32", "read_bytes": COPY_BYTES, "write_bytes": COPY_BYTES,
                            "avg_ms": copy_ms, "gbps": 2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9},
         "mean_accepted": mean_accepted,
+        "tree": tree,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
