@@ -109,7 +109,12 @@ specv_status specv_verify_workspace_size(int32_t batch, int32_t gamma,
  *            256-byte aligned. It must be zero-filled before its first use;
  *            every call leaves it zero-filled again, so one workspace can be
  *            reused by calls that are ordered on one stream. Calls that may
- *            run concurrently need separate workspaces.
+ *            run concurrently need separate workspaces. (Workgroups of one
+ *            call exchange statistics through it and wait only for
+ *            workgroups dispatched before them; the waits are bounded, and a
+ *            sequence whose wait ran out reports out_num_accepted = -1, after
+ *            which the caller must zero the workspace again. This is not
+ *            expected to happen.)
  */
 specv_status specv_verify(specv_logits target, specv_logits draft,
                           const int32_t* draft_tokens, const float* temperature,
@@ -191,6 +196,10 @@ specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes,
  * in walk order, then -1; out_num_accepted int32 [batch]; out_bonus int32
  * [batch]. Workspace as for specv_verify (zero-filled before first use, left
  * zero-filled by every call).
+ * Enqueues two kernels: the row statistics, then the walk, whose passes over
+ * a node's rows are shared by up to 16 workgroups per tree (a cooperative
+ * launch, so all of them are resident together; fewer per tree when the
+ * batch is large).
  */
 specv_status specv_tree_verify(specv_logits target, specv_logits draft,
                                const int32_t* parent, const int32_t* tokens,

@@ -128,6 +128,16 @@ size_t verify_topk_bytes(int64_t batch, int64_t gamma, int64_t vocab) {
     return plain > fused ? plain : fused;
 }
 
+// Tree workspace: the row words, then per tree the walk words (commands,
+// acknowledgements, tile sums).
+size_t tree_walk_offset(int64_t batch, int64_t nodes, int64_t vocab) {
+    return layout_for(batch, 2 * nodes, vocab).slot_bytes;
+}
+size_t tree_bytes(int64_t batch, int64_t nodes, int64_t vocab) {
+    const int64_t ntiles = (vocab + kTileElems - 1) / kTileElems;
+    return tree_walk_offset(batch, nodes, vocab) + round_up(size_t(batch) * (kWalkHeader + ntiles) * sizeof(uint64_t));
+}
+
 specv_status check_tree_sizes(int32_t batch, int32_t nodes, int32_t vocab) {
     if (batch < 1) return fail(SPECV_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
     if (nodes < 1 || nodes > SPECV_MAX_TREE_NODES)
@@ -184,7 +194,7 @@ specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes, int3
     if (bytes == nullptr) return fail(SPECV_ERR_INVALID_ARG, "bytes is NULL");
     specv_status st = check_tree_sizes(batch, nodes, vocab);
     if (st != SPECV_OK) return st;
-    *bytes = layout_for(batch, 2 * int64_t(nodes), vocab).slot_bytes;  // row words only
+    *bytes = tree_bytes(batch, nodes, vocab);
     return ok();
 }
 
@@ -332,7 +342,7 @@ specv_status specv_tree_verify(specv_logits target, specv_logits draft, const in
     const Layout L = layout_for(batch, 2 * int64_t(nodes), vocab);
     const int64_t grid = int64_t(batch) * 2 * nodes * L.S;
     if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch");
-    if ((st = check_workspace(workspace, workspace_bytes, L.slot_bytes)) != SPECV_OK) return st;
+    if ((st = check_workspace(workspace, workspace_bytes, tree_bytes(batch, nodes, vocab))) != SPECV_OK) return st;
 
     TreeArgs a;
     a.target = view(target);
@@ -351,6 +361,9 @@ specv_status specv_tree_verify(specv_logits target, specv_logits draft, const in
     a.out_nacc = out_num_accepted;
     a.out_bonus = out_bonus;
     a.slots = static_cast<uint64_t*>(workspace);
+    a.H = tree_walkers(vocab);
+    a.ntiles = int32_t((int64_t(vocab) + kTileElems - 1) / kTileElems);
+    a.walk = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + tree_walk_offset(batch, nodes, vocab));
     const hipError_t e = launch_tree(a, target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32,
                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_tree_verify launch failed: %s", hipGetErrorString(e));

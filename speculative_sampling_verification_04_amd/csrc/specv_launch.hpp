@@ -47,7 +47,12 @@ struct ChainArgs {
 
 // Tree verification. Per tree there are 2N row tasks (target rows of every
 // node, then draft rows of every node), each split into S chunks, one slot
-// per chunk.
+// per chunk (slots[(b * 2N + task) * S + chunk]). The walk runs H
+// workgroups per tree that meet in `walk` (kWalkHeader + ntiles words per
+// tree: two command words, one acknowledgement per walker, the tile sums).
+constexpr int kMaxWalkers = 16;
+constexpr int kWalkHeader = 2 + kMaxWalkers;
+
 struct TreeArgs {
     RowView target, draft;
     const int32_t* parent;
@@ -60,6 +65,8 @@ struct TreeArgs {
     int32_t* out_nacc;
     int32_t* out_bonus;
     uint64_t* slots;
+    int32_t H, ntiles;
+    uint64_t* walk;
 };
 
 struct TopFArgs {
@@ -123,6 +130,14 @@ __device__ __forceinline__ void decode_chain(int64_t g, int64_t B, int64_t RS, i
         sidx = int(B - D + i / H);
         w = RS + i % H;
     }
+}
+
+// Walkers per tree wanted for a vocabulary of V: about 32 tiles each (the
+// launch lowers it so that every walker of every tree is resident at once).
+inline int32_t tree_walkers(int64_t V) {
+    const int64_t ntiles = (V + kTileElems - 1) / kTileElems;
+    const int64_t h = (ntiles + 31) / 32;
+    return int32_t(h < 1 ? 1 : h > kMaxWalkers ? kMaxWalkers : h);
 }
 
 hipError_t launch_chain(const ChainArgs& a, int dtype, hipStream_t stream);

@@ -34,6 +34,10 @@ def test_named_tree_workload():
     (12, 7, 3000, "f32", "all0.6", 6, 1, 0.3, 5),
     (6, 200, 1000, "bf16", "all1", 10, 8, 0.3, 6),
     (40, 10, 8, "f32", "all1.5", 3, 4, 2.0, 7),
+    # passes shared by H = ceil(tiles / 32) walkers per tree (at most 16)
+    (6, 16, 20000, "bf16", "all1", 4, 4, 1.0, 8),          # 40 tiles: H = 2
+    (3, 24, 300000, "f32", "all0.8", 5, 4, 1.0, 9),        # 586 tiles: H = 16
+    (400, 4, 20000, "bf16", "half0_half1", 3, 2, 1.0, 10),  # 400 trees x 2 walkers may exceed residency
 ])
 def test_tree_shapes(B, N, V, dtype, temps, depth, branching, noise, seed):
     t = workloads.make_tree(B, N, V, depth=depth, branching=branching, dtype=dtype, sigma=3.0,
@@ -57,7 +61,7 @@ def test_tree_repeat_is_identical():
 def test_tree_leaves_workspace_zero():
     from speculative_sampling_verification_04_amd import binding
     ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
-    for i, (B, N, V) in enumerate([(4, 30, 700), (9, 5, 2000), (2, 64, 300)]):
+    for i, (B, N, V) in enumerate([(4, 30, 700), (9, 5, 2000), (2, 64, 300), (5, 12, 40000), (3, 8, 70000)]):
         t = workloads.make_tree(B, N, V, depth=4, branching=4, dtype="f32", temps="half0_half1",
                                 gen_seed=40 + i, philox_seed=i)
         log(f"tree shared workspace call {i}: B={B} N={N} V={V}")
