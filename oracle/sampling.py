@@ -66,20 +66,22 @@ def prob_at(p, x):
     return float(p[x]) if 0 <= x < len(p) else 0.0
 
 
-def accept(pt_x, pd_x, u):
+def accept(pt_x, pd_x, u, lenience=1.0):
     """Accept the drafted token iff u <= p_t(x)/p_d(x) [L5 sec. 2.2]; a draft
-    probability of 0 rejects [DLN Appendix]."""
+    probability of 0 rejects [DLN Appendix]. With a lenience l in (0, 1], q(x)
+    is multiplied by l before the comparison [L5 sec. 2.8]: u <= p_t/(l p_d);
+    l = 1 is the exact rule."""
     if not pd_x > 0:
         return False
-    return u <= pt_x / pd_x
+    return u <= pt_x / (lenience * pd_x)
 
 
-def accept_margin(pt_x, pd_x, u):
-    """|u - p_t(x)/p_d(x)|, the distance of the accept decision from a tie
+def accept_margin(pt_x, pd_x, u, lenience=1.0):
+    """|u - p_t(x)/(l p_d(x))|, the distance of the accept decision from a tie
     (infinite when the decision does not depend on u)."""
     if not pd_x > 0:
         return np.inf
-    return abs(u - pt_x / pd_x)
+    return abs(u - pt_x / (lenience * pd_x))
 
 
 def residual_weights(pt, pd):
@@ -119,13 +121,17 @@ class ChainOutcome:
     margins: list = field(default_factory=list)  # every decision's margin
 
 
-def verify_sequence(target, draft, draft_tokens, T, u, v):
+def verify_sequence(target, draft, draft_tokens, T, u, v, q_rows=None, lenience=1.0):
     """Verify one sequence with the uniforms given explicitly.
 
     target: [gamma+1, V] logits; draft: [>= gamma, V] logits (only rows
     0..gamma-1 are read, and none when T = 0); draft_tokens: gamma ids;
     u: gamma accept uniforms; v: the bonus uniform.
-    Follows [L5 sec. 3.1] steps 3-5 with the rule of [L5 sec. 2.2]."""
+    Follows [L5 sec. 3.1] steps 3-5 with the rule of [L5 sec. 2.2].
+    q_rows: the draft distributions the tokens were drawn from, when they are
+    not softmax(draft/T) (Saguaro sampling, oracle/ssd.py); lenience: l of
+    [L5 sec. 2.8] (1 = exact). Neither changes the greedy path, where p and q
+    are one-hot."""
     target = np.asarray(target, dtype=np.float64)
     gamma = len(draft_tokens)
     probs = np.zeros((gamma, 2), dtype=np.float64)
@@ -148,7 +154,7 @@ def verify_sequence(target, draft, draft_tokens, T, u, v):
 
     draft = np.asarray(draft, dtype=np.float64)
     pt_rows = [tempered_probs(target[i], T) for i in range(gamma + 1)]
-    pd_rows = [tempered_probs(draft[i], T) for i in range(gamma)]
+    pd_rows = list(q_rows) if q_rows is not None else [tempered_probs(draft[i], T) for i in range(gamma)]
     for i in range(gamma):
         x = int(draft_tokens[i])
         probs[i] = (prob_at(pt_rows[i], x), prob_at(pd_rows[i], x))
@@ -157,8 +163,8 @@ def verify_sequence(target, draft, draft_tokens, T, u, v):
     k = gamma
     for i in range(gamma):
         pt_x, pd_x = probs[i]
-        margins.append(accept_margin(pt_x, pd_x, u[i]))
-        if not accept(pt_x, pd_x, u[i]):
+        margins.append(accept_margin(pt_x, pd_x, u[i], lenience))
+        if not accept(pt_x, pd_x, u[i], lenience):
             k = i
             break
 
