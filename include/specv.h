@@ -19,7 +19,10 @@
  *  [DLN] Speculative Decoding (dl-note) -- sec. 2.2-2.3, Appendix
  *        "Implementation Details" (vLLM: zero draft probability rejects).
  *  [SSD] Speculative Speculative Decoding -- sec. 2.1 (outcome (k, t*)),
- *        sec. 4.1.1 (top-F bonus candidates excluding the drafted token).
+ *        sec. 4.1.1 (top-F bonus candidates excluding the drafted token; the
+ *        speculation cache and its fan-out), sec. 4.1.2 and Appendix A.2
+ *        (geometric fan-out), sec. 4.2.1 (Saguaro sampling).
+ *  [L5 sec. 2.8] the lenient rule.
  *
  * Random numbers: uniforms come from Philox4x32-10 (Salmon et al., SC'11) with
  * key = (seed mod 2^32, seed >> 32), counter = (offset mod 2^32, offset >> 32,
@@ -166,6 +169,58 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft,
                                float* out_probs, float* out_bonus_mass,
                                int32_t* out_topk, float* out_topk_logits,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace specv_verify_cache needs for (batch, gamma, vocab). */
+specv_status specv_verify_cache_workspace_size(int32_t batch, int32_t gamma,
+                                               int32_t vocab, size_t* bytes);
+
+/*
+ * Chain verification for SSD's speculation cache [SSD sec. 4.1.1, 4.2.1;
+ * L5 sec. 2.8]: specv_verify_topk generalised in three ways.
+ *
+ *  fanout: HOST int32 [gamma+1]. Position k has F_k = fanout[k] cache
+ *          candidates (0 <= F_k <= min(SPECV_MAX_TOPF, vocab - 1), at least
+ *          one F_k >= 1): the F_k largest draft logits of row k, without
+ *          draft_tokens[b][k] (k < gamma). out_topk / out_topk_logits are
+ *          [batch][gamma+1][Fmax], Fmax = max F_k; row k holds F_k entries, then
+ *          -1 (-inf). See specv_geometric_fanout for a budgeted choice.
+ *  saguaro_C: in [0, 1]. The draft tokens of T > 0 sequences were sampled from
+ *          Saguaro sampling sigma_{F_k,C}(draft[b][k] / T): weight
+ *          C * exp(z_t / T) on the F_k largest logits of the row (ties: lower
+ *          index first), exp(z_t / T) elsewhere. That distribution is the q of
+ *          the accept test and of the residual. 1 = plain softmax. (If the
+ *          total weight is 0, the plain softmax is used.)
+ *  lenience: l in (0, 1]. Accept iff q(x) > 0 and u <= p_t(x) / (l q(x));
+ *          1 = the exact rule. The residual stays max(p_t - q, 0).
+ *  out_hit: device int32 [batch] or NULL: 1 iff the outcome (k, bonus) is in
+ *          the cache, i.e. the bonus is one of the F_k candidates at k.
+ *
+ * Greedy sequences (T == 0) verify as in specv_verify; C and l do not apply.
+ * Other arguments, outputs and the workspace as for specv_verify_topk. One
+ * kernel streams every target and draft row once at every batch size.
+ */
+specv_status specv_verify_cache(specv_logits target, specv_logits draft,
+                                const int32_t* draft_tokens, const float* temperature,
+                                int32_t batch, int32_t gamma, int32_t vocab,
+                                const int32_t* fanout, float saguaro_C, float lenience,
+                                uint64_t seed, uint64_t offset,
+                                int32_t* out_tokens, int32_t* out_num_accepted,
+                                float* out_probs, float* out_bonus_mass,
+                                int32_t* out_topk, float* out_topk_logits,
+                                int32_t* out_hit, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * Saguaro's geometric fan-out [SSD sec. 4.1.2, Appendix A.2, Theorem 12]
+ * (host only, no GPU): for acceptance rate a in (0, 1) and a power-law hit
+ * rate 1 - F^-r (r > 0), the fan-outs F_k = F_0 a^(k/(1+r)) for k < K and
+ * F_K = F_0 a^(K/(1+r)) (1-a)^(-1/(1+r)), with F_0 such that they sum to
+ * `budget`, rounded to integers by largest remainder (floors first, then +1
+ * to the largest fractional parts, lower k first on equal parts) so that the
+ * K + 1 entries of out (HOST int32) sum to budget. 0 <= K <= SPECV_MAX_GAMMA.
+ */
+specv_status specv_geometric_fanout(int32_t K, double accept_rate, double r,
+                                    int32_t budget, int32_t* out);
 
 /* Bytes of workspace specv_tree_verify needs for (batch, nodes, vocab). */
 specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes,

@@ -30,7 +30,10 @@ def rank_order(z):
 
 def bonus_topf(z, F, exclude=None):
     """The F candidate bonus tokens of one draft row: the first F ids of
-    rank_order(z) once the excluded id (the drafted token, or None) is dropped."""
+    rank_order(z) once the excluded id (the drafted token, or None) is dropped.
+    F = 0 gives no candidates (a position the cache does not cover)."""
+    if F <= 0:
+        return []
     picks = []
     for j in rank_order(z):
         if exclude is not None and int(j) == int(exclude):

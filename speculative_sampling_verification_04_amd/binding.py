@@ -21,6 +21,7 @@ STATUS_NAMES = {0: "SPECV_OK", 1: "SPECV_ERR_INVALID_ARG", 2: "SPECV_ERR_WORKSPA
 EXPORTED = ("specv_verify_workspace_size", "specv_verify", "specv_bonus_topk",
             "specv_verify_topk_workspace_size", "specv_verify_topk",
             "specv_tree_verify_workspace_size", "specv_tree_verify",
+            "specv_verify_cache_workspace_size", "specv_verify_cache", "specv_geometric_fanout",
             "specv_uniforms", "specv_last_error", "specv_version")
 
 
@@ -65,6 +66,10 @@ def load_library(path=LIB_PATH):
             "specv_tree_verify": [Logits, Logits, P, P, P, I32, I32, I32, U64, U64,
                                   P, P, P, P, SZ, P],
             "specv_uniforms": [U64, U64, I32, I32, I32, P, P],
+            "specv_verify_cache_workspace_size": [I32, I32, I32, SZP],
+            "specv_verify_cache": [Logits, Logits, P, P, I32, I32, I32, P, ctypes.c_float, ctypes.c_float,
+                                   U64, U64, P, P, P, P, P, P, P, P, SZ, P],
+            "specv_geometric_fanout": [I32, ctypes.c_double, ctypes.c_double, I32, P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -213,6 +218,62 @@ def verify_topk(target, draft, draft_tokens, temperature, F, seed, offset=0, *,
                                  _ptr(out["bonus_mass"]), _ptr(out["topk"]), _ptr(out["topk_logits"]),
                                  _ptr(ws), ws.numel(), _stream(dev)))
     return out
+
+
+def verify_cache_workspace_bytes(batch, gamma, vocab):
+    lib = load_library()
+    n = ctypes.c_size_t()
+    _check(lib.specv_verify_cache_workspace_size(batch, gamma, vocab, ctypes.byref(n)))
+    return n.value
+
+
+def verify_cache(target, draft, draft_tokens, temperature, fanout, seed, offset=0, *, saguaro_C=1.0,
+                 lenience=1.0, with_probs=True, with_mass=True, with_logits=True, with_hit=True,
+                 workspace=None, out=None):
+    """Verification for SSD's speculation cache (specv_verify_cache): per-position
+    fan-out `fanout` (gamma + 1 ints), Saguaro draft sampling with C =
+    saguaro_C, lenience l. draft must be [B, gamma+1, V]. Returns dict(tokens,
+    num_accepted, probs, bonus_mass, topk [B, gamma+1, max F_k], topk_logits,
+    hit [B])."""
+    lib = load_library()
+    B, rows, V = target.shape
+    gamma = rows - 1
+    dev = target.device
+    _int32(draft_tokens, (B, gamma), "draft_tokens")
+    if temperature.dtype != torch.float32 or temperature.shape != (B,) or not temperature.is_contiguous():
+        raise ValueError("temperature must be a contiguous float32 tensor of shape (B,)")
+    if tuple(draft.shape) != (B, rows, V):
+        raise ValueError("draft must be [B, gamma+1, V]")
+    if len(fanout) != rows:
+        raise ValueError("fanout must have gamma + 1 entries")
+    fan = (ctypes.c_int32 * rows)(*[int(f) for f in fanout])
+    fmax = max(int(f) for f in fanout)
+    if out is None:
+        out = dict(
+            tokens=torch.empty((B, rows), dtype=torch.int32, device=dev),
+            num_accepted=torch.empty((B,), dtype=torch.int32, device=dev),
+            probs=torch.empty((B, gamma, 2), dtype=torch.float32, device=dev) if with_probs else None,
+            bonus_mass=torch.empty((B,), dtype=torch.float32, device=dev) if with_mass else None,
+            topk=torch.empty((B, rows, max(1, fmax)), dtype=torch.int32, device=dev),
+            topk_logits=torch.empty((B, rows, max(1, fmax)), dtype=torch.float32, device=dev) if with_logits else None,
+            hit=torch.empty((B,), dtype=torch.int32, device=dev) if with_hit else None)
+    nbytes = verify_cache_workspace_bytes(B, gamma, V)
+    ws = workspace if workspace is not None else _workspaces.get(nbytes, dev)
+    _check(lib.specv_verify_cache(logits_view(target), logits_view(draft), _ptr(draft_tokens), _ptr(temperature),
+                                  B, gamma, V, ctypes.cast(fan, ctypes.c_void_p), float(saguaro_C), float(lenience),
+                                  seed, offset, _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out["probs"]),
+                                  _ptr(out["bonus_mass"]), _ptr(out["topk"]), _ptr(out["topk_logits"]),
+                                  _ptr(out["hit"]), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def geometric_fanout(K, accept_rate, r, budget):
+    """Theorem 12's fan-outs rounded to integers summing to budget
+    (specv_geometric_fanout; host only). Returns a list of K + 1 ints."""
+    lib = load_library()
+    out = (ctypes.c_int32 * (K + 1))()
+    _check(lib.specv_geometric_fanout(K, float(accept_rate), float(r), budget, ctypes.cast(out, ctypes.c_void_p)))
+    return list(out)
 
 
 def bonus_topk(draft, draft_tokens, F, *, with_logits=True, out=None):

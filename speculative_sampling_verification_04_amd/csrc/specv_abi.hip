@@ -2,6 +2,7 @@
 // workspace sizing and kernel launches. Nothing here allocates device memory
 // or synchronises; a non-OK status means nothing was launched (except
 // SPECV_ERR_HIP, a failed launch).
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -85,13 +86,25 @@ Layout layout_for(int64_t batch, int64_t row_tasks_per_seq, int64_t vocab) {
     return L;
 }
 
-// Layout of the fused kernel: 2*gamma + 2 unsplit rows per sequence.
-Layout fused_layout(int64_t batch, int64_t gamma, int64_t vocab) {
+// Layout of the fused kernel: 2*gamma + 2 unsplit rows per sequence, plus
+// three cache words per draft row when the cache outputs are on.
+Layout fused_layout(int64_t batch, int64_t gamma, int64_t vocab, bool cache_words = false) {
     Layout L = layout_for(batch, 2 * gamma + 2, vocab);
     L.S = 1;
     L.chunk = vocab;
-    L.slot_bytes = round_up(size_t(batch) * (2 * gamma + 2) * sizeof(uint64_t));
+    const int64_t words = 2 * gamma + 2 + (cache_words ? 3 * (gamma + 1) : 0);
+    L.slot_bytes = round_up(size_t(batch) * words * sizeof(uint64_t));
     return L;
+}
+
+// Plain chain verification: softmax drafts, exact rule, no cache outputs.
+void set_plain(ChainArgs& a, int32_t F) {
+    a.F = F;
+    for (int k = 0; k < kMaxPositions; ++k) a.Fk[k] = F;
+    a.cache_words = 0;
+    a.C = 1.0f;
+    a.lenience = 1.0f;
+    a.out_hit = nullptr;
 }
 
 void set_bonus(ChainArgs& a, const Layout& L, int64_t row_words, void* workspace) {
@@ -224,6 +237,7 @@ specv_status specv_verify(specv_logits target, specv_logits draft, const int32_t
     a.gamma = gamma;
     a.V = vocab;
     set_bonus(a, L, (2 * int64_t(gamma) + 1) * L.S, workspace);
+    set_plain(a, 0);
     a.seed = seed;
     a.offset = offset;
     a.out_tokens = out_tokens;
@@ -276,7 +290,7 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
     a.out_nacc = out_num_accepted;
     a.out_probs = out_probs;
     a.out_mass = out_bonus_mass;
-    a.F = F;
+    set_plain(a, F);
     a.out_topk = out_topk;
     a.out_topk_logits = out_topk_logits;
     const int dt = target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32;
@@ -299,6 +313,111 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
         }
     }
     if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_verify_topk launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+specv_status specv_verify_cache_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, size_t* bytes) {
+    if (bytes == nullptr) return fail(SPECV_ERR_INVALID_ARG, "bytes is NULL");
+    specv_status st = check_chain_sizes(batch, gamma, vocab);
+    if (st != SPECV_OK) return st;
+    *bytes = fused_layout(batch, gamma, vocab, true).total();
+    return ok();
+}
+
+specv_status specv_verify_cache(specv_logits target, specv_logits draft, const int32_t* draft_tokens,
+                                const float* temperature, int32_t batch, int32_t gamma, int32_t vocab,
+                                const int32_t* fanout, float saguaro_C, float lenience, uint64_t seed,
+                                uint64_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                float* out_bonus_mass, int32_t* out_topk, float* out_topk_logits, int32_t* out_hit,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    specv_status st = check_chain_sizes(batch, gamma, vocab);
+    if (st != SPECV_OK) return st;
+    if ((st = check_logits("target", target)) != SPECV_OK) return st;
+    if ((st = check_logits("draft", draft)) != SPECV_OK) return st;
+    if (target.dtype != draft.dtype)
+        return fail(SPECV_ERR_UNSUPPORTED, "target and draft must have the same dtype");
+    if (fanout == nullptr) return fail(SPECV_ERR_INVALID_ARG, "fanout is NULL");
+    int32_t fmax = 0;
+    for (int k = 0; k <= gamma; ++k) {
+        if (fanout[k] < 0 || fanout[k] > SPECV_MAX_TOPF || fanout[k] > vocab - 1)
+            return fail(SPECV_ERR_INVALID_ARG, "fanout[%d] = %d must be in [0, min(%d, vocab - 1)]", k, fanout[k],
+                        SPECV_MAX_TOPF);
+        fmax = fanout[k] > fmax ? fanout[k] : fmax;
+    }
+    if (fmax < 1) return fail(SPECV_ERR_INVALID_ARG, "at least one fanout entry must be >= 1");
+    if (!(saguaro_C >= 0.0f && saguaro_C <= 1.0f))
+        return fail(SPECV_ERR_INVALID_ARG, "saguaro_C must be in [0, 1] (got %g)", double(saguaro_C));
+    if (!(lenience > 0.0f && lenience <= 1.0f))
+        return fail(SPECV_ERR_INVALID_ARG, "lenience must be in (0, 1] (got %g)", double(lenience));
+    if (!draft_tokens || !temperature || !out_tokens || !out_num_accepted || !out_topk)
+        return fail(SPECV_ERR_INVALID_ARG,
+                    "draft_tokens, temperature, out_tokens, out_num_accepted and out_topk are required");
+    const Layout L = fused_layout(batch, gamma, vocab, true);
+    const int64_t grid = int64_t(batch) * (2 * gamma + 2 + L.H);
+    if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch");
+    if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
+
+    ChainArgs a{};
+    a.target = view(target);
+    a.draft = view(draft);
+    a.tokens = draft_tokens;
+    a.temperature = temperature;
+    a.B = batch;
+    a.gamma = gamma;
+    a.V = vocab;
+    set_bonus(a, L, 2 * int64_t(gamma) + 2, workspace);
+    a.seed = seed;
+    a.offset = offset;
+    a.out_tokens = out_tokens;
+    a.out_nacc = out_num_accepted;
+    a.out_probs = out_probs;
+    a.out_mass = out_bonus_mass;
+    a.F = fmax;
+    for (int k = 0; k < kMaxPositions; ++k) a.Fk[k] = k <= gamma ? fanout[k] : 0;
+    a.out_topk = out_topk;
+    a.out_topk_logits = out_topk_logits;
+    a.cache_words = 1;
+    a.C = saguaro_C;
+    a.lenience = lenience;
+    a.out_hit = out_hit;
+    const hipError_t e = launch_verify_topf(a, target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32,
+                                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_verify_cache launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+specv_status specv_geometric_fanout(int32_t K, double accept_rate, double r, int32_t budget, int32_t* out) {
+    if (out == nullptr) return fail(SPECV_ERR_INVALID_ARG, "out is NULL");
+    if (K < 0 || K > SPECV_MAX_GAMMA) return fail(SPECV_ERR_INVALID_ARG, "K must be in [0, %d]", SPECV_MAX_GAMMA);
+    if (!(accept_rate > 0.0 && accept_rate < 1.0))
+        return fail(SPECV_ERR_INVALID_ARG, "accept_rate must be in (0, 1) (got %g)", accept_rate);
+    if (!(r > 0.0 && r < 1e6)) return fail(SPECV_ERR_INVALID_ARG, "r must be > 0 (got %g)", r);
+    if (budget < 0) return fail(SPECV_ERR_INVALID_ARG, "budget must be >= 0");
+    // Theorem 12: F_k = F0 a^(k/(1+r)) (k < K), F_K = F0 a^(K/(1+r)) (1-a)^(-1/(1+r)),
+    // F0 from the budget.
+    const double e = 1.0 / (1.0 + r);
+    const double g = pow(accept_rate, e);
+    const double tail = pow(accept_rate, K * e) * pow(1.0 - accept_rate, -e);
+    const double F0 = double(budget) / (tail + (1.0 - pow(g, K)) / (1.0 - g));
+    double F[SPECV_MAX_GAMMA + 1];
+    for (int k = 0; k < K; ++k) F[k] = F0 * pow(accept_rate, k * e);
+    F[K] = F0 * tail;
+    // Largest remainder: floors, then +1 to the largest fractional parts
+    // (lower k first among equal parts) until the budget is met.
+    int64_t used = 0;
+    for (int k = 0; k <= K; ++k) {
+        out[k] = int32_t(floor(F[k]));
+        used += out[k];
+    }
+    bool taken[SPECV_MAX_GAMMA + 1] = {};
+    for (int64_t left = budget - used; left > 0; --left) {
+        int best = -1;
+        for (int k = 0; k <= K; ++k)
+            if (!taken[k] && (best < 0 || F[k] - floor(F[k]) > F[best] - floor(F[best]))) best = k;
+        if (best < 0) break;
+        taken[best] = true;
+        ++out[best];
+    }
     return ok();
 }
 

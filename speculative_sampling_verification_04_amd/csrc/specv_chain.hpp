@@ -42,6 +42,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T
     const bool greedy = !(T > 0.0f);
     const bool last = h == a.H - 1;
     const float c = greedy ? 0.0f : log2e_over(T);
+    const uint64_t* extra = slots + 2 * gamma + 2;  // the cache words, when a.cache_words
 
     if (greedy && !last) return;  // the greedy bonus is an argmax: nothing to share
 
@@ -49,6 +50,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T
     __shared__ int32_t s_k;
     __shared__ int32_t s_bonus;
     __shared__ float s_mass;
+    __shared__ uint64_t s_cache_word;
     __shared__ float tile_sum[kMaxTiles];
 
     if (!wait_slots(slots, nslots)) {  // never expected: see wait_slots
@@ -80,11 +82,21 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T
             } else {
                 double pt = 0.0, pd = 0.0;
                 if (in_range) {
+                    const float zd = load_elem<DT>(row_ptr(a.draft, esz, b, i), x);
                     pt = prob_of(load_elem<DT>(row_ptr(a.target, esz, b, i), x), c, st[i]);
-                    pd = prob_of(load_elem<DT>(row_ptr(a.draft, esz, b, i), x), c, st[gamma + 1 + i]);
+                    RowStats qs = st[gamma + 1 + i];
+                    double scale = 1.0;
+                    if (a.cache_words) {  // Saguaro sampling: q = sigma_{F_i,C}(draft_i / T)
+                        const uint64_t zw = peek(extra + 3 * i);
+                        if ((zw >> 32) == 1ull) {
+                            qs.Z = double(__uint_as_float(uint32_t(zw)));
+                            if (full_key(zd, x) + 1ull >= peek(extra + 3 * i + 1)) scale = double(a.C);
+                        }
+                    }
+                    pd = scale * prob_of(zd, c, qs);
                 }
                 const float u = stream_uniform(a.seed, a.offset, uint32_t(b), 0u, uint32_t(i));
-                reject = !(pd > 0.0 && double(u) <= pt / pd);
+                reject = !(pd > 0.0 && double(u) <= pt / (double(a.lenience) * pd));
                 pt_out = float(pt);
                 pd_out = float(pd);
             }
@@ -112,7 +124,20 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T
         res.V = a.V;
         tgt.p = res.p;
         tgt.V = a.V;
-        if (k < gamma) res.q.init(row_ptr(a.draft, esz, b, k), c, st[gamma + 1 + k]);
+        if (k < gamma) {
+            RowStats qs = st[gamma + 1 + k];
+            uint64_t top_word = 0ull;
+            if (a.cache_words) {
+                const uint64_t zw = peek(extra + 3 * k);
+                if ((zw >> 32) == 1ull) {
+                    qs.Z = double(__uint_as_float(uint32_t(zw)));
+                    top_word = peek(extra + 3 * k + 1);
+                }
+            }
+            res.q.init(row_ptr(a.draft, esz, b, k), c, qs);
+            res.q.scale = a.C;
+            res.q.top_word = top_word;
+        }
 
         // Tile sums of the bonus weights: residual of row k, or p_t of row gamma.
         if (a.H > 1) {
@@ -150,6 +175,8 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T
         }
         if (threadIdx.x == 0) { s_bonus = bonus; s_mass = mass; }
     }
+    if (threadIdx.x == 0) s_cache_word = (a.out_hit && a.cache_words) ? peek(extra + 3 * k + 2) : ~0ull;
+    __syncthreads();
     zero_slots(slots, nslots);   // consumed: back to the resting state
     __syncthreads();
 
@@ -162,6 +189,15 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T
     if (threadIdx.x == 0) {
         a.out_nacc[b] = k;
         if (a.out_mass) a.out_mass[b] = s_mass;
+        if (a.out_hit) {  // (k, bonus) is in the cache iff the bonus is a candidate at k
+            const uint64_t cw = s_cache_word;
+            const int32_t bonus = s_bonus;
+            const int32_t xk = k < gamma ? a.tokens[int64_t(b) * gamma + k] : -1;
+            bool hit = false;
+            if (cw != ~0ull && bonus >= 0 && bonus < a.V && bonus != xk)
+                hit = full_key(load_elem<DT>(row_ptr(a.draft, esz, b, k), bonus), bonus) + 1ull >= cw;
+            a.out_hit[b] = hit ? 1 : 0;
+        }
     }
 }
 

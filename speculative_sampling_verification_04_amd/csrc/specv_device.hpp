@@ -231,7 +231,9 @@ __device__ __forceinline__ uint64_t pack_slot(float hi, uint32_t lo) {
 __device__ __forceinline__ uint64_t pack_softmax(float m, double s) { return pack_slot(m, ~__float_as_uint(float(s))); }
 __device__ __forceinline__ uint64_t pack_argmax(float v, int32_t idx) { return pack_slot(v, ~uint32_t(idx)); }
 __device__ __forceinline__ uint64_t pack_skipped() { return pack_slot(-INFINITY, ~__float_as_uint(0.0f)); }
-__device__ __forceinline__ bool slot_ready(uint64_t w) { return uint32_t(w) != 0u; }
+// Any published word is nonzero as a whole (the row words even in their low
+// half); tile and cache words rely on the whole-word test.
+__device__ __forceinline__ bool slot_ready(uint64_t w) { return w != 0ull; }
 __device__ __forceinline__ float slot_hi(uint64_t w) { return __uint_as_float(uint32_t(w >> 32)); }
 __device__ __forceinline__ float slot_s(uint64_t w) { return __uint_as_float(~uint32_t(w)); }
 __device__ __forceinline__ int32_t slot_idx(uint64_t w) { return int32_t(~uint32_t(w)); }

@@ -10,6 +10,8 @@
 
 namespace specv {
 
+constexpr int kMaxPositions = 65;  // gamma + 1 <= SPECV_MAX_GAMMA + 1
+
 struct RowView {
     const void* data;
     int64_t stride_seq;
@@ -39,10 +41,21 @@ struct ChainArgs {
     int32_t H, ntiles;
     uint64_t* tiles;
     int32_t D;               // bonus workgroups trail their rows by D sequences (see decode_chain)
-    // Fused top-F (verify_topf_kernel only).
+    // Fused top-F (verify_topf_kernel only): F_k candidates at position k
+    // (Fk[k] <= F), written with row stride F.
     int32_t F;
     int32_t* out_topk;
     float* out_topk_logits;
+    int32_t Fk[kMaxPositions];
+    // SSD cache extensions (verify_topf_kernel only; off when cache_words = 0):
+    // draft distribution sigma_{F_k,C} (C = 1: softmax), lenience l, and the
+    // hit flag. With cache_words, every draft row also publishes three words
+    // (after the 2*gamma + 2 row words of its sequence): the sigma
+    // normaliser, the sigma threshold key and the cache threshold key.
+    int32_t cache_words;
+    float C;
+    float lenience;
+    int32_t* out_hit;
 };
 
 // Tree verification. Per tree there are 2N row tasks (target rows of every

@@ -169,21 +169,32 @@ __device__ __forceinline__ void load_group(const void* row, int64_t j0, int64_t 
     }
 }
 
-// Probabilities p = 2^(z*c - mc) / Z of one row (fp32).
+// Probabilities p = 2^(z*c - mc) / Z of one row (fp32). With a threshold key
+// (Saguaro sampling), the elements whose key reaches it (the row's top F) are
+// scaled by `scale` and Z is the correspondingly reduced normaliser.
 template <int DT>
 struct ProbRow {
     const void* row;
     float c, nmc, invZ;
     bool vec;
+    float scale;          // factor on the top-F elements (1: none)
+    uint64_t top_word;    // threshold key + 1 (0: no scaling)
     __device__ void init(const void* r, float c_, const RowStats& st) {
         row = r; c = c_; nmc = -st.mc; invZ = float(1.0 / st.Z);
         vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0;
+        scale = 1.0f; top_word = 0ull;
     }
-    __device__ __forceinline__ void probs(const Raw8<DT>& raw, float p[kLaneElems]) const {
+    // Elements j0 .. j0 + 7.
+    __device__ __forceinline__ void probs(const Raw8<DT>& raw, int64_t j0, float p[kLaneElems]) const {
         float z[kLaneElems];
         unpack8<DT>(raw, z);
 #pragma unroll
         for (int e = 0; e < kLaneElems; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(z[e], c, nmc)) * invZ;
+        if (top_word != 0ull) {
+#pragma unroll
+            for (int e = 0; e < kLaneElems; ++e)
+                if (full_key(z[e], j0 + e) + 1ull >= top_word) p[e] *= scale;
+        }
     }
 };
 
@@ -194,7 +205,7 @@ struct TargetWeights {
     ProbRow<DT> p;
     int64_t V;
     __device__ __forceinline__ void load(int64_t j0, Raw& r) const { load_group<DT>(p.row, j0, V, p.vec, r.p); }
-    __device__ __forceinline__ void weights(const Raw& r, float w[kLaneElems]) const { p.probs(r.p, w); }
+    __device__ __forceinline__ void weights(const Raw& r, int64_t j0, float w[kLaneElems]) const { p.probs(r.p, j0, w); }
 };
 
 // Weights max(p - coef * q, 0): the chain residual (coef = 1) and the MSS
@@ -209,10 +220,10 @@ struct ResidualWeights {
         load_group<DT>(p.row, j0, V, p.vec, r.p);
         load_group<DT>(q.row, j0, V, q.vec, r.q);
     }
-    __device__ __forceinline__ void weights(const Raw& r, float w[kLaneElems]) const {
+    __device__ __forceinline__ void weights(const Raw& r, int64_t j0, float w[kLaneElems]) const {
         float a[kLaneElems], b[kLaneElems];
-        p.probs(r.p, a);
-        q.probs(r.q, b);
+        p.probs(r.p, j0, a);
+        q.probs(r.q, j0, b);
 #pragma unroll
         for (int e = 0; e < kLaneElems; ++e) w[e] = fmaxf(fmaf(-coef, b[e], a[e]), 0.0f);
     }
@@ -233,7 +244,7 @@ __device__ __forceinline__ void weight_tile_range(const WFn& f, int t_lo, int t_
         for (int u = 0; u < TIF; ++u) {
             if (t0 + u >= t_hi) break;
             float w[kLaneElems];
-            f.weights(raw[u], w);
+            f.weights(raw[u], int64_t(t0 + u) * kTileElems + lane_id() * kLaneElems, w);
             const float ls = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
             const float ts = wave_sum(ls);
             if (lane_id() == 0) sink(t0 + u, ts);
@@ -318,7 +329,7 @@ __device__ __forceinline__ int32_t sample_from_tiles(const WFn& f, int64_t V, fl
         typename WFn::Raw raw;
         f.load(int64_t(tile) * kTileElems + lane * kLaneElems, raw);
         float w[kLaneElems];
-        f.weights(raw, w);
+        f.weights(raw, int64_t(tile) * kTileElems + lane * kLaneElems, w);
         double ls = 0.0;
 #pragma unroll
         for (int e = 0; e < kLaneElems; ++e) ls += double(w[e]);

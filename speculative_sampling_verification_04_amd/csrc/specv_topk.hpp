@@ -165,10 +165,12 @@ struct TopKAcc {
 // Ends a row's selection (whole workgroup, after streaming): every wave
 // compacts its candidates to at most K groups, the keys that reach the largest
 // wave threshold are gathered, wave 0 pops the F + 1 largest, and thread 0
-// writes the first F ids (and logits) that are not `excl`.
+// writes the first F ids (and logits) that are not `excl`, then -1 up to
+// Fmax entries. Returns the F + 1 largest keys of the row in LDS (0 = none),
+// before the exclusion; they stay valid until the caller's next barrier.
 template <int DT, int K>
-__device__ __forceinline__ void topf_finish(TopKAcc<DT, K>& acc, const void* rp, int64_t V, int F, int32_t excl,
-                            int32_t* out_ids, float* out_logits) {
+__device__ __forceinline__ const uint64_t* topf_finish(TopKAcc<DT, K>& acc, const void* rp, int64_t V, int F,
+                                                       int Fmax, int32_t excl, int32_t* out_ids, float* out_logits) {
     __shared__ uint64_t keys[kWaves * kLaneElems * K];
     __shared__ uint64_t s_theta[kWaves];
     __shared__ uint64_t s_pick[K];
@@ -220,12 +222,30 @@ __device__ __forceinline__ void topf_finish(TopKAcc<DT, K>& acc, const void* rp,
             if (out_logits) out_logits[n] = key_logit(uint32_t(key >> 32));
             ++n;
         }
-        for (; n < F; ++n) {  // fewer candidates than F (only when vocab <= F)
+        for (; n < Fmax; ++n) {  // unused entries (and fewer candidates than F, only when vocab <= F)
             out_ids[n] = -1;
             if (out_logits) out_logits[n] = -INFINITY;
         }
     }
     __syncthreads();
+    return s_pick;
+}
+
+// The F-th largest key of the row (no exclusion), or 0 when F = 0: a key is
+// among the row's top F iff it is >= this.
+__device__ __forceinline__ uint64_t topf_sigma_key(const uint64_t* pick, int F) { return F > 0 ? pick[F - 1] : 0ull; }
+
+// The F-th largest key once `excl` is dropped, or 0 when F = 0: a key other
+// than excl's is a cache candidate iff it is >= this.
+__device__ __forceinline__ uint64_t topf_cache_key(const uint64_t* pick, int F, int32_t excl) {
+    int n = 0;
+    for (int r = 0; r <= F && n < F; ++r) {
+        const uint64_t key = pick[r];
+        if (key == 0) break;
+        if (int32_t(~uint32_t(key)) == excl) continue;
+        if (++n == F) return key;
+    }
+    return 0ull;
 }
 
 }  // namespace specv

@@ -50,9 +50,10 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     const int b = sequence_for_slot(a.temperature, a.B, sidx);
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
-    uint64_t* slots = a.slots + int64_t(sidx) * R1;
+    const int64_t words = R1 + (a.cache_words ? 3 * (a.gamma + 1) : 0);  // per sequence
+    uint64_t* slots = a.slots + int64_t(sidx) * words;
     if (slot >= R1) {  // bonus workgroup: dispatched after every row of the sequence
-        chain_resolve<DT>(a, b, T, slots, R1, a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, slot - R1);
+        chain_resolve<DT>(a, b, T, slots, words, a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, slot - R1);
         return;
     }
     const bool draft_row = slot > a.gamma;
@@ -78,20 +79,40 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
         __shared__ uint64_t cand_key[kWaves][kCandCap];
         const void* rp = row_ptr(a.draft, esz, b, row);
         const int32_t excl = row < a.gamma ? a.tokens[int64_t(b) * a.gamma + row] : -1;
+        const int Fk = a.Fk[row];
         int32_t* ids = a.out_topk + (int64_t(b) * (a.gamma + 1) + row) * a.F;
         float* vals = a.out_topk_logits ? a.out_topk_logits + (int64_t(b) * (a.gamma + 1) + row) * a.F : nullptr;
+        uint64_t zword = 2ull << 32;  // sigma normaliser word: softmax (no Saguaro scaling on this row)
+        const uint64_t* pick;
         if (!greedy && row < a.gamma) {
             SoftmaxTopK<DT, K> acc(log2e_over(T));
             acc.tk.init(rp, V, cand[wave_id()], cand_key[wave_id()]);
             stream_chunk<DT, kDraftU, kDraftD>(rp, 0, V, acc);
             block_merge_softmax(acc.sm.m, acc.sm.mc, acc.sm.s);
             word = pack_softmax(acc.sm.m, acc.sm.s);
-            topf_finish<DT, K>(acc.tk, rp, V, a.F, excl, ids, vals);
+            pick = topf_finish<DT, K>(acc.tk, rp, V, Fk, a.F, excl, ids, vals);
+            if (a.cache_words && a.C < 1.0f && Fk > 0 && threadIdx.x == 0) {
+                // sigma_{F,C}: the normaliser loses (1 - C) of the top-F terms,
+                // taken relative to the same reference m*c as the row sum.
+                const float c = log2e_over(T);
+                double top = 0.0;
+                for (int r = 0; r < Fk; ++r)
+                    if (pick[r] != 0ull)
+                        top += exp2(double(key_logit(uint32_t(pick[r] >> 32))) * double(c) - double(acc.sm.mc));
+                const double zs = acc.sm.s - (1.0 - double(a.C)) * top;
+                if (zs > 0.0) zword = (1ull << 32) | uint64_t(__float_as_uint(float(zs)));
+            }
         } else {
             TopKAcc<DT, K> acc;
             acc.init(rp, V, cand[wave_id()], cand_key[wave_id()]);
             stream_chunk<DT, kDraftU, kDraftD>(rp, 0, V, acc);
-            topf_finish<DT, K>(acc, rp, V, a.F, excl, ids, vals);
+            pick = topf_finish<DT, K>(acc, rp, V, Fk, a.F, excl, ids, vals);
+        }
+        if (a.cache_words && threadIdx.x == 0) {
+            uint64_t* extra = slots + R1 + 3 * row;
+            publish(extra + 0, zword);
+            publish(extra + 1, Fk > 0 ? topf_sigma_key(pick, Fk) + 1ull : ~0ull);
+            publish(extra + 2, Fk > 0 ? topf_cache_key(pick, Fk, excl) + 1ull : ~0ull);
         }
     }
     if (threadIdx.x == 0) publish(slots + slot, word);

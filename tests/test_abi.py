@@ -34,8 +34,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("specv_verify", "specv_bonus_topk", "specv_tree_verify", "specv_verify_topk",
               "specv_verify_workspace_size", "specv_tree_verify_workspace_size",
-              "specv_verify_topk_workspace_size",
-              "specv_uniforms", "specv_last_error", "specv_version"):
+              "specv_verify_topk_workspace_size", "specv_verify_cache", "specv_verify_cache_workspace_size",
+              "specv_geometric_fanout", "specv_uniforms", "specv_last_error", "specv_version"):
         assert n in names
 
 
@@ -146,6 +146,53 @@ def test_tree_validation(lib):
     assert call(parent=None) == INVALID
     assert call(ws_bytes=0) == WORKSPACE
     assert call(B=0) == INVALID
+
+
+def test_verify_cache_validation(lib):
+    st, n = ws_size(lib, "specv_verify_cache_workspace_size", 256, 8, 128256)
+    assert st == 0 and n == 256 * (18 + 27) * 8 + 256 * 251 * 8   # row words + 3 cache words per draft row
+
+    def call(fan=(2, 2, 1, 3), C=0.5, l=1.0, B=2, topk=FAKE, ws_bytes=1 << 20, V=10):
+        arr = (ctypes.c_int32 * len(fan))(*fan)
+        return lib.specv_verify_cache(L(), L(), FAKE, FAKE, B, 3, V, ctypes.cast(arr, ctypes.c_void_p),
+                                      ctypes.c_float(C), ctypes.c_float(l), 1, 0, FAKE, FAKE, None, None, topk,
+                                      None, None, FAKE, ws_bytes, None)
+    assert call(fan=(0, 0, 0, 0)) == INVALID          # no candidates anywhere
+    assert call(fan=(2, -1, 1, 1)) == INVALID
+    assert call(fan=(2, 10, 1, 1)) == INVALID         # F_k <= vocab - 1
+    assert call(fan=(2, 32, 1, 1), V=100) == INVALID  # F_k <= SPECV_MAX_TOPF
+    assert call(C=-0.1) == INVALID
+    assert call(C=1.5) == INVALID
+    assert call(C=float("nan")) == INVALID
+    assert call(l=0.0) == INVALID
+    assert call(l=1.01) == INVALID
+    assert call(topk=None) == INVALID
+    assert call(B=0) == INVALID
+    assert call(ws_bytes=8) == WORKSPACE
+    assert lib.specv_verify_cache(L(), L(), FAKE, FAKE, 2, 3, 10, None, ctypes.c_float(1), ctypes.c_float(1), 1,
+                                  0, FAKE, FAKE, None, None, FAKE, None, None, FAKE, 1 << 20, None) == INVALID
+
+
+def test_geometric_fanout_matches_oracle(lib):
+    # Host-only entry point: Theorem 12 plus largest-remainder rounding.
+    import numpy as np
+    from oracle import ssd
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        K = int(rng.integers(0, 20))
+        a = float(rng.uniform(0.05, 0.95))
+        r = float(rng.uniform(0.2, 4.0))
+        budget = int(rng.integers(0, 400))
+        got = binding.geometric_fanout(K, a, r, budget)
+        want = ssd.integer_fanout(ssd.geometric_fanout(K, a, r, budget), budget)
+        assert sum(got) == budget
+        assert got == [int(x) for x in want], (K, a, r, budget)
+    out = (ctypes.c_int32 * 4)()
+    assert lib.specv_geometric_fanout(3, 1.0, 1.0, 10, out) == INVALID
+    assert lib.specv_geometric_fanout(3, 0.5, 0.0, 10, out) == INVALID
+    assert lib.specv_geometric_fanout(65, 0.5, 1.0, 10, out) == INVALID
+    assert lib.specv_geometric_fanout(3, 0.5, 1.0, -1, out) == INVALID
+    assert lib.specv_geometric_fanout(3, 0.5, 1.0, 10, None) == INVALID
 
 
 def test_uniforms_validation(lib):

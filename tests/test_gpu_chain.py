@@ -203,3 +203,23 @@ def test_one_workspace_across_shapes():
         ref, seqs = run_chain_oracle(w)
         compare_chain(gpu, ref, seqs, gamma, f"shared workspace {i}")
         assert int(ws.count_nonzero().item()) == 0
+
+
+def test_bonus_pass_with_zero_tiles():
+    # A draft far above the target on the first 1024 ids makes the residual
+    # max(p_t - p_d, 0) exactly 0 on whole tiles; the tile words of the shared
+    # bonus pass must still count as published (V = 20000: two bonus workgroups).
+    rng = np.random.default_rng(21)
+    B, gamma, V = 8, 2, 20000
+    target = rng.normal(0, 1, (B, gamma + 1, V)).astype(np.float32)
+    draft = target.copy()
+    draft[:, :, :1024] += 3.0
+    tokens = np.full((B, gamma), 5, np.int32)
+    w = workloads.ChainInputs("zero-tiles", B, gamma, V, "f32", target, draft, tokens,
+                              np.ones(B, np.float32), 8, 0, 4)
+    log("chain zero tiles")
+    gpu = run_chain_gpu(w)
+    ref, seqs = run_chain_oracle(w)
+    assert np.all(gpu["num_accepted"] >= 0)
+    good, bad = compare_chain(gpu, ref, seqs, gamma, "zero tiles")
+    assert bad <= 1

@@ -186,8 +186,9 @@ def test_cache_candidates_and_hit():
     zt = rng.normal(0, 1, (gamma + 1, V))
     zd = zt + rng.normal(0, 1, (gamma + 1, V))
     tokens = [int(rng.integers(V)) for _ in range(gamma)]
-    fan = [2, 3, 1, 4]
+    fan = [2, 3, 0, 4]
     cands = ssd.cache_candidates(zd, tokens, fan)
+    assert cands[2] == []   # F_k = 0: the cache does not cover position 2
     for k in range(gamma + 1):
         order = [int(j) for j in rank_order(zd[k]) if k == gamma or int(j) != tokens[k]]
         assert cands[k] == order[:fan[k]]
