@@ -51,6 +51,10 @@ def algorithmic_bytes(w):
     return verify, topf, step
 
 
+def step_bytes_of(w):
+    return algorithmic_bytes(w)[2]
+
+
 def tree_algorithmic_bytes(tw):
     """Logit bytes of one tree call: every node's target row, plus the draft
     row of every node that has children when T > 0 (greedy trees read none)."""
@@ -184,6 +188,19 @@ def main():
     verify_ms = timed(lambda i: binding.verify(target, draft, tokens, temp, w.seed, i, workspace=vws, out=vout))
     topf_ms = timed(lambda i: binding.bonus_topk(draft, tokens, F, out=(out["topk"], out["topk_logits"])))
 
+    # SSD cache verification on the same rows: Theorem 12 fan-outs for a
+    # budget of (gamma + 1) * F candidates (a = 0.6, r = 1), Saguaro sampling
+    # with C = 47/147, exact rule (not part of the step).
+    fan = binding.geometric_fanout(gamma, 0.6, 1.0, (gamma + 1) * F)
+    cws = torch.zeros(binding.verify_cache_workspace_bytes(B, gamma, w.V), dtype=torch.uint8, device=dev)
+    cout = binding.verify_cache(target, draft, tokens, temp, fan, w.seed, 0, saguaro_C=47 / 147, workspace=cws)
+    cache_ms = timed(lambda i: binding.verify_cache(target, draft, tokens, temp, fan, w.seed, i, saguaro_C=47 / 147,
+                                                    workspace=cws, out=cout))
+    cache = {"entry": "specv_verify_cache", "fanout": fan, "saguaro_C": 47 / 147, "lenience": 1.0,
+             "avg_ms": cache_ms, "algorithmic_bytes": step_bytes_of(w),
+             "gbps": step_bytes_of(w) / (cache_ms * 1e-3) / 1e9,
+             "hit_rate": float(cout["hit"].float().mean().item())}
+
     # Token-tree verification (MSS, T = 1) on its own workload: B = 32 trees of
     # N = 64 nodes over V = 152064 bf16 logits (not part of the step).
     tree = None
@@ -248,6 +265,7 @@ def main():
         "copy_yardstick": {"kernel": "torch.neg int32", "read_bytes": COPY_BYTES, "write_bytes": COPY_BYTES,
                            "avg_ms": copy_ms, "gbps": 2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9},
         "mean_accepted": mean_accepted,
+        "cache": cache,
         "tree": tree,
     }
     if not args.no_cpu_baseline:
