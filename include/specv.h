@@ -222,6 +222,48 @@ specv_status specv_verify_cache(specv_logits target, specv_logits draft,
 specv_status specv_geometric_fanout(int32_t K, double accept_rate, double r,
                                     int32_t budget, int32_t* out);
 
+/* Bytes of workspace specv_verify_ragged needs for (batch, max_gamma, vocab)
+ * with (has_draft != 0) or without draft logits. */
+specv_status specv_verify_ragged_workspace_size(int32_t batch, int32_t max_gamma,
+                                                int32_t vocab, int32_t has_draft,
+                                                size_t* bytes);
+
+/*
+ * Chain verification of a ragged batch [L5 sec. 2.2, 3.1; DLN sec. 2.2-2.3,
+ * Appendix "Implementation Details"]: sequence b drafts gamma_b tokens,
+ * draft_tokens[draft_offsets[b] .. draft_offsets[b+1]) (0 <= gamma_b <=
+ * max_gamma), and the rule is that of specv_verify with gamma = gamma_b (the
+ * bonus uniform uses j = gamma_b, so a batch with every gamma_b = gamma gives
+ * specv_verify's results).
+ *
+ * Rows are packed, addressed by stride_row (stride_seq is ignored):
+ *  target: num_draft + batch rows; sequence b's target rows 0..gamma_b are
+ *          rows draft_offsets[b] + b + i.
+ *  draft:  num_draft rows; sequence b's row i is row draft_offsets[b] + i.
+ *          draft.data == NULL: the drafts have no probabilities (an n-gram or
+ *          prompt-lookup proposer): q is the point mass at the drafted token,
+ *          so x is accepted iff u <= p_t(x), and the bonus after a rejection
+ *          is drawn from p_t with x removed.
+ * draft_offsets: device int32 [batch + 1], nondecreasing, draft_offsets[0]
+ *          = 0, draft_offsets[batch] = num_draft. A sequence whose offsets
+ *          break this (or exceed max_gamma tokens) reads nothing and reports
+ *          out_num_accepted = -2.
+ * draft_tokens: device int32 [num_draft] (may be NULL when num_draft == 0).
+ * Outputs: out_tokens int32 [batch][max_gamma+1] (accepted tokens, the bonus,
+ *          then -1), out_num_accepted [batch], out_probs float [num_draft][2]
+ *          or NULL ((p_t(x), 1) without draft probabilities), out_bonus_mass
+ *          [batch] or NULL. Workspace as for specv_verify, sized by
+ *          specv_verify_ragged_workspace_size.
+ */
+specv_status specv_verify_ragged(specv_logits target, specv_logits draft,
+                                 const int32_t* draft_offsets, const int32_t* draft_tokens,
+                                 const float* temperature, int32_t batch, int32_t max_gamma,
+                                 int32_t num_draft, int32_t vocab, uint64_t seed,
+                                 uint64_t offset, int32_t* out_tokens,
+                                 int32_t* out_num_accepted, float* out_probs,
+                                 float* out_bonus_mass, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace specv_tree_verify needs for (batch, nodes, vocab). */
 specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes,
                                               int32_t vocab, size_t* bytes);

@@ -20,6 +20,8 @@ path computes, in fp64 numpy, written from the pages' definitions:
                   (MSS) over a token tree.
 * ``ssd``      -- Saguaro sampling sigma_{F,C}, per-position fan-out (Theorem
                   12) and the cache-hit check of SSD, and the lenient rule.
+* ``ragged``   -- ragged batches (per-sequence draft counts, packed rows) and
+                  drafts without probabilities (q = point mass at the token).
 
 Every function cites the page and section it follows. Each is pinned by a
 ``-m "not gpu"`` test in ``tests/test_oracle_*.py`` against something other
@@ -29,4 +31,4 @@ an independent Philox implementation (rocRAND's source header) and the
 published Philox known-answer vectors. No function here is "parity unpinned".
 """
 
-from . import philox, sampling, ssd, topf, tree  # noqa: F401
+from . import philox, ragged, sampling, ssd, topf, tree  # noqa: F401

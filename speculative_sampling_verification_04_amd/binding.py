@@ -22,6 +22,7 @@ EXPORTED = ("specv_verify_workspace_size", "specv_verify", "specv_bonus_topk",
             "specv_verify_topk_workspace_size", "specv_verify_topk",
             "specv_tree_verify_workspace_size", "specv_tree_verify",
             "specv_verify_cache_workspace_size", "specv_verify_cache", "specv_geometric_fanout",
+            "specv_verify_ragged_workspace_size", "specv_verify_ragged",
             "specv_uniforms", "specv_last_error", "specv_version")
 
 
@@ -70,6 +71,8 @@ def load_library(path=LIB_PATH):
             "specv_verify_cache": [Logits, Logits, P, P, I32, I32, I32, P, ctypes.c_float, ctypes.c_float,
                                    U64, U64, P, P, P, P, P, P, P, P, SZ, P],
             "specv_geometric_fanout": [I32, ctypes.c_double, ctypes.c_double, I32, P],
+            "specv_verify_ragged_workspace_size": [I32, I32, I32, I32, SZP],
+            "specv_verify_ragged": [Logits, Logits, P, P, P, I32, I32, I32, I32, U64, U64, P, P, P, P, P, SZ, P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -264,6 +267,56 @@ def verify_cache(target, draft, draft_tokens, temperature, fanout, seed, offset=
                                   seed, offset, _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out["probs"]),
                                   _ptr(out["bonus_mass"]), _ptr(out["topk"]), _ptr(out["topk_logits"]),
                                   _ptr(out["hit"]), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def verify_ragged_workspace_bytes(batch, max_gamma, vocab, has_draft=True):
+    lib = load_library()
+    n = ctypes.c_size_t()
+    _check(lib.specv_verify_ragged_workspace_size(batch, max_gamma, vocab, int(has_draft), ctypes.byref(n)))
+    return n.value
+
+
+def packed_view(t):
+    """A [rows, V] tensor as packed rows (stride_seq unused)."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("packed logits must be a [rows, V] tensor with unit stride along V")
+    dt = SPECV_BF16 if t.dtype == torch.bfloat16 else SPECV_F32
+    if t.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("logits must be bfloat16 or float32")
+    return Logits(t.data_ptr(), dt, 0, t.stride(0))
+
+
+def verify_ragged(target, draft, offsets, draft_tokens, temperature, max_gamma, seed, offset=0, *,
+                  with_probs=True, with_mass=True, workspace=None, out=None):
+    """Ragged chain verification (specv_verify_ragged). target: packed
+    [num_draft + B, V]; draft: packed [num_draft, V] or None (drafts without
+    probabilities); offsets int32 [B + 1]; draft_tokens int32 [num_draft].
+    Returns dict(tokens [B, max_gamma+1], num_accepted, probs [num_draft, 2],
+    bonus_mass)."""
+    lib = load_library()
+    B = offsets.shape[0] - 1
+    num_draft = draft_tokens.shape[0]
+    V = target.shape[1]
+    dev = target.device
+    _int32(offsets, (B + 1,), "offsets")
+    _int32(draft_tokens, (num_draft,), "draft_tokens")
+    if target.shape[0] != num_draft + B:
+        raise ValueError("target must have num_draft + B rows")
+    if draft is not None and tuple(draft.shape) != (num_draft, V):
+        raise ValueError("draft must be [num_draft, V]")
+    if out is None:
+        out = dict(tokens=torch.empty((B, max_gamma + 1), dtype=torch.int32, device=dev),
+                   num_accepted=torch.empty((B,), dtype=torch.int32, device=dev),
+                   probs=torch.empty((num_draft, 2), dtype=torch.float32, device=dev) if with_probs else None,
+                   bonus_mass=torch.empty((B,), dtype=torch.float32, device=dev) if with_mass else None)
+    nbytes = verify_ragged_workspace_bytes(B, max_gamma, V, draft is not None)
+    ws = workspace if workspace is not None else _workspaces.get(nbytes, dev)
+    dview = packed_view(draft) if draft is not None else Logits(0, packed_view(target).dtype, 0, 0)
+    _check(lib.specv_verify_ragged(packed_view(target), dview, _ptr(offsets), _ptr(draft_tokens),
+                                   _ptr(temperature), B, max_gamma, num_draft, V, seed, offset,
+                                   _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out["probs"]),
+                                   _ptr(out["bonus_mass"]), _ptr(ws), ws.numel(), _stream(dev)))
     return out
 
 

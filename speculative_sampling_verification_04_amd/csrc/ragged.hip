@@ -1,0 +1,111 @@
+// Chain verification of a ragged batch [Lecture 5: Speculative Decoding and
+// SpecInfer, sec. 2.2, 2.7, 3.1; Speculative Decoding (dl-note), sec. 2.2-2.3
+// and Appendix "Implementation Details"]: sequence b drafts gamma_b =
+// offsets[b+1] - offsets[b] tokens (0 <= gamma_b <= G), its draft rows are
+// packed rows offsets[b] .. offsets[b+1]-1 and its gamma_b + 1 target rows are
+// packed rows offsets[b] + b .. offsets[b+1] + b. A draft without
+// probabilities (an n-gram or prompt-lookup proposer) makes q the point mass
+// at the drafted token: x is accepted iff u <= p_t(x), and the residual is
+// p_t with x removed.
+//
+// The grid has the shape of the dense verify kernel at gamma = G: per
+// sequence G + 1 target-row tasks (and G draft-row tasks unless NoDraft), each
+// in S chunks, then the H bonus workgroups; tasks past gamma_b publish a
+// skipped word without reading anything. Offsets that break the contract
+// (decreasing, past num_draft, or more than G tokens) are caught here: the
+// sequence reports out_num_accepted = -2 and reads no row.
+#include "specv_chain.hpp"
+
+namespace specv {
+
+namespace {
+
+constexpr int kU = 4;  // 16-byte steps per lane per iteration
+constexpr int kD = 0;  // prefetch form (see stream_chunk)
+
+template <int DT, bool NoDraft>
+__global__ __launch_bounds__(kThreads) void ragged_verify_kernel(ChainArgs a) {
+    constexpr int esz = ElemT<DT>::kBytes;
+    const int G = a.gamma;
+    const int R = NoDraft ? G + 1 : 2 * G + 1;
+    const int64_t RS = int64_t(R) * a.S;
+    int sidx;
+    int64_t w;
+    decode_chain(blockIdx.x, a.B, RS, a.H, a.D, sidx, w);
+    const int b = sequence_for_slot(a.temperature, a.B, sidx);
+    const float T = a.temperature[b];
+    const bool greedy = !(T > 0.0f);
+    const int32_t o0 = a.offsets[b], o1 = a.offsets[b + 1];
+    const bool valid = o0 >= 0 && o0 <= o1 && o1 <= a.num_draft && o1 - o0 <= G;
+    const int gb = valid ? o1 - o0 : 0;
+    uint64_t* slots = a.slots + int64_t(sidx) * RS;
+
+    if (w >= RS) {  // bonus workgroup
+        const int h = int(w - RS);
+        if (!valid) {
+            if (h == a.H - 1) {
+                if (wait_slots(slots, RS)) zero_slots(slots, RS);
+                for (int j = threadIdx.x; j <= G; j += kThreads) a.out_tokens[int64_t(b) * (G + 1) + j] = -1;
+                if (threadIdx.x == 0) a.out_nacc[b] = -2;
+            }
+            return;
+        }
+        SeqView q;
+        q.b = b;
+        q.gamma = gb;
+        q.G = G;
+        q.tokens = a.tokens + o0;
+        q.trow = static_cast<const char*>(row_ptr(a.target, esz, 0, int64_t(o0) + b));
+        q.tstride = a.target.stride_row * esz;
+        q.drow = NoDraft ? nullptr : static_cast<const char*>(row_ptr(a.draft, esz, 0, o0));
+        q.dstride = NoDraft ? 0 : a.draft.stride_row * esz;
+        q.out_tokens = a.out_tokens + int64_t(b) * (G + 1);
+        q.out_len = G + 1;
+        q.out_probs = a.out_probs ? a.out_probs + int64_t(o0) * 2 : nullptr;
+        chain_resolve<DT, NoDraft>(a, q, T, slots, RS, a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, h);
+        return;
+    }
+
+    const int chunk = int(w % a.S);
+    const int slot = int(w / a.S);
+    const bool draft_row = slot > G;
+    const int row = draft_row ? slot - (G + 1) : slot;
+    const int64_t lo = int64_t(chunk) * a.chunk;
+    const int64_t hi = min(int64_t(a.V), lo + a.chunk);
+    const bool needed = valid && lo < hi && (draft_row ? (!greedy && row < gb) : row <= gb);
+
+    uint64_t word = pack_skipped();
+    if (needed) {
+        const void* rp = draft_row ? row_ptr(a.draft, esz, 0, int64_t(o0) + row)
+                                   : row_ptr(a.target, esz, 0, int64_t(o0) + b + row);
+        if (greedy) {
+            ArgmaxAcc acc;
+            stream_chunk<DT, kU, kD>(rp, lo, hi, acc);
+            block_merge_argmax(acc.best, acc.idx);
+            word = pack_argmax(acc.best, acc.idx);
+        } else {
+            SoftmaxAcc acc(log2e_over(T));
+            stream_chunk<DT, kU, kD>(rp, lo, hi, acc);
+            block_merge_softmax(acc.m, acc.mc, acc.s);
+            word = pack_softmax(acc.m, acc.s);
+        }
+    }
+    if (threadIdx.x == 0) publish(slots + w, word);
+}
+
+template <int DT, bool NoDraft>
+hipError_t launch_dt(const ChainArgs& a, hipStream_t stream) {
+    const int64_t R = NoDraft ? a.gamma + 1 : 2 * a.gamma + 1;
+    const int64_t grid = int64_t(a.B) * (R * a.S + a.H);
+    hipLaunchKernelGGL((ragged_verify_kernel<DT, NoDraft>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ragged(const ChainArgs& a, int dtype, bool no_draft, hipStream_t stream) {
+    if (no_draft) return dtype == DT_BF16 ? launch_dt<DT_BF16, true>(a, stream) : launch_dt<DT_F32, true>(a, stream);
+    return dtype == DT_BF16 ? launch_dt<DT_BF16, false>(a, stream) : launch_dt<DT_F32, false>(a, stream);
+}
+
+}  // namespace specv

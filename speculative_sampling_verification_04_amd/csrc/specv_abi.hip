@@ -160,6 +160,17 @@ specv_status check_tree_sizes(int32_t batch, int32_t nodes, int32_t vocab) {
     return SPECV_OK;
 }
 
+specv_status check_ragged_sizes(int32_t batch, int32_t max_gamma, int32_t vocab) {
+    if (batch < 1) return fail(SPECV_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+    if (max_gamma < 0 || max_gamma > SPECV_MAX_GAMMA)
+        return fail(SPECV_ERR_INVALID_ARG, "max_gamma must be in [0, %d] (got %d)", SPECV_MAX_GAMMA, max_gamma);
+    if (vocab < 1 || vocab > SPECV_MAX_VOCAB)
+        return fail(SPECV_ERR_INVALID_ARG, "vocab must be in [1, %d] (got %d)", SPECV_MAX_VOCAB, vocab);
+    return SPECV_OK;
+}
+
+int64_t ragged_rows(int32_t max_gamma, bool has_draft) { return has_draft ? 2 * int64_t(max_gamma) + 1 : max_gamma + 1; }
+
 }  // namespace
 
 __global__ void uniforms_kernel(uint64_t seed, uint64_t offset, uint32_t tag, int32_t B, int32_t J, float* out) {
@@ -383,6 +394,62 @@ specv_status specv_verify_cache(specv_logits target, specv_logits draft, const i
     const hipError_t e = launch_verify_topf(a, target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32,
                                             static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_verify_cache launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+specv_status specv_verify_ragged_workspace_size(int32_t batch, int32_t max_gamma, int32_t vocab, int32_t has_draft,
+                                                size_t* bytes) {
+    if (bytes == nullptr) return fail(SPECV_ERR_INVALID_ARG, "bytes is NULL");
+    specv_status st = check_ragged_sizes(batch, max_gamma, vocab);
+    if (st != SPECV_OK) return st;
+    *bytes = layout_for(batch, ragged_rows(max_gamma, has_draft != 0), vocab).total();
+    return ok();
+}
+
+specv_status specv_verify_ragged(specv_logits target, specv_logits draft, const int32_t* draft_offsets,
+                                 const int32_t* draft_tokens, const float* temperature, int32_t batch,
+                                 int32_t max_gamma, int32_t num_draft, int32_t vocab, uint64_t seed, uint64_t offset,
+                                 int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                 float* out_bonus_mass, void* workspace, size_t workspace_bytes, void* stream) {
+    specv_status st = check_ragged_sizes(batch, max_gamma, vocab);
+    if (st != SPECV_OK) return st;
+    const bool has_draft = draft.data != nullptr;
+    if ((st = check_logits("target", target)) != SPECV_OK) return st;
+    if (has_draft) {
+        if ((st = check_logits("draft", draft)) != SPECV_OK) return st;
+        if (target.dtype != draft.dtype)
+            return fail(SPECV_ERR_UNSUPPORTED, "target and draft must have the same dtype");
+    }
+    if (num_draft < 0) return fail(SPECV_ERR_INVALID_ARG, "num_draft must be >= 0");
+    if (!draft_offsets || !temperature || !out_tokens || !out_num_accepted || (num_draft > 0 && !draft_tokens))
+        return fail(SPECV_ERR_INVALID_ARG,
+                    "draft_offsets, draft_tokens, temperature, out_tokens and out_num_accepted are required");
+    const Layout L = layout_for(batch, ragged_rows(max_gamma, has_draft), vocab);
+    const int64_t grid = int64_t(batch) * (ragged_rows(max_gamma, has_draft) * L.S + L.H);
+    if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch");
+    if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
+
+    ChainArgs a{};
+    a.target = view(target);
+    a.draft = view(draft);
+    a.tokens = draft_tokens;
+    a.temperature = temperature;
+    a.B = batch;
+    a.gamma = max_gamma;
+    a.V = vocab;
+    set_bonus(a, L, ragged_rows(max_gamma, has_draft) * L.S, workspace);
+    set_plain(a, 0);
+    a.seed = seed;
+    a.offset = offset;
+    a.out_tokens = out_tokens;
+    a.out_nacc = out_num_accepted;
+    a.out_probs = out_probs;
+    a.out_mass = out_bonus_mass;
+    a.offsets = draft_offsets;
+    a.num_draft = num_draft;
+    const hipError_t e = launch_ragged(a, target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32, !has_draft,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_verify_ragged launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -1,7 +1,7 @@
-// Chain verification pieces shared by the verify kernel and the fused
-// verify + top-F kernel [Lecture 5: Speculative Decoding and SpecInfer, sec.
-// 2.2, 2.7, 3.1; Speculative Decoding (dl-note), sec. 2.2-2.3 and Appendix
-// "Implementation Details"].
+// Chain verification pieces shared by the verify kernel, the fused
+// verify + top-F kernel and the ragged kernel [Lecture 5: Speculative Decoding
+// and SpecInfer, sec. 2.2, 2.7, 3.1; Speculative Decoding (dl-note), sec.
+// 2.2-2.3 and Appendix "Implementation Details"].
 //
 // After a sequence's row workgroups, H bonus workgroups are dispatched
 // (h = 0 .. H-1). Each waits for the row statistics and decides the accepted
@@ -13,6 +13,8 @@
 // one workgroup. The last one (h = H-1) collects the tile sums, draws the
 // bonus, writes the outcome and returns the words it consumed to zero.
 #pragma once
+
+#include <type_traits>
 
 #include "specv_launch.hpp"
 #include "specv_sample.hpp"
@@ -30,19 +32,60 @@ __device__ __forceinline__ const void* row_ptr(const RowView& v, int esz, int64_
 
 __device__ __forceinline__ float log2e_over(float T) { return float(1.4426950408889634 / double(T)); }
 
-// Bonus workgroup h of sequence b. slots: the sequence's nslots row words
-// (row r chunk j at r * S + j: target row r for r <= gamma, draft row
-// r - gamma - 1 after that). tiles: its ntiles tile words (used when H > 1).
+// One sequence as the resolve step sees it.
+struct SeqView {
+    int b;                   // sequence index: Philox counter and per-sequence outputs
+    int gamma;               // its number of draft tokens
+    int G;                   // layout: target rows at words 0..G, draft rows at G+1+i
+    const int32_t* tokens;   // its gamma draft tokens
+    const char* trow;        // target row i at trow + i * tstride (bytes)
+    int64_t tstride;
+    const char* drow;        // draft row i at drow + i * dstride (null: no draft probabilities)
+    int64_t dstride;
+    int32_t* out_tokens;     // out_len entries: accepted tokens, the bonus, then -1
+    int out_len;
+    float* out_probs;        // gamma x 2, or null
+    __device__ __forceinline__ const void* target(int i) const { return trow + i * tstride; }
+    __device__ __forceinline__ const void* draft(int i) const { return drow + i * dstride; }
+};
+
+// The view of sequence b in the dense [B][rows][V] layout of specv_verify and
+// specv_verify_topk.
 template <int DT>
-__device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T, uint64_t* slots, int64_t nslots,
-                                              uint64_t* tiles, int h) {
+__device__ __forceinline__ SeqView dense_seq(const ChainArgs& a, int b) {
     constexpr int esz = ElemT<DT>::kBytes;
-    const int gamma = a.gamma;
-    const int R = 2 * gamma + 1;
+    SeqView q;
+    q.b = b;
+    q.gamma = a.gamma;
+    q.G = a.gamma;
+    q.tokens = a.tokens + int64_t(b) * a.gamma;
+    q.trow = static_cast<const char*>(row_ptr(a.target, esz, b, 0));
+    q.tstride = a.target.stride_row * esz;
+    q.drow = static_cast<const char*>(row_ptr(a.draft, esz, b, 0));
+    q.dstride = a.draft.stride_row * esz;
+    q.out_tokens = a.out_tokens + int64_t(b) * (a.gamma + 1);
+    q.out_len = a.gamma + 1;
+    q.out_probs = a.out_probs ? a.out_probs + int64_t(b) * a.gamma * 2 : nullptr;
+    return q;
+}
+
+// Bonus workgroup h of a sequence. slots: the sequence's nslots words (row r
+// chunk j at r * S + j: target row r for r <= G, draft row r - G - 1 after
+// that; then, with a.cache_words, three cache words per draft row from word
+// 2G + 2). tiles: its ntiles tile words (used when H > 1). NoDraft: the draft
+// has no probabilities (q is the point mass at the drafted token). Cache: the
+// cache words exist (a.cache_words; specv_verify_cache only).
+template <int DT, bool NoDraft = false, bool Cache = false>
+__device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView& q, float T, uint64_t* slots,
+                                              int64_t nslots, uint64_t* tiles, int h) {
+    const int b = q.b;
+    const int gamma = q.gamma;
+    const int G = q.G;
+    const int R = NoDraft ? G + 1 : 2 * G + 1;   // row words to merge
     const bool greedy = !(T > 0.0f);
     const bool last = h == a.H - 1;
     const float c = greedy ? 0.0f : log2e_over(T);
-    const uint64_t* extra = slots + 2 * gamma + 2;  // the cache words, when a.cache_words
+    const uint64_t* extra = slots + 2 * G + 2;  // the cache words, when a.cache_words
 
     if (greedy && !last) return;  // the greedy bonus is an argmax: nothing to share
 
@@ -61,7 +104,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T
         return;
     }
     for (int r = threadIdx.x; r < R; r += kThreads) {
-        const bool draft_row = r > gamma;
+        const bool draft_row = r > G;
         st[r] = (greedy && draft_row) ? RowStats{-INFINITY, -INFINITY, -1, 0.0}
                                       : merge_slots(slots + int64_t(r) * a.S, a.S, greedy, c);
     }
@@ -72,7 +115,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T
         const int i = lane_id();
         bool reject = false;
         if (i < gamma) {
-            const int32_t x = a.tokens[int64_t(b) * gamma + i];
+            const int32_t x = q.tokens[i];
             const bool in_range = x >= 0 && x < a.V;
             float pt_out = 0.0f, pd_out = 1.0f;
             if (greedy) {
@@ -82,27 +125,31 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T
             } else {
                 double pt = 0.0, pd = 0.0;
                 if (in_range) {
-                    const float zd = load_elem<DT>(row_ptr(a.draft, esz, b, i), x);
-                    pt = prob_of(load_elem<DT>(row_ptr(a.target, esz, b, i), x), c, st[i]);
-                    RowStats qs = st[gamma + 1 + i];
-                    double scale = 1.0;
-                    if (a.cache_words) {  // Saguaro sampling: q = sigma_{F_i,C}(draft_i / T)
-                        const uint64_t zw = peek(extra + 3 * i);
-                        if ((zw >> 32) == 1ull) {
-                            qs.Z = double(__uint_as_float(uint32_t(zw)));
-                            if (full_key(zd, x) + 1ull >= peek(extra + 3 * i + 1)) scale = double(a.C);
+                    pt = prob_of(load_elem<DT>(q.target(i), x), c, st[i]);
+                    if (NoDraft) {
+                        pd = 1.0;
+                    } else {
+                        const float zd = load_elem<DT>(q.draft(i), x);
+                        RowStats qs = st[G + 1 + i];
+                        double scale = 1.0;
+                        if (Cache) {  // Saguaro sampling: q = sigma_{F_i,C}(draft_i / T)
+                            const uint64_t zw = peek(extra + 3 * i);
+                            if ((zw >> 32) == 1ull) {
+                                qs.Z = double(__uint_as_float(uint32_t(zw)));
+                                if (full_key(zd, x) + 1ull >= peek(extra + 3 * i + 1)) scale = double(a.C);
+                            }
                         }
+                        pd = scale * prob_of(zd, c, qs);
                     }
-                    pd = scale * prob_of(zd, c, qs);
                 }
                 const float u = stream_uniform(a.seed, a.offset, uint32_t(b), 0u, uint32_t(i));
                 reject = !(pd > 0.0 && double(u) <= pt / (double(a.lenience) * pd));
                 pt_out = float(pt);
                 pd_out = float(pd);
             }
-            if (last && a.out_probs) {
-                a.out_probs[(int64_t(b) * gamma + i) * 2 + 0] = pt_out;
-                a.out_probs[(int64_t(b) * gamma + i) * 2 + 1] = pd_out;
+            if (last && q.out_probs) {
+                q.out_probs[i * 2 + 0] = pt_out;
+                q.out_probs[i * 2 + 1] = pd_out;
             }
         }
         const uint64_t rej = __ballot(reject);
@@ -116,27 +163,32 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T
     } else {
         const int ntiles = int((int64_t(a.V) + kTileElems - 1) / kTileElems);
         const float v = stream_uniform(a.seed, a.offset, uint32_t(b), 0u, uint32_t(gamma));
-        const void* trow = row_ptr(a.target, esz, b, k);
-        ResidualWeights<DT> res;
+        const void* trow = q.target(k);
+        using Resid = typename std::conditional<NoDraft, ExcludeWeights<DT>, ResidualWeights<DT, Cache>>::type;
+        Resid res;
         TargetWeights<DT> tgt;
-        res.p.init(trow, c, st[k]);
-        res.coef = 1.0f;
-        res.V = a.V;
-        tgt.p = res.p;
+        tgt.p.init(trow, c, st[k]);
         tgt.V = a.V;
-        if (k < gamma) {
-            RowStats qs = st[gamma + 1 + k];
-            uint64_t top_word = 0ull;
-            if (a.cache_words) {
-                const uint64_t zw = peek(extra + 3 * k);
-                if ((zw >> 32) == 1ull) {
-                    qs.Z = double(__uint_as_float(uint32_t(zw)));
-                    top_word = peek(extra + 3 * k + 1);
+        res.p = tgt.p;
+        res.V = a.V;
+        if constexpr (NoDraft) {
+            res.x = k < gamma ? q.tokens[k] : -1;
+        } else {
+            res.coef = 1.0f;
+            if (k < gamma) {
+                RowStats qs = st[G + 1 + k];
+                uint64_t top_word = 0ull;
+                if (Cache) {
+                    const uint64_t zw = peek(extra + 3 * k);
+                    if ((zw >> 32) == 1ull) {
+                        qs.Z = double(__uint_as_float(uint32_t(zw)));
+                        top_word = peek(extra + 3 * k + 1);
+                    }
                 }
+                res.q.init(q.draft(k), c, qs);
+                res.q.scale = a.C;
+                res.q.top_word = top_word;
             }
-            res.q.init(row_ptr(a.draft, esz, b, k), c, qs);
-            res.q.scale = a.C;
-            res.q.top_word = top_word;
         }
 
         // Tile sums of the bonus weights: residual of row k, or p_t of row gamma.
@@ -175,27 +227,27 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, int b, float T
         }
         if (threadIdx.x == 0) { s_bonus = bonus; s_mass = mass; }
     }
-    if (threadIdx.x == 0) s_cache_word = (a.out_hit && a.cache_words) ? peek(extra + 3 * k + 2) : ~0ull;
+    if (threadIdx.x == 0) s_cache_word = (Cache && a.out_hit) ? peek(extra + 3 * k + 2) : ~0ull;
     __syncthreads();
     zero_slots(slots, nslots);   // consumed: back to the resting state
     __syncthreads();
 
-    for (int j = threadIdx.x; j <= gamma; j += kThreads) {
+    for (int j = threadIdx.x; j < q.out_len; j += kThreads) {
         int32_t t = -1;
-        if (j < k) t = a.tokens[int64_t(b) * gamma + j];
+        if (j < k) t = q.tokens[j];
         else if (j == k) t = s_bonus;
-        a.out_tokens[int64_t(b) * (gamma + 1) + j] = t;
+        q.out_tokens[j] = t;
     }
     if (threadIdx.x == 0) {
         a.out_nacc[b] = k;
         if (a.out_mass) a.out_mass[b] = s_mass;
-        if (a.out_hit) {  // (k, bonus) is in the cache iff the bonus is a candidate at k
+        if (Cache && !NoDraft && a.out_hit) {  // (k, bonus) is in the cache iff the bonus is a candidate at k
             const uint64_t cw = s_cache_word;
             const int32_t bonus = s_bonus;
-            const int32_t xk = k < gamma ? a.tokens[int64_t(b) * gamma + k] : -1;
+            const int32_t xk = k < gamma ? q.tokens[k] : -1;
             bool hit = false;
             if (cw != ~0ull && bonus >= 0 && bonus < a.V && bonus != xk)
-                hit = full_key(load_elem<DT>(row_ptr(a.draft, esz, b, k), bonus), bonus) + 1ull >= cw;
+                hit = full_key(load_elem<DT>(q.draft(k), bonus), bonus) + 1ull >= cw;
             a.out_hit[b] = hit ? 1 : 0;
         }
     }

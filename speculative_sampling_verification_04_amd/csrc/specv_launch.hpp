@@ -56,6 +56,10 @@ struct ChainArgs {
     float C;
     float lenience;
     int32_t* out_hit;
+    // Ragged batches (ragged_verify_kernel only): sequence b's draft tokens are
+    // tokens[offsets[b] .. offsets[b+1]); gamma is the largest allowed count.
+    const int32_t* offsets;
+    int32_t num_draft;
 };
 
 // Tree verification. Per tree there are 2N row tasks (target rows of every
@@ -155,6 +159,7 @@ inline int32_t tree_walkers(int64_t V) {
 
 hipError_t launch_chain(const ChainArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_verify_topf(const ChainArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_ragged(const ChainArgs& a, int dtype, bool no_draft, hipStream_t stream);
 hipError_t launch_tree(const TreeArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_topf(const TopFArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_uniforms(uint64_t seed, uint64_t offset, int32_t tag, int32_t B,

@@ -172,13 +172,13 @@ __device__ __forceinline__ void load_group(const void* row, int64_t j0, int64_t 
 // Probabilities p = 2^(z*c - mc) / Z of one row (fp32). With a threshold key
 // (Saguaro sampling), the elements whose key reaches it (the row's top F) are
 // scaled by `scale` and Z is the correspondingly reduced normaliser.
-template <int DT>
+template <int DT, bool kScaled = false>
 struct ProbRow {
     const void* row;
     float c, nmc, invZ;
     bool vec;
-    float scale;          // factor on the top-F elements (1: none)
-    uint64_t top_word;    // threshold key + 1 (0: no scaling)
+    float scale;          // factor on the top-F elements (kScaled only)
+    uint64_t top_word;    // threshold key + 1 (0: no scaling; kScaled only)
     __device__ void init(const void* r, float c_, const RowStats& st) {
         row = r; c = c_; nmc = -st.mc; invZ = float(1.0 / st.Z);
         vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0;
@@ -190,7 +190,7 @@ struct ProbRow {
         unpack8<DT>(raw, z);
 #pragma unroll
         for (int e = 0; e < kLaneElems; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(z[e], c, nmc)) * invZ;
-        if (top_word != 0ull) {
+        if (kScaled && top_word != 0ull) {
 #pragma unroll
             for (int e = 0; e < kLaneElems; ++e)
                 if (full_key(z[e], j0 + e) + 1ull >= top_word) p[e] *= scale;
@@ -208,12 +208,31 @@ struct TargetWeights {
     __device__ __forceinline__ void weights(const Raw& r, int64_t j0, float w[kLaneElems]) const { p.probs(r.p, j0, w); }
 };
 
+// Weights of p with one token removed: max(p - onehot(x), 0), the residual
+// when the draft has no probabilities and q is the point mass at the drafted
+// token x [Speculative Decoding (dl-note), Appendix "Implementation Details"].
+template <int DT>
+struct ExcludeWeights {
+    struct Raw { Raw8<DT> p; };
+    ProbRow<DT> p;
+    int64_t V;
+    int64_t x;
+    __device__ __forceinline__ void load(int64_t j0, Raw& r) const { load_group<DT>(p.row, j0, V, p.vec, r.p); }
+    __device__ __forceinline__ void weights(const Raw& r, int64_t j0, float w[kLaneElems]) const {
+        p.probs(r.p, j0, w);
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e)
+            if (j0 + e == x) w[e] = 0.0f;
+    }
+};
+
 // Weights max(p - coef * q, 0): the chain residual (coef = 1) and the MSS
 // residual after rejections (coef = c_j of the tree kernel's recurrence).
-template <int DT>
+template <int DT, bool kScaledQ = false>
 struct ResidualWeights {
     struct Raw { Raw8<DT> p, q; };
-    ProbRow<DT> p, q;
+    ProbRow<DT> p;
+    ProbRow<DT, kScaledQ> q;
     float coef;
     int64_t V;
     __device__ __forceinline__ void load(int64_t j0, Raw& r) const {

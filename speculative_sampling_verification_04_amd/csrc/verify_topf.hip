@@ -39,7 +39,7 @@ struct SoftmaxTopK {
     }
 };
 
-template <int DT, int K>
+template <int DT, int K, bool Cache>
 __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     constexpr int esz = ElemT<DT>::kBytes;
     const int R1 = 2 * a.gamma + 2;
@@ -50,10 +50,11 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     const int b = sequence_for_slot(a.temperature, a.B, sidx);
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
-    const int64_t words = R1 + (a.cache_words ? 3 * (a.gamma + 1) : 0);  // per sequence
+    const int64_t words = R1 + (Cache ? 3 * (a.gamma + 1) : 0);  // per sequence
     uint64_t* slots = a.slots + int64_t(sidx) * words;
     if (slot >= R1) {  // bonus workgroup: dispatched after every row of the sequence
-        chain_resolve<DT>(a, b, T, slots, words, a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, slot - R1);
+        chain_resolve<DT, false, Cache>(a, dense_seq<DT>(a, b), T, slots, words,
+                          a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, slot - R1);
         return;
     }
     const bool draft_row = slot > a.gamma;
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
             block_merge_softmax(acc.sm.m, acc.sm.mc, acc.sm.s);
             word = pack_softmax(acc.sm.m, acc.sm.s);
             pick = topf_finish<DT, K>(acc.tk, rp, V, Fk, a.F, excl, ids, vals);
-            if (a.cache_words && a.C < 1.0f && Fk > 0 && threadIdx.x == 0) {
+            if (Cache && a.C < 1.0f && Fk > 0 && threadIdx.x == 0) {
                 // sigma_{F,C}: the normaliser loses (1 - C) of the top-F terms,
                 // taken relative to the same reference m*c as the row sum.
                 const float c = log2e_over(T);
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
             stream_chunk<DT, kDraftU, kDraftD>(rp, 0, V, acc);
             pick = topf_finish<DT, K>(acc, rp, V, Fk, a.F, excl, ids, vals);
         }
-        if (a.cache_words && threadIdx.x == 0) {
+        if (Cache && threadIdx.x == 0) {
             uint64_t* extra = slots + R1 + 3 * row;
             publish(extra + 0, zword);
             publish(extra + 1, Fk > 0 ? topf_sigma_key(pick, Fk) + 1ull : ~0ull);
@@ -118,22 +119,24 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     if (threadIdx.x == 0) publish(slots + slot, word);
 }
 
-template <int DT>
+template <int DT, bool Cache>
 hipError_t launch_dt(const ChainArgs& a, hipStream_t stream) {
     const dim3 grid(unsigned(int64_t(a.B) * (2 * a.gamma + 2 + a.H)));
     const int K = a.F + 1;
-    if (K <= 2) hipLaunchKernelGGL((verify_topf_kernel<DT, 2>), grid, dim3(kThreads), 0, stream, a);
-    else if (K <= 4) hipLaunchKernelGGL((verify_topf_kernel<DT, 4>), grid, dim3(kThreads), 0, stream, a);
-    else if (K <= 8) hipLaunchKernelGGL((verify_topf_kernel<DT, 8>), grid, dim3(kThreads), 0, stream, a);
-    else if (K <= 16) hipLaunchKernelGGL((verify_topf_kernel<DT, 16>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((verify_topf_kernel<DT, 32>), grid, dim3(kThreads), 0, stream, a);
+    if (K <= 2) hipLaunchKernelGGL((verify_topf_kernel<DT, 2, Cache>), grid, dim3(kThreads), 0, stream, a);
+    else if (K <= 4) hipLaunchKernelGGL((verify_topf_kernel<DT, 4, Cache>), grid, dim3(kThreads), 0, stream, a);
+    else if (K <= 8) hipLaunchKernelGGL((verify_topf_kernel<DT, 8, Cache>), grid, dim3(kThreads), 0, stream, a);
+    else if (K <= 16) hipLaunchKernelGGL((verify_topf_kernel<DT, 16, Cache>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((verify_topf_kernel<DT, 32, Cache>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_verify_topf(const ChainArgs& a, int dtype, hipStream_t stream) {
-    return dtype == DT_BF16 ? launch_dt<DT_BF16>(a, stream) : launch_dt<DT_F32>(a, stream);
+    if (a.cache_words)
+        return dtype == DT_BF16 ? launch_dt<DT_BF16, true>(a, stream) : launch_dt<DT_F32, true>(a, stream);
+    return dtype == DT_BF16 ? launch_dt<DT_BF16, false>(a, stream) : launch_dt<DT_F32, false>(a, stream);
 }
 
 }  // namespace specv

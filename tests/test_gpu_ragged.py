@@ -1,0 +1,126 @@
+"""GPU parity of specv_verify_ragged: per-sequence draft counts with packed
+rows, with and without draft logits, against oracle/ragged.py; equality with
+specv_verify when every count is gamma; offsets that break the contract."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_common import ILL_MASS, PROB_TOL, chain_to_dev, log, to_dev
+from speculative_sampling_verification_04_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+
+
+def make_ragged(B, G, V, dtype, temps, seed, counts=None):
+    rng = np.random.default_rng(seed)
+    counts = rng.integers(0, G + 1, B) if counts is None else np.asarray(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    nd = int(offsets[-1])
+    target = workloads.round_to_bf16(rng.normal(0, 3, (nd + B, V)).astype(np.float32)) if dtype == "bf16" \
+        else rng.normal(0, 3, (nd + B, V)).astype(np.float32)
+    draft = np.empty((nd, V), np.float32)
+    temperature = np.where(np.arange(B) % 2 == 0, 0.0, 1.0).astype(np.float32) if temps == "mixed" \
+        else np.full(B, float(temps), np.float32)
+    tokens = np.zeros(nd, np.int32)
+    for b in range(B):
+        for i in range(int(counts[b])):
+            r = offsets[b] + i
+            d = target[offsets[b] + b + i] + rng.normal(0, 1, V).astype(np.float32)
+            draft[r] = workloads.round_to_bf16(d) if dtype == "bf16" else d
+            tokens[r] = workloads.gumbel_max_sample(rng, draft[r], float(temperature[b]))
+    return dict(target=target, draft=draft, offsets=offsets, tokens=tokens, temperature=temperature, counts=counts,
+                B=B, G=G, V=V, dtype=dtype, seed=seed % 97)
+
+
+def run(r, with_draft):
+    dev = "cuda"
+    target = to_dev(r["target"], r["dtype"], dev)
+    draft = to_dev(r["draft"], r["dtype"], dev) if with_draft else None
+    out = binding.verify_ragged(target, draft, torch.from_numpy(r["offsets"]).to(dev),
+                                torch.from_numpy(r["tokens"]).to(dev), torch.from_numpy(r["temperature"]).to(dev),
+                                r["G"], r["seed"], 0)
+    torch.cuda.synchronize()
+    gpu = {k: v.cpu().numpy() for k, v in out.items() if v is not None}
+    ref = oracle.ragged.verify_ragged_batch(r["target"], r["draft"] if with_draft else None, r["offsets"], r["tokens"],
+                                            r["temperature"], r["seed"], 0, r["G"])
+    return gpu, ref
+
+
+def compare(gpu, ref, r, name):
+    bad = []
+    for b in range(r["B"]):
+        o0, o1 = r["offsets"][b], r["offsets"][b + 1]
+        np.testing.assert_allclose(gpu["probs"][o0:o1], ref["probs"][o0:o1], atol=PROB_TOL,
+                                   err_msg=f"{name}: probs of sequence {b}")
+        k = ref["num_accepted"][b]
+        if ref["near_tie"][b] or (k < o1 - o0 and ref["bonus_mass"][b] < ILL_MASS):
+            bad.append(b)
+            continue
+        assert gpu["num_accepted"][b] == k, f"{name}: k of sequence {b}"
+        np.testing.assert_array_equal(gpu["tokens"][b], ref["tokens"][b], err_msg=f"{name}: tokens of {b}")
+        assert abs(gpu["bonus_mass"][b] - ref["bonus_mass"][b]) <= PROB_TOL
+    log(f"{name}: {r['B'] - len(bad)} sequences bit-exact, {len(bad)} near ties {bad}, "
+        f"mean accepted {ref['num_accepted'].mean():.2f}")
+    return len(bad)
+
+
+@pytest.mark.parametrize("with_draft", [True, False])
+@pytest.mark.parametrize("B,G,V,dtype,temps,seed", [
+    (40, 8, 30000, "bf16", "mixed", 1),
+    (17, 5, 3000, "f32", "0.7", 2),
+    (9, 64, 700, "f32", "1.0", 3),
+    (300, 3, 2000, "bf16", "mixed", 4),
+])
+def test_ragged_matches_oracle(B, G, V, dtype, temps, seed, with_draft):
+    r = make_ragged(B, G, V, dtype, temps, seed)
+    log(f"ragged B={B} G={G} V={V} {dtype} T={temps} draft={with_draft} counts {r['counts'][:12].tolist()}...")
+    gpu, ref = run(r, with_draft)
+    assert compare(gpu, ref, r, f"ragged V={V} draft={with_draft}") <= max(1, B // 10)
+
+
+def test_ragged_with_equal_counts_equals_dense():
+    w = workloads.make_chain(12, 4, 5000, dtype="bf16", sigma=3.0, temps="half0_half1", gen_seed=13, philox_seed=13)
+    d = chain_to_dev(w)
+    log("ragged = dense")
+    dense = binding.verify(d["target"], d["draft"], d["tokens"], d["temperature"], w.seed, 0)
+    B, g, V = w.B, w.gamma, w.V
+    offsets = torch.arange(B + 1, dtype=torch.int32, device="cuda") * g
+    rag = binding.verify_ragged(d["target"].reshape(B * (g + 1), V), d["draft"][:, :g].contiguous().reshape(B * g, V),
+                                offsets, d["tokens"].reshape(-1), d["temperature"], g, w.seed, 0)
+    torch.cuda.synchronize()
+    for k in ("tokens", "num_accepted"):
+        np.testing.assert_array_equal(rag[k].cpu().numpy(), dense[k].cpu().numpy(), err_msg=k)
+    np.testing.assert_array_equal(rag["probs"].cpu().numpy().reshape(B, g, 2), dense["probs"].cpu().numpy())
+    np.testing.assert_array_equal(rag["bonus_mass"].cpu().numpy(), dense["bonus_mass"].cpu().numpy())
+
+
+def test_ragged_bad_offsets_are_reported():
+    r = make_ragged(4, 3, 1000, "f32", "1.0", 5, counts=[2, 1, 3, 2])
+    offs = r["offsets"].copy()          # [0, 2, 3, 6, 8]
+    bad = offs.copy()
+    bad[2] = 1                          # sequence 1: 2 -> 1 (decreasing); sequence 2: 1 -> 6 (5 > G tokens)
+    dev = "cuda"
+    ws = torch.zeros(binding.verify_ragged_workspace_bytes(4, 3, 1000), dtype=torch.uint8, device=dev)
+    log("ragged bad offsets")
+    out = binding.verify_ragged(to_dev(r["target"], "f32"), to_dev(r["draft"], "f32"), torch.from_numpy(bad).to(dev),
+                                torch.from_numpy(r["tokens"]).to(dev), torch.from_numpy(r["temperature"]).to(dev),
+                                3, r["seed"], 0, workspace=ws)
+    torch.cuda.synchronize()
+    nacc = out["num_accepted"].cpu().numpy()
+    assert nacc[1] == -2 and nacc[2] == -2
+    assert np.all(out["tokens"].cpu().numpy()[[1, 2]] == -1)
+    assert int(ws.count_nonzero().item()) == 0
+    ref = oracle.ragged.verify_ragged_batch(r["target"], r["draft"], offs, r["tokens"], r["temperature"], r["seed"],
+                                            0, 3)
+    for b in (0, 3):
+        if not ref["near_tie"][b]:
+            assert nacc[b] == ref["num_accepted"][b]
