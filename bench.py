@@ -201,6 +201,30 @@ def main():
              "gbps": step_bytes_of(w) / (cache_ms * 1e-3) / 1e9,
              "hit_rate": float(cout["hit"].float().mean().item())}
 
+    # Ragged batch over the same rows: sequence b drafts gamma_b in 1..gamma
+    # tokens (seeded), rows packed; with draft logits, then without (n-gram
+    # style drafts). Not part of the step.
+    counts = np.random.default_rng(1234).integers(1, gamma + 1, B)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    t_rows = torch.cat([target[b, :counts[b] + 1] for b in range(B)])
+    d_rows = torch.cat([draft[b, :counts[b]] for b in range(B)])
+    r_tok = torch.cat([tokens[b, :counts[b]] for b in range(B)])
+    r_off = torch.from_numpy(offs).to(dev)
+    ragged = {}
+    for mode, dr in (("with_draft", d_rows), ("no_draft", None)):
+        rws = torch.zeros(binding.verify_ragged_workspace_bytes(B, gamma, w.V, dr is not None), dtype=torch.uint8,
+                          device=dev)
+        rout = binding.verify_ragged(t_rows, dr, r_off, r_tok, temp, gamma, w.seed, 0, workspace=rws)
+        r_ms = timed(lambda i: binding.verify_ragged(t_rows, dr, r_off, r_tok, temp, gamma, w.seed, i,
+                                                     workspace=rws, out=rout))
+        n_rows = int((counts + 1).sum()) + (int(counts[w.temperature > 0].sum()) if dr is not None else 0)
+        r_bytes = n_rows * w.V * 2
+        ragged[mode] = {"avg_ms": r_ms, "rows_read": n_rows, "algorithmic_bytes": r_bytes,
+                        "gbps": r_bytes / (r_ms * 1e-3) / 1e9,
+                        "mean_accepted": float(rout["num_accepted"].float().mean().item())}
+    ragged["draft_counts"] = "uniform in 1..gamma, seed 1234"
+    del t_rows, d_rows
+
     # Token-tree verification (MSS, T = 1) on its own workload: B = 32 trees of
     # N = 64 nodes over V = 152064 bf16 logits (not part of the step).
     tree = None
@@ -266,6 +290,7 @@ def main():
                            "avg_ms": copy_ms, "gbps": 2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9},
         "mean_accepted": mean_accepted,
         "cache": cache,
+        "ragged": ragged,
         "tree": tree,
     }
     if not args.no_cpu_baseline:
