@@ -279,11 +279,11 @@ def verify_ragged_workspace_bytes(batch, max_gamma, vocab, has_draft=True):
 
 def packed_view(t):
     """A [rows, V] tensor as packed rows (stride_seq unused)."""
-    if t.dim() != 2 or t.stride(1) != 1:
+    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
         raise ValueError("packed logits must be a [rows, V] tensor with unit stride along V")
-    dt = SPECV_BF16 if t.dtype == torch.bfloat16 else SPECV_F32
     if t.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("logits must be bfloat16 or float32")
+    dt = SPECV_BF16 if t.dtype == torch.bfloat16 else SPECV_F32
     return Logits(t.data_ptr(), dt, 0, t.stride(0))
 
 
@@ -297,6 +297,8 @@ def verify_ragged(target, draft, offsets, draft_tokens, temperature, max_gamma, 
     lib = load_library()
     B = offsets.shape[0] - 1
     num_draft = draft_tokens.shape[0]
+    if draft is not None and draft.numel() == 0:
+        draft = None  # no draft rows at all: nothing to read either way
     V = target.shape[1]
     dev = target.device
     _int32(offsets, (B + 1,), "offsets")

@@ -73,6 +73,8 @@ CASES = [
     ("saguaro-lenient-uneven", 33, 3, 20000, "bf16", "all1", (1, 0, 5, 2), 0.5, 0.8),
     ("zero-C", 16, 3, 3000, "f32", "all1", (3, 2, 2, 4), 0.0, 1.0),
     ("greedy-cache", 20, 4, 5000, "bf16", "all0", (5, 4, 3, 2, 1), 0.3, 0.7),
+    ("tiny-vocab", 6, 3, 3, "f32", "half0_half1", (2, 2, 2, 2), 0.5, 1.0),
+    ("max-fanout", 8, 2, 40, "bf16", "all1", (31, 31, 20), 0.6, 1.0),    # F_k up to SPECV_MAX_TOPF
 ]
 
 
@@ -115,3 +117,25 @@ def test_cache_leaves_workspace_zero():
         gpu, ref = run_case(w, fan, C, 1.0, workspace=ws)
         check(gpu, ref, w, f"cache shared workspace {i}")
         assert int(ws.count_nonzero().item()) == 0
+
+
+def test_cache_unaligned_strided_rows():
+    # Rows whose start is not 16-byte aligned take the element path.
+    w = workloads.make_chain(20, 3, 3001, dtype="bf16", sigma=3.0, temps="half0_half1", gen_seed=31,
+                             philox_seed=31, F=4)
+    fan = (4, 3, 2, 4)
+    w = saguaro_tokens(w, fan, 0.5, seed=32)
+    d = chain_to_dev(w)
+    B, rows, V = w.B, w.gamma + 1, w.V
+    big_t = torch.zeros((B, rows, V + 3), dtype=torch.bfloat16, device="cuda")
+    big_d = torch.zeros_like(big_t)
+    big_t[:, :, 1:V + 1] = d["target"]
+    big_d[:, :, 1:V + 1] = d["draft"]
+    t_view, d_view = big_t[:, :, 1:V + 1], big_d[:, :, 1:V + 1]
+    log("cache unaligned rows")
+    out = binding.verify_cache(t_view, d_view, d["tokens"], d["temperature"], fan, w.seed, 0, saguaro_C=0.5)
+    torch.cuda.synchronize()
+    gpu = {k: v.cpu().numpy() for k, v in out.items() if v is not None}
+    ref = oracle.ssd.verify_cached_batch(w.target.astype(np.float64), w.draft.astype(np.float64), w.draft_tokens,
+                                         w.temperature, w.seed, 0, fan, C=0.5)
+    assert check(gpu, ref, w, "cache unaligned") <= 2
