@@ -33,15 +33,21 @@ template <int DT> struct ElemT;
 template <> struct ElemT<DT_F32> { static constexpr int kBytes = 4; };
 template <> struct ElemT<DT_BF16> { static constexpr int kBytes = 2; };
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// bf16 -> fp32 is exact (the 16 bits become the high half). It is written as
+// a floating-point conversion rather than as bit operations so that the
+// compiler knows the results are canonical floats: a max over them then
+// needs no NaN-quieting instruction per operand, and chains of max fold into
+// three-operand max instructions.
+__device__ __forceinline__ float bf16_bits(uint16_t h) { return float(__builtin_bit_cast(__bf16, h)); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return bf16_bits(uint16_t(w)); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return bf16_bits(uint16_t(w >> 16)); }
 
 template <int DT>
 __device__ __forceinline__ float load_elem(const void* row, int64_t j) {
     if constexpr (DT == DT_F32) {
         return static_cast<const float*>(row)[j];
     } else {
-        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(row)[j]) << 16);
+        return bf16_bits(static_cast<const uint16_t*>(row)[j]);
     }
 }
 
@@ -62,6 +68,39 @@ __device__ __forceinline__ void load_raw8(Raw8<DT>& r, const char* p) {
         const u32x4_t x = __builtin_nontemporal_load(q + i);
         r.w[i] = make_uint4(x.x, x.y, x.z, x.w);
     }
+}
+
+// The streaming loop reads through buffer resources (base and size in scalar
+// registers). A load whose offset lies at or past the resource's size returns
+// zero without touching memory, so the loop needs no per-lane address
+// arithmetic or clamping: each lane keeps one fixed offset, and the scalar
+// unit moves the base. Only the per-lane offset is range checked (the scalar
+// offset operand is not), hence the base, not that operand, advances.
+constexpr int32_t kRsrcWord3 = 0x00020000;   // gfx9 raw buffer: 32-bit data format
+constexpr int kNontemporal = 2;              // cache-policy operand: nt
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t step_rsrc(const char* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, int32_t(bytes), kRsrcWord3);
+}
+
+template <int DT>
+__device__ __forceinline__ void buffer_raw8(Raw8<DT>& r, __amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+#pragma unroll
+    for (int i = 0; i < ElemT<DT>::kBytes / 2; ++i) {
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, int32_t(voff + 16u * i), 0, kNontemporal);
+        r.w[i] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+}
+
+// Values the caller guarantees equal across the workgroup, moved to scalar
+// registers (the compiler cannot prove it for values read from LDS).
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+    return int64_t((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+    return reinterpret_cast<const char*>(uniform_i64(reinterpret_cast<int64_t>(p)));
 }
 
 template <int DT>
@@ -101,7 +140,7 @@ __device__ __forceinline__ float max8(const float v[kLaneElems]) {
 // are unpacked at a time. Every load in the loop is issued unconditionally
 // (a load under a per-lane or per-iteration branch makes the compiler wait
 // for every outstanding load before the processing, which would serialise
-// the ring); refills past the last iteration are clamped and never visited.
+// the ring); refills past the last iteration read zeros and are never visited.
 // Per-lane validity is tested only in the last iteration.
 template <int DT, int U, class Acc>
 __device__ __forceinline__ void visit_steps(const Raw8<DT> (&r)[U], int64_t lo, int64_t s0, int64_t nstep,
@@ -128,19 +167,27 @@ __device__ __forceinline__ void stream_chunk(const void* row, int64_t lo, int64_
     static_assert(U >= 1 && D >= 0, "U >= 1 steps per iteration; D = 0 (prefetch) or a ring of D >= 1");
     constexpr int kB = ElemT<DT>::kBytes;
     constexpr int64_t kStride = int64_t(kThreads) * U;
-    const char* base = static_cast<const char*>(row) + lo * kB;
+    constexpr uint32_t kStepBytes = kLaneElems * kB;
+    lo = uniform_i64(lo);
+    hi = uniform_i64(hi);
+    const char* base = uniform_ptr(static_cast<const char*>(row) + lo * kB);
     const int64_t n = hi - lo;
     const bool aligned = (reinterpret_cast<uintptr_t>(base) & 15u) == 0;
     const int64_t nstep = aligned ? n / kLaneElems : 0;
     const int64_t nit = (nstep + kStride - 1) / kStride;
-    const int64_t last = nstep - 1;
-    // Loads of steps past the end are clamped to the last step (in bounds,
-    // and the same line for every such lane); their data is never used.
+    // Steps are read through a resource over the whole steps of the chunk
+    // (fewer than 2^32 bytes: rows hold at most kMaxTiles * kTileElems
+    // elements); steps past the end read as zero and are never visited.
+    // (The remaining size is a signed max, which the scalar unit has; an
+    // unsigned saturating subtract would be computed per lane and force a
+    // loop over lanes around every load.)
+    const int32_t total = int32_t(nstep) * int32_t(kStepBytes);
+    const uint32_t voff = threadIdx.x * kStepBytes;
     auto load_it = [&](Raw8<DT> (&r)[U], int64_t it) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t s = it * kStride + threadIdx.x + int64_t(u) * kThreads;
-            load_raw8<DT>(r[u], base + (s < last ? s : last) * (kLaneElems * kB));
+            const int32_t start = int32_t(it * kStride + int64_t(u) * kThreads) * int32_t(kStepBytes);
+            buffer_raw8<DT>(r[u], step_rsrc(base + start, uint32_t(max(total - start, 0))), voff);
         }
     };
 

@@ -1,0 +1,116 @@
+// Dispatch order of the chain launches: which sequence and which task each
+// workgroup index stands for. Plain integer arithmetic with no GPU types, so
+// that the host (and a CPU test) can check it.
+//
+// Every launch relies on two properties of these maps, since workgroups are
+// started in index order and a waiting workgroup holds its CU slot:
+//   * each map is a bijection from [0, B * (RS + H)) onto the tasks;
+//   * every bonus workgroup of a sequence comes after all of its rows, and its
+//     H bonus workgroups come in order h = 0 .. H-1 (the last one collects
+//     what the others publish).
+// Then everything a workgroup waits for was started before it.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define SPECV_HD __host__ __device__
+#else
+#define SPECV_HD
+#endif
+
+namespace specv {
+
+// How many sequences the bonus workgroups of a sequence trail its rows by in
+// dispatch order: about one GPU-full of row workgroups (RS per sequence), so
+// that when they start their rows are (nearly) done and they do not hold CU
+// slots waiting.
+inline SPECV_HD int32_t bonus_delay(int64_t B, int64_t RS) {
+    const int64_t d = (1536 + RS - 1) / RS;
+    return int32_t(d < B ? d : B);
+}
+
+// Chain launch: unit u = the RS row workgroups of the sequence in dispatch
+// slot u (u < B), then the H bonus workgroups of sequence u - D (u >= D).
+// Maps workgroup g to its sequence slot and its index w in that sequence
+// (w < RS: row chunk w; else bonus workgroup w - RS). 0 <= D <= B.
+inline SPECV_HD void decode_chain(int64_t g, int64_t B, int64_t RS, int64_t H, int64_t D, int& sidx,
+                                  int64_t& w) {
+    const int64_t a_end = D * RS;                      // units 0..D-1: rows only
+    const int64_t b_end = a_end + (B - D) * (RS + H);  // units D..B-1: rows, then bonus of u - D
+    if (g < a_end) {
+        sidx = int(g / RS);
+        w = g % RS;
+    } else if (g < b_end) {
+        const int64_t u = D + (g - a_end) / (RS + H);
+        const int64_t o = (g - a_end) % (RS + H);
+        sidx = int(o < RS ? u : u - D);
+        w = o;
+    } else {                                           // units B..B+D-1: bonus only
+        const int64_t i = g - b_end;
+        sidx = int(B - D + i / H);
+        w = RS + i % H;
+    }
+}
+
+// Fused verify + top-F launch. Sequence slots 0 .. nS-1 hold the T > 0
+// sequences and nS .. B-1 the greedy ones; each has `half` target rows
+// (w = 0 .. half-1) and `half` draft rows (w = half .. 2*half-1), RS = 2*half
+// rows in all. The rows come in B units of RS workgroups: first the T > 0
+// sequences (unit u = sequence u), then the greedy sequences' rows as one
+// list, all draft rows (top-K: the longest rows) before all target rows
+// (argmax: the shortest). The H bonus workgroups of T > 0 sequence v follow
+// row unit v + D, so their draws (which re-read a row) overlap later rows,
+// greedy ones included; the greedy sequences' bonus workgroups come last.
+// The launch thus ends on its shortest rows: longest first keeps the partly
+// idle tail of the launch short. With nS = B this is decode_chain.
+inline SPECV_HD void decode_fused(int64_t g, int64_t B, int64_t nS, int64_t half, int64_t H, int64_t D, int& sidx,
+                                  int64_t& w) {
+    const int64_t RS = 2 * half;
+    const int64_t nG = B - nS;
+    if (D > B) D = B;
+    const int64_t u2 = D + nS < B ? D + nS : B;       // units D .. u2-1 carry a bonus unit
+    const int64_t r1 = D * RS;                          // units 0 .. D-1: rows only
+    const int64_t r2 = r1 + (u2 - D) * (RS + H);        // units D .. u2-1: rows, then bonus of u - D
+    const int64_t r3 = r2 + (B - u2) * RS;              // units u2 .. B-1: rows only
+    const int64_t r4 = r3 + (nS - (u2 - D)) * H;        // bonus of T > 0 sequences u2-D .. nS-1
+    int64_t u, o;                                       // row unit and row within it
+    if (g < r1) {
+        u = g / RS;
+        o = g % RS;
+    } else if (g < r2) {
+        u = D + (g - r1) / (RS + H);
+        o = (g - r1) % (RS + H);
+        if (o >= RS) {
+            sidx = int(u - D);
+            w = o;
+            return;
+        }
+    } else if (g < r3) {
+        u = u2 + (g - r2) / RS;
+        o = (g - r2) % RS;
+    } else if (g < r4) {
+        sidx = int(u2 - D + (g - r3) / H);
+        w = RS + (g - r3) % H;
+        return;
+    } else {                                            // greedy bonus workgroups
+        sidx = int(nS + (g - r4) / H);
+        w = RS + (g - r4) % H;
+        return;
+    }
+    if (u < nS) {
+        sidx = int(u);
+        w = o;
+        return;
+    }
+    const int64_t k = (u - nS) * RS + o;                // index in the greedy row list
+    if (k < nG * half) {                                // draft rows
+        sidx = int(nS + k / half);
+        w = half + k % half;
+    } else {                                            // target rows
+        sidx = int(nS + (k - nG * half) / half);
+        w = (k - nG * half) % half;
+    }
+}
+
+}  // namespace specv

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "specv_device.hpp"
+#include "specv_dispatch.hpp"
 
 namespace specv {
 
@@ -115,38 +116,6 @@ inline int32_t bonus_helpers(int64_t V) {
     const int64_t ntiles = (V + kTileElems - 1) / kTileElems;
     const int64_t h = (ntiles + 31) / 32;
     return int32_t(h < 1 ? 1 : h > 16 ? 16 : h);
-}
-
-// How many sequences the bonus workgroups of a sequence trail its rows by in
-// dispatch order: about one GPU-full of row workgroups (RS per sequence), so
-// that when they start their rows are (nearly) done and they do not hold CU
-// slots waiting.
-inline int32_t bonus_delay(int64_t B, int64_t RS) {
-    const int64_t d = (1536 + RS - 1) / RS;
-    return int32_t(d < B ? d : B);
-}
-
-// Dispatch order of a chain launch: unit u = the RS row workgroups of the
-// sequence in dispatch slot u (u < B), then the H bonus workgroups of
-// sequence u - D (u >= D). Maps workgroup g to its sequence slot and its
-// index w in that sequence (w < RS: row chunk w; else bonus workgroup w - RS).
-__device__ __forceinline__ void decode_chain(int64_t g, int64_t B, int64_t RS, int64_t H, int64_t D, int& sidx,
-                                             int64_t& w) {
-    const int64_t a_end = D * RS;                      // units 0..D-1: rows only
-    const int64_t b_end = a_end + (B - D) * (RS + H);  // units D..B-1: rows, then bonus of u - D
-    if (g < a_end) {
-        sidx = int(g / RS);
-        w = g % RS;
-    } else if (g < b_end) {
-        const int64_t u = D + (g - a_end) / (RS + H);
-        const int64_t o = (g - a_end) % (RS + H);
-        sidx = int(o < RS ? u : u - D);
-        w = o;
-    } else {                                           // units B..B+D-1: bonus only
-        const int64_t i = g - b_end;
-        sidx = int(B - D + i / H);
-        w = RS + i % H;
-    }
 }
 
 // Walkers per tree wanted for a vocabulary of V: about 32 tiles each (the

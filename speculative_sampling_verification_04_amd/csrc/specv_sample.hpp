@@ -50,14 +50,16 @@ __device__ __forceinline__ void block_merge_argmax(float& v, int32_t& i) {
 constexpr int kMaxOrderedBatch = 4096;
 
 // Dispatch order of sequences: those with T > 0 first, then the greedy ones,
-// each group by increasing index (identity when B > kMaxOrderedBatch). A
-// sequence's last workgroup resolves it, and only T > 0 sequences re-read a
-// row to draw the bonus, so this keeps the cheap resolves at the end of the
-// grid. Returns the sequence handled by dispatch slot s (whole workgroup).
-__device__ int sequence_for_slot(const float* temperature, int B, int s) {
-    if (B > kMaxOrderedBatch) return s;
-    __shared__ uint64_t masks[kMaxOrderedBatch / kWaveSize];
-    __shared__ int s_b;
+// each group by increasing index (identity when B > kMaxOrderedBatch). Only
+// T > 0 sequences re-read a row to draw the bonus, so their bonus workgroups
+// start early and overlap the greedy sequences' rows.
+//
+// sampled_sequences: ballot masks of the T > 0 sequences into `masks` (LDS,
+// kMaxOrderedBatch / kWaveSize words) and their number, or -1 when B >
+// kMaxOrderedBatch (no reordering). Whole workgroup.
+__device__ int sampled_sequences(const float* temperature, int B, uint64_t* masks) {
+    if (B > kMaxOrderedBatch) return -1;
+    __shared__ int s_total;
     const int nm = (B + kWaveSize - 1) / kWaveSize;
     for (int c = wave_id(); c < nm; c += kWaves) {
         const int i = c * kWaveSize + lane_id();
@@ -68,6 +70,19 @@ __device__ int sequence_for_slot(const float* temperature, int B, int s) {
     if (threadIdx.x == 0) {
         int total = 0;
         for (int c = 0; c < nm; ++c) total += __popcll(masks[c]);
+        s_total = total;
+    }
+    __syncthreads();
+    return s_total;
+}
+
+// The sequence in dispatch slot s, given sampled_sequences' masks and count.
+// Whole workgroup.
+__device__ int sequence_at(const uint64_t* masks, int B, int total, int s) {
+    if (total < 0) return s;
+    __shared__ int s_b;
+    if (threadIdx.x == 0) {
+        const int nm = (B + kWaveSize - 1) / kWaveSize;
         const bool sampled = s < total;
         int k = sampled ? s : s - total;
         int b = s;
@@ -87,6 +102,12 @@ __device__ int sequence_for_slot(const float* temperature, int B, int s) {
     }
     __syncthreads();
     return s_b;
+}
+
+// The sequence handled by dispatch slot s (whole workgroup).
+__device__ int sequence_for_slot(const float* temperature, int B, int s) {
+    __shared__ uint64_t masks[kMaxOrderedBatch / kWaveSize];
+    return sequence_at(masks, B, sampled_sequences(temperature, B, masks), s);
 }
 
 // Waits until the n slots are all published (wave 0 polls with agent-scope

@@ -9,8 +9,9 @@
 // selection, writes that row's candidates directly, and publishes its
 // statistics; target rows are as in the verify kernel. Per sequence the
 // slots are target rows 0..gamma, then draft rows 0..gamma; the sequence's H
-// bonus workgroups follow and resolve it (chain_resolve). Used when every row
-// fits one workgroup (S = 1); otherwise the library runs the two kernels.
+// bonus workgroups come after its rows (decode_fused) and resolve it
+// (chain_resolve). Used when every row fits one workgroup (S = 1); otherwise
+// the library runs the two kernels.
 #include "specv_chain.hpp"
 #include "specv_topk.hpp"
 
@@ -43,11 +44,13 @@ template <int DT, int K, bool Cache>
 __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     constexpr int esz = ElemT<DT>::kBytes;
     const int R1 = 2 * a.gamma + 2;
+    __shared__ uint64_t masks[kMaxOrderedBatch / kWaveSize];
+    const int nS = sampled_sequences(a.temperature, a.B, masks);
     int sidx;
     int64_t w;
-    decode_chain(blockIdx.x, a.B, R1, a.H, a.D, sidx, w);
+    decode_fused(blockIdx.x, a.B, nS < 0 ? a.B : nS, a.gamma + 1, a.H, a.D, sidx, w);
     const int slot = int(w);
-    const int b = sequence_for_slot(a.temperature, a.B, sidx);
+    const int b = sequence_at(masks, a.B, nS, sidx);
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
     const int64_t words = R1 + (Cache ? 3 * (a.gamma + 1) : 0);  // per sequence

@@ -1,0 +1,22 @@
+"""The dispatch maps of the chain launches (csrc/specv_dispatch.hpp), checked
+on the CPU: bijections onto the tasks, bonus workgroups after their rows and in
+order, and the longest-first layout of the fused launch's greedy sequences."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(os.path.dirname(HERE), "speculative_sampling_verification_04_amd", "csrc")
+
+
+def test_dispatch_maps(tmp_path):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path / "dispatch_order_check")
+    subprocess.run([gxx, "-O1", "-std=c++17", "-I", CSRC, os.path.join(HERE, "dispatch_order_check.cpp"), "-o", exe],
+                   check=True)
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0 and res.stdout.strip() == "ok", res.stdout + res.stderr
