@@ -59,7 +59,8 @@ typedef enum {
  * `data` points at element [0][0][0] and must be aligned to the element size.
  * Strides are in elements (not bytes), may be 0 (broadcast) and must be >= 0;
  * the vocabulary dimension is contiguous. Rows whose start is 16-byte aligned
- * are read with 16-byte vector loads, others element by element. */
+ * are read with 16-byte vector loads, others element by element. Logits may
+ * be -inf but never NaN (results are unspecified for NaN logits). */
 typedef struct {
     const void* data;
     int32_t dtype;        /* specv_dtype */

@@ -118,9 +118,32 @@ __device__ __forceinline__ void unpack8(const Raw8<DT>& r, float v[kLaneElems]) 
     }
 }
 
+// Three-operand max as one instruction. Written out because the compiler,
+// given a max over widened bf16 values whose only use is more max and
+// compares, narrows it to bf16 and converts every intermediate back and forth
+// (three instructions per max). Logits are never NaN (the interface requires
+// it), so the IEEE-mode NaN rules of the instruction do not matter.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ float max8(const float v[kLaneElems]) {
-    return fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
-                 fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    const float a = max3f(v[0], v[1], v[2]);
+    const float b = max3f(v[3], v[4], v[5]);
+    return max3f(max3f(a, v[6], v[7]), b, b);
+}
+
+// Maximum over U groups' maxima.
+template <int U>
+__device__ __forceinline__ float max_of(const float (&m)[U]) {
+    float r = m[0];
+    int u = 1;
+#pragma unroll
+    for (; u + 1 < U; u += 2) r = max3f(r, m[u], m[u + 1]);
+    if (u < U) r = max3f(r, m[u], m[u]);
+    return r;
 }
 
 // ------------------------------------------------------------- streaming
@@ -395,9 +418,10 @@ struct SoftmaxAcc {
 
     template <int U>
     __device__ __forceinline__ void block(const float (&v)[U][kLaneElems], const int64_t*, const bool*) {
-        float cm = max8(v[0]);
+        float gm[U];
 #pragma unroll
-        for (int u = 1; u < U; ++u) cm = fmaxf(cm, max8(v[u]));
+        for (int u = 0; u < U; ++u) gm[u] = max8(v[u]);
+        const float cm = max_of<U>(gm);
         rebase(cm);
         const float nmc = (m == -INFINITY) ? 0.0f : -mc;
         float part[U];

@@ -3,20 +3,19 @@
 // 4.1.1].
 //
 // Keys: (order-preserving logit key << 32) | ~index, so a larger key is a
-// larger logit, or an equal logit at a lower index. Each lane tracks only its
-// running maximum value. Every other streaming iteration the wave forms a
-// lower bound theta on the K-th largest key seen so far: the
-// minimum, over K groups of lanes, of each group's largest lane maximum (K
-// distinct elements are >= theta). An 8-element group whose maximum reaches
-// theta is recorded as a candidate (its start index and its largest key) in
-// the wave's LDS list; every other group cannot hold one of the K largest
-// keys. When the list runs full, and at the end of the chunk, it is compacted
-// exactly from LDS: the K groups with the largest maxima are kept and theta
-// becomes the K-th of those maxima. The K largest keys of the chunk then lie
-// in the kept groups.
+// larger logit, or an equal logit at a lower index. The row is seen in
+// 8-element groups, and a group's key is (its maximum's logit key << 32) |
+// ~(its start): groups do not overlap, so group keys order groups exactly as
+// the keys of their largest elements do. Each wave records the groups whose
+// maximum reaches a threshold theta in an LDS list (start, group key). When
+// the list runs full, and at the end of the chunk, it is compacted exactly:
+// the K groups with the largest keys are kept and theta becomes the K-th of
+// them. A group whose maximum is below theta's logit cannot hold one of the K
+// largest elements (each of the K kept groups holds an element at least that
+// large), so the K largest keys of the chunk lie in the kept groups. While
+// streaming, a group costs one compare against theta; recording is rare once
+// theta has settled.
 #pragma once
-
-#include <limits.h>
 
 #include "specv_sample.hpp"
 
@@ -30,57 +29,24 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 }
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ uint64_t group_key(float vm, int64_t start) {
+    return (uint64_t(logit_key(vm)) << 32) | uint64_t(~uint32_t(start));
+}
 
 template <int DT, int K>
 struct TopKAcc {
     static_assert(K >= 1 && K <= 32 && (K & (K - 1)) == 0, "K is a power of two <= 32");
-    static constexpr int kGroupLanes = kWaveSize / K;
 
-    const void* row;
-    int64_t hi;          // elements at or past hi are not part of the chunk
     int32_t* ent;        // this wave's candidates (LDS, kCandCap each): start
-    uint64_t* mkey;      //   index (| kSingle for one element) and largest key
+    uint64_t* mkey;      //   index (| kSingle for one element) and group key
     int count;           // wave-uniform
-    float lm;            // lane maximum (li < 0: the lane has seen no element yet)
-    int32_t li;
-    uint64_t theta;      // wave-uniform lower bound on the K-th largest key (0: none)
-    float th_val;
-    int32_t th_idx;
-    int iter;            // block() calls so far
+    uint64_t theta;      // wave-uniform: K-th largest group key at the last compaction (0: none)
+    float th_val;        // its logit (-inf: none)
 
-    __device__ void init(const void* r, int64_t h, int32_t* e, uint64_t* k) {
-        row = r; hi = h; ent = e; mkey = k; count = 0;
-        lm = -INFINITY; li = -1;
-        theta = 0; th_val = -INFINITY; th_idx = INT_MAX;
-        iter = 0;
-    }
-
-    // theta's logit and index; an index part of 0 (key lo) stands for "any
-    // index", i.e. th_idx = INT_MAX.
-    __device__ __forceinline__ void raise_theta(uint64_t k) {
-        if (k > theta) {
-            theta = k;
-            th_val = key_logit(uint32_t(k >> 32));
-            th_idx = uint32_t(k) == 0u ? INT_MAX : int32_t(~uint32_t(k));
-        }
-    }
-
-    // Min over K groups of the group's largest lane maximum (wave-uniform
-    // result), on logit keys only: (key << 32 | 0) is below every full key with
-    // that logit, so it is still a lower bound on the K-th largest full key.
-    __device__ __forceinline__ void refresh() {
-        uint32_t k = li >= 0 ? logit_key(lm) : 0u;
-#pragma unroll
-        for (int o = 1; o < kGroupLanes; o <<= 1) k = max(k, uint32_t(__shfl_xor(k, o)));
-#pragma unroll
-        for (int o = kGroupLanes; o < kWaveSize; o <<= 1) k = min(k, uint32_t(__shfl_xor(k, o)));
-        raise_theta(uint64_t(k) << 32);
-    }
-
-    // A group with maximum vm starting at `start` may hold a key >= theta.
-    __device__ __forceinline__ bool reaches(float vm, int64_t start) const {
-        return vm > th_val || (vm == th_val && start <= th_idx);
+    __device__ void init(int32_t* e, uint64_t* k) {
+        ent = e; mkey = k; count = 0;
+        theta = 0; th_val = -INFINITY;
     }
 
     __device__ __forceinline__ void push(bool pass, int32_t e, uint64_t key) {
@@ -93,9 +59,9 @@ struct TopKAcc {
         count += __popcll(m);
     }
 
-    // Exact compaction from LDS: the K-th largest recorded group maximum
-    // becomes theta and only the groups whose maximum reaches it are kept
-    // (nothing changes while fewer than K candidates exist).
+    // Exact compaction from LDS: the K-th largest recorded group key becomes
+    // theta and only the groups whose key reaches it are kept (nothing
+    // changes while fewer than K candidates exist).
     __device__ void compact() {
         if (count < K) return;
         // Keys are unique: round k finds the largest key below round k-1's.
@@ -108,7 +74,10 @@ struct TopKAcc {
             }
             kth = wave_max_u64(l);
         }
-        raise_theta(kth);
+        if (kth > theta) {
+            theta = kth;
+            th_val = key_logit(uint32_t(kth >> 32));
+        }
         int n = 0;
         for (int base = 0; base < count; base += kWaveSize) {
             const int i = base + lane_id();
@@ -130,35 +99,19 @@ struct TopKAcc {
     __device__ __forceinline__ void block(const float (&v)[U][kLaneElems], const int64_t* base, const bool* valid) {
         float vm[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            vm[u] = max8(v[u]);
-            if (valid[u] && (vm[u] > lm || li < 0)) {
-                lm = vm[u];
-                li = int32_t(base[u]);
-            }
-        }
-        if ((++iter & 1) == 0) refresh();  // every other iteration: theta only lags
+        for (int u = 0; u < U; ++u) vm[u] = max8(v[u]);
         if (count > kCandCap - kWaveSize * U) compact();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const bool pass = valid[u] && reaches(vm[u], base[u]);
-            uint64_t key = 0;
-            if (pass) {  // rare once theta has settled: locate the group maximum
-                int e = kLaneElems - 1;
-#pragma unroll
-                for (int k = kLaneElems - 2; k >= 0; --k) e = (v[u][k] == vm[u]) ? k : e;
-                key = full_key(vm[u], base[u] + e);
-            }
-            push(pass, int32_t(base[u]), key);
+            const bool pass = valid[u] && vm[u] >= th_val;
+            push(pass, int32_t(base[u]), pass ? group_key(vm[u], base[u]) : 0ull);
         }
     }
 
     __device__ __forceinline__ void one(float z, int64_t j, bool ok) {
-        if (ok && (z > lm || li < 0)) { lm = z; li = int32_t(j); }
-        refresh();
         if (count > kCandCap - kWaveSize) compact();
-        const bool pass = ok && reaches(z, j);
-        push(pass, int32_t(j) | kSingle, pass ? full_key(z, j) : 0);
+        const bool pass = ok && z >= th_val;
+        push(pass, int32_t(j) | kSingle, pass ? full_key(z, j) : 0ull);
     }
 };
 
@@ -183,6 +136,9 @@ __device__ __forceinline__ const uint64_t* topf_finish(TopKAcc<DT, K>& acc, cons
     uint64_t th = s_theta[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) th = umax64(th, s_theta[w]);
+    // The logit part only: every element of the workgroup's K largest has a
+    // logit at least that of every wave's K-th group maximum.
+    th &= 0xffffffff00000000ull;
 
     // Keys that reach the workgroup threshold: at most 8 per kept group.
     for (int e = lane_id(); e < acc.count; e += kWaveSize) {

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kThreads) void topf_kernel(TopFArgs a) {
     __shared__ int32_t cand[kWaves][kCandCap];
     __shared__ uint64_t cand_key[kWaves][kCandCap];
     TopKAcc<DT, K> acc;
-    acc.init(rp, a.V, cand[wave_id()], cand_key[wave_id()]);
+    acc.init(cand[wave_id()], cand_key[wave_id()]);
     stream_chunk<DT, kU, kD>(rp, 0, a.V, acc);
     const int32_t excl = (a.tokens != nullptr && k < a.gamma) ? a.tokens[int64_t(b) * a.gamma + k] : -1;
     const int64_t out = (int64_t(b) * rows + k) * a.F;

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
         const uint64_t* pick;
         if (!greedy && row < a.gamma) {
             SoftmaxTopK<DT, K> acc(log2e_over(T));
-            acc.tk.init(rp, V, cand[wave_id()], cand_key[wave_id()]);
+            acc.tk.init(cand[wave_id()], cand_key[wave_id()]);
             stream_chunk<DT, kDraftU, kDraftD>(rp, 0, V, acc);
             block_merge_softmax(acc.sm.m, acc.sm.mc, acc.sm.s);
             word = pack_softmax(acc.sm.m, acc.sm.s);
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
             }
         } else {
             TopKAcc<DT, K> acc;
-            acc.init(rp, V, cand[wave_id()], cand_key[wave_id()]);
+            acc.init(cand[wave_id()], cand_key[wave_id()]);
             stream_chunk<DT, kDraftU, kDraftD>(rp, 0, V, acc);
             pick = topf_finish<DT, K>(acc, rp, V, Fk, a.F, excl, ids, vals);
         }
