@@ -141,14 +141,13 @@ size_t verify_topk_bytes(int64_t batch, int64_t gamma, int64_t vocab) {
     return plain > fused ? plain : fused;
 }
 
-// Tree workspace: the row words, then per tree the walk words (commands,
-// acknowledgements, tile sums).
+// Tree workspace: the row words, then per tree the walk words (the walkers'
+// pass totals, acknowledgements, the drawn token).
 size_t tree_walk_offset(int64_t batch, int64_t nodes, int64_t vocab) {
     return layout_for(batch, 2 * nodes, vocab).slot_bytes;
 }
 size_t tree_bytes(int64_t batch, int64_t nodes, int64_t vocab) {
-    const int64_t ntiles = (vocab + kTileElems - 1) / kTileElems;
-    return tree_walk_offset(batch, nodes, vocab) + round_up(size_t(batch) * (kWalkHeader + ntiles) * sizeof(uint64_t));
+    return tree_walk_offset(batch, nodes, vocab) + round_up(size_t(batch) * kWalkWords * sizeof(uint64_t));
 }
 
 specv_status check_tree_sizes(int32_t batch, int32_t nodes, int32_t vocab) {

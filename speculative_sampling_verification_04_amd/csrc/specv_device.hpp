@@ -355,16 +355,50 @@ __device__ __forceinline__ void wave_merge_argmax(float& v, int32_t& i) {
     }
 }
 
-__device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-    for (int o = 1; o < kWaveSize; o <<= 1) x += __shfl_xor(x, o);
-    return x;
+// Wave sums through DPP row moves (no LDS round trip per step): pairs within
+// quads, then half-row and row mirrors give every lane its 16-lane row sum;
+// two row broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3)
+// leave the total in lane 63, which is returned to every lane. Disabled rows
+// of a broadcast add 0.
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kCtrl, kRowMask, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140,
+              kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ float dpp_f32(float v) { return __uint_as_float(dpp_u32<kCtrl, kRowMask>(__float_as_uint(v))); }
+
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = uint64_t(__double_as_longlong(v));
+    const uint32_t lo = dpp_u32<kCtrl, kRowMask>(uint32_t(u));
+    const uint32_t hi = dpp_u32<kCtrl, kRowMask>(uint32_t(u >> 32));
+    return __longlong_as_double(int64_t((uint64_t(hi) << 32) | lo));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int o = 1; o < kWaveSize; o <<= 1) x += __shfl_xor(x, o);
-    return x;
+    x += dpp_f32<kDppQuadXor1>(x);
+    x += dpp_f32<kDppQuadXor2>(x);
+    x += dpp_f32<kDppRowHalfMirror>(x);
+    x += dpp_f32<kDppRowMirror>(x);
+    x += dpp_f32<kDppRowBcast15, 0xa>(x);
+    x += dpp_f32<kDppRowBcast31, 0xc>(x);
+    return __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(__float_as_uint(x)), kWaveSize - 1)));
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+    x += dpp_f64<kDppQuadXor1>(x);
+    x += dpp_f64<kDppQuadXor2>(x);
+    x += dpp_f64<kDppRowHalfMirror>(x);
+    x += dpp_f64<kDppRowMirror>(x);
+    x += dpp_f64<kDppRowBcast15, 0xa>(x);
+    x += dpp_f64<kDppRowBcast31, 0xc>(x);
+    const uint64_t u = uint64_t(__double_as_longlong(x));
+    const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u)), kWaveSize - 1));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u >> 32)), kWaveSize - 1));
+    return __longlong_as_double(int64_t((uint64_t(hi) << 32) | lo));
 }
 
 // Inclusive prefix sum across the wave (lane order).
@@ -376,6 +410,11 @@ __device__ __forceinline__ double wave_inclusive_scan(double x) {
         if (lane >= o) x += y;
     }
     return x;
+}
+
+// Number of lanes below this one whose bit is set in m.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {

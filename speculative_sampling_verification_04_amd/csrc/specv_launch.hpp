@@ -65,11 +65,11 @@ struct ChainArgs {
 
 // Tree verification. Per tree there are 2N row tasks (target rows of every
 // node, then draft rows of every node), each split into S chunks, one slot
-// per chunk (slots[(b * 2N + task) * S + chunk]). The walk runs H
-// workgroups per tree that meet in `walk` (kWalkHeader + ntiles words per
-// tree: two command words, one acknowledgement per walker, the tile sums).
+// per chunk (slots[(b * 2N + task) * S + chunk]), and H walkers that meet in
+// `walk` (kWalkWords words per tree: the walkers' pass totals for two pass
+// parities, one acknowledgement per walker, the drawn token).
 constexpr int kMaxWalkers = 16;
-constexpr int kWalkHeader = 2 + kMaxWalkers;
+constexpr int kWalkWords = 3 * kMaxWalkers + 1;
 
 struct TreeArgs {
     RowView target, draft;
@@ -118,8 +118,8 @@ inline int32_t bonus_helpers(int64_t V) {
     return int32_t(h < 1 ? 1 : h > 16 ? 16 : h);
 }
 
-// Walkers per tree wanted for a vocabulary of V: about 32 tiles each (the
-// launch lowers it so that every walker of every tree is resident at once).
+// Walkers per tree for a vocabulary of V: about 32 tiles each, at most
+// kMaxWalkers.
 inline int32_t tree_walkers(int64_t V) {
     const int64_t ntiles = (V + kTileElems - 1) / kTileElems;
     const int64_t h = (ntiles + 31) / 32;

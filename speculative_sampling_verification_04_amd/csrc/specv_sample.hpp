@@ -320,6 +320,95 @@ __device__ __forceinline__ double weight_tiles(const WFn& f, int64_t V, float* t
 __device__ __forceinline__ uint64_t pack_tile(float ts) { return (1ull << 32) | uint64_t(__float_as_uint(ts)); }
 __device__ __forceinline__ float tile_of(uint64_t w) { return __uint_as_float(uint32_t(w)); }
 
+// The element of tile `tile` at which the running sum of f's weights over the
+// tile first reaches tin; rounding past the tile's scanned total takes its
+// last positive element. Wave 0 computes; whole workgroup.
+template <class WFn>
+__device__ __forceinline__ int32_t sample_in_tile(const WFn& f, int tile, double tin) {
+    __shared__ int32_t s_idx;
+    const int lane = lane_id();
+    if (wave_id() == 0) {
+        typename WFn::Raw raw;
+        f.load(int64_t(tile) * kTileElems + lane * kLaneElems, raw);
+        float w[kLaneElems];
+        f.weights(raw, int64_t(tile) * kTileElems + lane * kLaneElems, w);
+        double ls = 0.0;
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) ls += double(w[e]);
+        const double incl = wave_inclusive_scan(ls);
+        double acc = __shfl_up(incl, 1);
+        if (lane == 0) acc = 0.0;
+        int fe = -1, le = -1;
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) {
+            acc += double(w[e]);
+            if (fe < 0 && w[e] > 0.0f && acc >= tin) fe = e;
+            if (w[e] > 0.0f) le = e;
+        }
+        const uint64_t m = __ballot(fe >= 0);
+        int32_t idx;
+        if (m != 0) {
+            const int L = __builtin_ctzll(m);
+            idx = tile * kTileElems + L * kLaneElems + __shfl(fe, L);
+        } else {  // rounding: v*W fell past the tile's scanned total; take its last positive element
+            const uint64_t m2 = __ballot(le >= 0);
+            const int L = 63 - __builtin_clzll(m2);
+            idx = tile * kTileElems + L * kLaneElems + __shfl(le, L);
+        }
+        if (lane == 0) s_idx = idx;
+    }
+    __syncthreads();
+    return s_idx;
+}
+
+// The tile of tile_sum[0..n) (fp32 sums of consecutive tiles) at which a
+// running fp64 sum that starts at `base` first reaches `target`, counting
+// positive tiles only, and the remainder of the target inside it (*tin).
+// Rounding that leaves the target past the last tile takes the last positive
+// tile. -1 when no tile is positive. Wave 0 computes; whole workgroup.
+__device__ __forceinline__ int find_tile(const float* tile_sum, int n, double base, double target, double* tin) {
+    __shared__ int32_t s_tile;
+    __shared__ double s_tin;
+    const int lane = lane_id();
+    if (wave_id() == 0) {
+        const int seg = (n + kWaveSize - 1) / kWaveSize;
+        const int t0 = lane * seg;
+        const int t1 = min(n, t0 + seg);
+        double ps = 0.0;
+        bool pos = false;
+        for (int t = t0; t < t1; ++t) { ps += tile_sum[t]; pos = pos || tile_sum[t] > 0.0f; }
+        const double incl = base + wave_inclusive_scan(ps);
+        double excl = __shfl_up(incl, 1);
+        if (lane == 0) excl = base;
+        const uint64_t m = __ballot(pos && incl >= target);
+        const uint64_t mp = __ballot(pos);
+        int tile = -1;
+        double rem = 0.0;
+        if (mp != 0) {
+            const int L = m != 0 ? __builtin_ctzll(m) : 63 - __builtin_clzll(mp);
+            if (lane == L) {
+                double acc = excl;
+                for (int t = t0; t < t1; ++t) {
+                    const float ts = tile_sum[t];
+                    const double nx = acc + double(ts);
+                    if (ts > 0.0f && nx >= target) { tile = t; rem = target - acc; break; }
+                    acc = nx;
+                }
+                if (tile < 0) {  // rounding left the target past this segment: its last positive tile
+                    for (int t = t1 - 1; t >= t0; --t)
+                        if (tile_sum[t] > 0.0f) { tile = t; rem = double(tile_sum[t]); break; }
+                }
+            }
+            tile = __shfl(tile, L);
+            rem = __shfl(rem, L);
+        }
+        if (lane == 0) { s_tile = tile; s_tin = rem; }
+    }
+    __syncthreads();
+    *tin = s_tin;
+    return s_tile;
+}
+
 // Pass B: given the tile sums of pass A, the smallest j with S_j >= v * W.
 // Returns -1 when the total is 0.
 template <class WFn>
@@ -328,7 +417,6 @@ __device__ __forceinline__ int32_t sample_from_tiles(const WFn& f, int64_t V, fl
     const int lane = lane_id();
     __shared__ int32_t s_tile;
     __shared__ double s_tin;
-    __shared__ int32_t s_idx;
     if (wave_id() == 0) {
         const int seg = (ntiles + kWaveSize - 1) / kWaveSize;
         const int t0 = lane * seg;
@@ -365,39 +453,7 @@ __device__ __forceinline__ int32_t sample_from_tiles(const WFn& f, int64_t V, fl
     }
     __syncthreads();
     const int tile = s_tile;
-    if (wave_id() == 0 && tile >= 0) {
-        typename WFn::Raw raw;
-        f.load(int64_t(tile) * kTileElems + lane * kLaneElems, raw);
-        float w[kLaneElems];
-        f.weights(raw, int64_t(tile) * kTileElems + lane * kLaneElems, w);
-        double ls = 0.0;
-#pragma unroll
-        for (int e = 0; e < kLaneElems; ++e) ls += double(w[e]);
-        const double incl = wave_inclusive_scan(ls);
-        double acc = __shfl_up(incl, 1);
-        if (lane == 0) acc = 0.0;
-        const double tin = s_tin;
-        int fe = -1, le = -1;
-#pragma unroll
-        for (int e = 0; e < kLaneElems; ++e) {
-            acc += double(w[e]);
-            if (fe < 0 && w[e] > 0.0f && acc >= tin) fe = e;
-            if (w[e] > 0.0f) le = e;
-        }
-        const uint64_t m = __ballot(fe >= 0);
-        int32_t idx;
-        if (m != 0) {
-            const int L = __builtin_ctzll(m);
-            idx = tile * kTileElems + L * kLaneElems + __shfl(fe, L);
-        } else {  // rounding: v*W fell past the tile's scanned total; take its last positive element
-            const uint64_t m2 = __ballot(le >= 0);
-            const int L = 63 - __builtin_clzll(m2);
-            idx = tile * kTileElems + L * kLaneElems + __shfl(le, L);
-        }
-        if (lane == 0) s_idx = idx;
-    }
-    __syncthreads();
-    return tile >= 0 ? s_idx : -1;
+    return tile >= 0 ? sample_in_tile(f, tile, s_tin) : -1;
 }
 
 }  // namespace specv

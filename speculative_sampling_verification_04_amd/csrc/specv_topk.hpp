@@ -24,10 +24,6 @@ namespace specv {
 constexpr int kCandCap = 256;                  // candidate groups per wave
 constexpr int32_t kSingle = 0x40000000;       // candidate holds one element, not 8
 
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-    return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
-}
-
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 __device__ __forceinline__ uint64_t group_key(float vm, int64_t start) {

@@ -10,13 +10,16 @@
 //    workgroup publishes one 64-bit word.
 //
 // 2. tree_walk_kernel: H workgroups ("walkers") per tree, all resident at
-//    once (a cooperative launch when H > 1). Walker 0 walks the tree from the
-//    root; every full pass over a node's rows that the walk needs is shared by
-//    all H walkers: walker 0 posts the pass as two command words tagged with
-//    the pass number, each walker sums its share of the 512-element tiles and
-//    publishes every tile sum as a word tagged with the same number, and
-//    walker 0 collects them. A pass therefore costs a couple of memory round
-//    trips instead of a single workgroup's walk over two rows.
+//    once (a cooperative launch when H > 1). Every walker of a tree runs the
+//    same walk on the same data and takes the same decisions; each full pass
+//    over a node's rows that the walk needs is split between them: walker h
+//    sums the weights over its share of the 512-element tiles, keeps its tile
+//    sums in LDS and publishes its share's total as one word tagged with the
+//    pass number, and every walker then adds the H totals in walker order. A
+//    pass therefore costs one exchange of H words, with no command round trip;
+//    the accept tests of a node's children are prepared in parallel when the
+//    walk reaches the node. The final draw is made by the walker whose share
+//    holds the inverse-CDF point.
 //
 // MSS bookkeeping: after j rejections at a node the residual is
 //   r_j = max(0, p - c_j q) / M_j,  c_1 = 0, M_1 = 1,
@@ -38,32 +41,29 @@ constexpr int kU = 4;          // 16-byte steps per lane per iteration
 constexpr int kD = 0;          // prefetch form (see stream_chunk)
 constexpr int kWalkTiles = 8;  // tiles in flight per wave in a walk pass
 
-// Pass kinds posted by walker 0.
-constexpr uint32_t kPassTarget = 0;    // weights p of the node
-constexpr uint32_t kPassResidual = 1;  // weights max(0, p - coef * q)
-constexpr uint32_t kPassDone = 2;      // no more passes: acknowledge and exit
-
 __device__ __forceinline__ const void* row_ptr(const RowView& v, int esz, int64_t b, int64_t r) {
     return static_cast<const char*>(v.data) + (b * v.stride_seq + r * v.stride_row) * esz;
 }
 
 __device__ __forceinline__ float log2e_over(float T) { return float(1.4426950408889634 / double(T)); }
 
-// ------------------------------------------------------------------ pass 1
+// ------------------------------------------------------------------ rows
 
+// Row task w of tree b (w = task * S + chunk; task < N: target row of node
+// task, else draft row of node task - N) -> its statistics word.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void tree_stats_kernel(TreeArgs a) {
     constexpr int esz = ElemT<DT>::kBytes;
+    const int64_t RS = int64_t(2) * a.N * a.S;
+    const int b = int(blockIdx.x / RS);
+    const int64_t w = blockIdx.x % RS;
     const int N = a.N;
-    const int64_t g = blockIdx.x;
-    const int chunk = int(g % a.S);
-    const int64_t task = g / a.S;
-    const int slot = int(task % (2 * N));
-    const int b = int(task / (2 * N));
+    const int chunk = int(w % a.S);
+    const int task = int(w / a.S);
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
-    const bool draft_row = slot >= N;
-    const int node = draft_row ? slot - N : slot;
+    const bool draft_row = task >= N;
+    const int node = draft_row ? task - N : task;
     const int64_t lo = int64_t(chunk) * a.chunk;
     const int64_t hi = min(int64_t(a.V), lo + a.chunk);
 
@@ -90,42 +90,35 @@ __global__ __launch_bounds__(kThreads) void tree_stats_kernel(TreeArgs a) {
             word = pack_softmax(acc.m, acc.s);
         }
     }
-    if (threadIdx.x == 0) publish(a.slots + g, word);
+    if (threadIdx.x == 0) publish(a.slots + int64_t(b) * 2 * N * a.S + w, word);
 }
 
 // ------------------------------------------------------------------ walk
 
-// Smallest c > after (and > node) with parent[c] == node, or -1; wave 0 only.
-__device__ int next_child(const int32_t* par, int N, int node, int after) {
-    for (int base = max(after, node) + 1; base < N; base += kWaveSize) {
-        const int c = base + lane_id();
-        const uint64_t m = __ballot(c < N && par[c] == node);
-        if (m) return base + __builtin_ctzll(m);
-    }
-    return -1;
+// Walk words of one tree (a.walk + b * kWalkWords, zero at rest): the walkers'
+// pass totals, double-buffered by pass parity (tag = pass number in the high
+// half, fp32 total in the low half), one acknowledgement per walker, and the
+// bonus word of the final draw (1 << 32 | bonus).
+struct WalkWords {
+    uint64_t* part;   // [2][kMaxWalkers]
+    uint64_t* ack;    // [kMaxWalkers]
+    uint64_t* bonus;  // [1]
+};
+
+__device__ __forceinline__ WalkWords walk_of(const TreeArgs& a, int b) {
+    uint64_t* w = a.walk + int64_t(b) * kWalkWords;
+    return WalkWords{w, w + 2 * kMaxWalkers, w + 3 * kMaxWalkers};
 }
 
-// Lowest-id child of `node` carrying token g, or -1; wave 0 only.
-__device__ int child_with_token(const int32_t* par, const int32_t* tok, int N, int node, int32_t g) {
-    for (int base = node + 1; base < N; base += kWaveSize) {
-        const int c = base + lane_id();
-        const uint64_t m = __ballot(c < N && par[c] == node && tok[c] == g);
-        if (m) return base + __builtin_ctzll(m);
-    }
-    return -1;
-}
-
-__device__ __forceinline__ uint32_t word_hi(uint64_t w) { return uint32_t(w >> 32); }
-
-// Waits until every one of the n words carries tag `p` in its high half
-// (wave 0 polls; bounded like wait_slots). Whole workgroup.
+// Waits until each of the n words carries tag `p` in its high half (wave 0
+// polls; bounded like wait_slots). Whole workgroup.
 __device__ bool wait_tagged(const uint64_t* w, int n, uint32_t p) {
     __shared__ int s_ok;
     if (wave_id() == 0) {
         int ok = 0;
         for (int spin = 0; spin < kMaxSpin; ++spin) {
             bool mine = true;
-            for (int i = lane_id(); i < n; i += kWaveSize) mine = mine && word_hi(peek(w + i)) == p;
+            for (int i = lane_id(); i < n; i += kWaveSize) mine = mine && uint32_t(peek(w + i) >> 32) == p;
             if (__all(mine)) { ok = 1; break; }
             __builtin_amdgcn_s_sleep(2);
         }
@@ -135,257 +128,277 @@ __device__ bool wait_tagged(const uint64_t* w, int n, uint32_t p) {
     return s_ok != 0;
 }
 
-struct Walk {
-    uint64_t* cmd;    // [0]: tag | kind << 16 | node, [1]: tag | bits(coef)
-    uint64_t* ack;    // one per walker
-    uint64_t* tiles;  // ntiles tile words: tag | bits(tile sum)
+// Per-walker state of one walk (LDS of the walker).
+struct WalkLds {
+    RowStats sp, sq;              // statistics of the current node's target and draft rows
+    int32_t kid[kThreads];        // a batch of the current node's children, ascending
+    double pc[kThreads], qc[kThreads];  // p(t), q(t) of each child's token t
+    float u[kThreads];            // each child's uniform
+    float part[kMaxWalkers];      // the walkers' totals of the last pass
+    float tile[kMaxTiles];        // this walker's tile sums of the last pass
+    int nk, from;                 // batch size; next position of the child scan
+    int ok;
 };
 
-__device__ __forceinline__ Walk walk_of(const TreeArgs& a, int b) {
-    uint64_t* w = a.walk + int64_t(b) * (kWalkHeader + a.ntiles);
-    return Walk{w, w + 2, w + kWalkHeader};
-}
-
-// Walker h's share of pass p: the tile sums of the pass's weights over tiles
-// [ntiles*h/H, ntiles*(h+1)/H), each published as tag p | bits(sum).
 template <int DT>
-__device__ __forceinline__ void share_pass(const TreeArgs& a, int b, float c, int node, uint32_t kind, float coef,
-                                           uint32_t p, int h, const Walk& w) {
-    constexpr int esz = ElemT<DT>::kBytes;
-    __shared__ RowStats s_st[2];
-    const uint64_t* slots = a.slots + int64_t(b) * 2 * a.N * a.S;
-    if (threadIdx.x == 0) {
-        s_st[0] = merge_slots(slots + int64_t(node) * a.S, a.S, false, c);
-        s_st[1] = merge_slots(slots + int64_t(a.N + node) * a.S, a.S, false, c);
-    }
-    __syncthreads();
-    const int lo = int(int64_t(a.ntiles) * h / a.H);
-    const int hi = int(int64_t(a.ntiles) * (h + 1) / a.H);
-    auto put = [&](int t, float ts) { publish(w.tiles + t, (uint64_t(p) << 32) | __float_as_uint(ts)); };
-    if (kind == kPassTarget) {
-        TargetWeights<DT> f;
-        f.p.init(row_ptr(a.target, esz, b, node), c, s_st[0]);
-        f.V = a.V;
-        weight_tile_range<kWalkTiles>(f, lo, hi, put);
-    } else {
-        ResidualWeights<DT> f;
-        f.p.init(row_ptr(a.target, esz, b, node), c, s_st[0]);
-        f.q.init(row_ptr(a.draft, esz, b, node), c, s_st[1]);
-        f.coef = coef;
-        f.V = a.V;
-        weight_tile_range<kWalkTiles>(f, lo, hi, put);
-    }
-    __syncthreads();
-}
+struct Walker {
+    const TreeArgs& a;
+    int b, h, N, lo, hi;
+    float c, v;
+    WalkWords w;
+    WalkLds& s;
+    const void* prow;
+    const void* qrow;
+    uint32_t pass = 0;
 
-// Walkers 1 .. H-1: serve passes until walker 0 posts kPassDone.
-template <int DT>
-__device__ __forceinline__ void walk_helper(const TreeArgs& a, int b, int h) {
-    const float T = a.temperature[b];
-    const float c = T > 0.0f ? log2e_over(T) : 0.0f;
-    const Walk w = walk_of(a, b);
-    for (uint32_t p = 1;; ++p) {
-        if (!wait_tagged(w.cmd, 2, p)) return;  // walker 0 reports the failure
-        const uint64_t c0 = peek(w.cmd), c1 = peek(w.cmd + 1);
-        const uint32_t kind = (uint32_t(c0) >> 16) & 3u;
-        if (kind == kPassDone) {
-            if (threadIdx.x == 0) publish(w.ack + h, 1ull);
-            return;
+    // One shared pass over the current node's weights (target: p; else
+    // max(0, p - coef q)). Returns the fp64 sum of the H walker totals, or -1
+    // if a wait ran out.
+    __device__ __forceinline__ double run_pass(bool target, float coef) {
+        ++pass;
+        auto put = [&](int t, float ts) { s.tile[t - lo] = ts; };
+        if (target) {
+            TargetWeights<DT> f;
+            f.p.init(prow, c, s.sp);
+            f.V = a.V;
+            weight_tile_range<kWalkTiles>(f, lo, hi, put);
+        } else {
+            ResidualWeights<DT> f;
+            f.p.init(prow, c, s.sp);
+            f.q.init(qrow, c, s.sq);
+            f.coef = coef;
+            f.V = a.V;
+            weight_tile_range<kWalkTiles>(f, lo, hi, put);
         }
-        share_pass<DT>(a, b, c, int(uint32_t(c0) & 0xffffu), kind, __uint_as_float(uint32_t(c1)), p, h, w);
+        const double mine = tiles_total(s.tile, hi - lo);
+        uint64_t* part = w.part + (pass & 1u) * kMaxWalkers;
+        if (threadIdx.x == 0) publish(part + h, (uint64_t(pass) << 32) | __float_as_uint(float(mine)));
+        if (!wait_tagged(part, a.H, pass)) return -1.0;
+        if (threadIdx.x < a.H) s.part[threadIdx.x] = __uint_as_float(uint32_t(peek(part + threadIdx.x)));
+        __syncthreads();
+        double total = 0.0;
+        for (int k = 0; k < a.H; ++k) total += double(s.part[k]);
+        return total;
     }
-}
 
-// Walker 0: the walk itself.
+    // The next batch of the node's children (ascending ids from s.from) and
+    // their accept-test inputs. Whole workgroup.
+    __device__ __forceinline__ void next_batch(int node) {
+        const int32_t* par = a.parent + int64_t(b) * N;
+        const int32_t* tok = a.tokens + int64_t(b) * N;
+        if (wave_id() == 0) {
+            int n = 0, base = s.from;
+            for (; base < N && n <= kThreads - kWaveSize; base += kWaveSize) {
+                const int ch = base + lane_id();
+                const bool is = ch < N && par[ch] == node;
+                const uint64_t m = __ballot(is);
+                if (is) s.kid[n + lanes_below(m)] = ch;
+                n += __popcll(m);
+            }
+            if (lane_id() == 0) { s.nk = n; s.from = base; }
+        }
+        __syncthreads();
+        if (threadIdx.x < s.nk) {
+            const int ch = s.kid[threadIdx.x];
+            const int32_t t = tok[ch];
+            double pt = 0.0, qt = 0.0;
+            if (t >= 0 && t < a.V) {
+                pt = prob_of(load_elem<DT>(prow, t), c, s.sp);
+                qt = prob_of(load_elem<DT>(qrow, t), c, s.sq);
+            }
+            s.pc[threadIdx.x] = pt;
+            s.qc[threadIdx.x] = qt;
+            s.u[threadIdx.x] = stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(ch));
+        }
+        __syncthreads();
+    }
+
+    // Final draw from the weights of the last pass (their fp32 walker totals
+    // in s.part, total W): the walker whose share holds v * W finds the tile
+    // and the token and publishes it. Returns whether a draw was made.
+    __device__ __forceinline__ bool draw(bool target, float coef, double W) {
+        if (!(W > 0.0)) return false;
+        const double want = double(v) * W;
+        int owner = -1;
+        double base = 0.0, acc = 0.0;
+        for (int k = 0; k < a.H; ++k) {  // same in every thread of every walker
+            const double P = double(s.part[k]);
+            if (P > 0.0) {
+                owner = k;
+                base = acc;
+                if (acc + P >= want) break;
+            }
+            acc += P;
+        }
+        if (h == owner) {
+            double tin = 0.0;
+            const int t = find_tile(s.tile, hi - lo, base, want, &tin);
+            int32_t bonus = -1;
+            if (t >= 0) {
+                if (target) {
+                    TargetWeights<DT> f;
+                    f.p.init(prow, c, s.sp);
+                    f.V = a.V;
+                    bonus = sample_in_tile(f, lo + t, tin);
+                } else {
+                    ResidualWeights<DT> f;
+                    f.p.init(prow, c, s.sp);
+                    f.q.init(qrow, c, s.sq);
+                    f.coef = coef;
+                    f.V = a.V;
+                    bonus = sample_in_tile(f, lo + t, tin);
+                }
+            }
+            if (threadIdx.x == 0) publish(w.bonus, (1ull << 32) | uint32_t(bonus));
+        }
+        return owner >= 0;
+    }
+};
+
+// Walker h of tree b.
 template <int DT>
-__device__ __forceinline__ void walk_tree(const TreeArgs& a, int b) {
+__device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     constexpr int esz = ElemT<DT>::kBytes;
+    __shared__ WalkLds s;
+    __shared__ int s_nacc, s_fail;
     const int N = a.N;
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
-    const float c = greedy ? 0.0f : log2e_over(T);
-    const int32_t* par = a.parent + int64_t(b) * N;
-    const int32_t* tok = a.tokens + int64_t(b) * N;
-    const float v = greedy ? 0.0f : stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(N));
+    const WalkWords w = walk_of(a, b);
     uint64_t* slots = a.slots + int64_t(b) * 2 * N * a.S;
-    const Walk w = walk_of(a, b);
 
-    __shared__ float tile_sum[kMaxTiles];
-    __shared__ RowStats s_tp, s_dp;
-    __shared__ int s_node, s_nacc, s_child, s_bonus, s_accept, s_fail;
-
-    uint32_t pass = 0;
-    // One shared pass: post it, do walker 0's share, collect every tile sum
-    // into LDS. Returns the total weight (fp64), or -1 if a wait ran out.
-    auto run_pass = [&](int node, uint32_t kind, float coef) -> double {
-        ++pass;
-        if (threadIdx.x == 0) {
-            publish(w.cmd + 1, (uint64_t(pass) << 32) | __float_as_uint(coef));
-            publish(w.cmd, (uint64_t(pass) << 32) | (kind << 16) | uint32_t(node));
-        }
-        share_pass<DT>(a, b, c, node, kind, coef, pass, 0, w);
-        if (!wait_tagged(w.tiles, a.ntiles, pass)) {
-            if (threadIdx.x == 0) s_fail = 1;
-            __syncthreads();
-            return -1.0;
-        }
-        for (int t = threadIdx.x; t < a.ntiles; t += kThreads) tile_sum[t] = __uint_as_float(uint32_t(peek(w.tiles + t)));
-        return tiles_total(tile_sum, a.ntiles);
-    };
-
-    if (threadIdx.x == 0) { s_node = 0; s_nacc = 0; s_bonus = -1; s_fail = 0; }
+    if (greedy && h != 0) {  // VerifyGreedy is one walker's argmax walk
+        if (threadIdx.x == 0) publish(w.ack + h, 1ull);
+        return;
+    }
+    if (threadIdx.x == 0) { s_nacc = 0; s_fail = 0; }
     __syncthreads();
 
-    while (true) {
-        const int node = s_node;
-        if (threadIdx.x == 0) {
-            s_tp = merge_slots(slots + int64_t(node) * a.S, a.S, greedy, c);
-            if (!greedy) s_dp = merge_slots(slots + int64_t(N + node) * a.S, a.S, false, c);
-        }
-        __syncthreads();
-
-        if (greedy) {  // VerifyGreedy
+    int32_t bonus = -1;
+    bool drew = false;
+    if (greedy) {  // VerifyGreedy
+        int node = 0;
+        const int32_t* par = a.parent + int64_t(b) * N;
+        const int32_t* tok = a.tokens + int64_t(b) * N;
+        while (true) {
+            if (threadIdx.x == 0) s.sp = merge_slots(slots + int64_t(node) * a.S, a.S, true, 0.0f);
+            __syncthreads();
+            const int32_t g = s.sp.idx;
             if (wave_id() == 0) {
-                const int32_t g = s_tp.idx;
-                const int ch = child_with_token(par, tok, N, node, g);
+                int ch = -1;
+                for (int base = node + 1; base < N && ch < 0; base += kWaveSize) {
+                    const int c2 = base + lane_id();
+                    const uint64_t m = __ballot(c2 < N && par[c2] == node && tok[c2] == g);
+                    if (m) ch = base + __builtin_ctzll(m);
+                }
                 if (lane_id() == 0) {
-                    if (ch >= 0) {
-                        a.out_path[int64_t(b) * N + s_nacc] = ch;
-                        s_nacc = s_nacc + 1;
-                        s_node = ch;
-                    } else {
-                        s_bonus = g;
-                    }
+                    if (ch >= 0) a.out_path[int64_t(b) * N + s_nacc] = ch;
+                    s.ok = ch;
+                    if (ch >= 0) s_nacc = s_nacc + 1;
                 }
             }
             __syncthreads();
-            if (s_bonus >= 0 || s_node == node) break;
-            continue;
+            if (s.ok < 0) { bonus = g; break; }
+            node = s.ok;
         }
-
-        const void* prow = row_ptr(a.target, esz, b, node);
-        const void* qrow = row_ptr(a.draft, esz, b, node);
-        if (wave_id() == 0) {
-            const int ch = next_child(par, N, node, -1);
-            if (lane_id() == 0) s_child = ch;
-        }
-        __syncthreads();
-
-        if (s_child < 0) {  // leaf: the bonus is drawn from p of the leaf
-            if (run_pass(node, kPassTarget, 0.0f) < 0.0) break;
-            TargetWeights<DT> f;
-            f.p.init(prow, c, s_tp);
-            f.V = a.V;
-            const int32_t bonus = sample_from_tiles(f, a.V, v, tile_sum);
-            if (threadIdx.x == 0) s_bonus = bonus;
+    } else {  // MSS
+        Walker<DT> wk{a, b, h, N, int(int64_t(a.ntiles) * h / a.H), int(int64_t(a.ntiles) * (h + 1) / a.H),
+                      log2e_over(T), stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(N)), w, s,
+                      nullptr, nullptr};
+        int node = 0;
+        bool failed = false;
+        while (!failed) {
+            wk.prow = row_ptr(a.target, esz, b, node);
+            wk.qrow = row_ptr(a.draft, esz, b, node);
+            if (threadIdx.x == 0) {
+                s.sp = merge_slots(slots + int64_t(node) * a.S, a.S, false, wk.c);
+                s.sq = merge_slots(slots + int64_t(N + node) * a.S, a.S, false, wk.c);
+                s.from = node + 1;
+                s.nk = 0;
+            }
             __syncthreads();
+            double cj = 0.0, Mj = 1.0;   // r = max(0, p - cj q) / Mj; identical everywhere
+            bool tiles_valid = false;    // the last pass's tiles hold the weights of the current r
+            bool any_child = false, accepted = false;
+            int k = 0;
+            while (true) {
+                if (k == s.nk) {
+                    if (s.from >= N) break;
+                    __syncthreads();   // every thread is done with the previous batch
+                    wk.next_batch(node);
+                    k = 0;
+                    continue;
+                }
+                any_child = true;
+                const double pt = s.pc[k], qt = s.qc[k];
+                const double rt = fmax(pt - cj * qt, 0.0) / Mj;
+                if (qt > 0.0 && double(s.u[k]) <= rt / qt) {
+                    const int ch = s.kid[k];
+                    if (threadIdx.x == 0) {
+                        if (h == 0) a.out_path[int64_t(b) * N + s_nacc] = ch;
+                        s_nacc = s_nacc + 1;
+                    }
+                    node = ch;
+                    accepted = true;
+                    break;
+                }
+                // Rejected: r <- norm(max(0, r - q)).
+                const double M = wk.run_pass(false, float(cj + Mj));
+                if (M < 0.0) { failed = true; break; }
+                if (M > 0.0) { cj = cj + Mj; Mj = M; tiles_valid = true; }
+                else tiles_valid = false;
+                ++k;
+            }
+            if (failed) break;
+            if (accepted) { __syncthreads(); continue; }
+
+            // Every child rejected (or a leaf): draw the bonus from the last
+            // residual, or from p when no residual of positive mass was formed.
+            const bool from_p = !any_child || cj == 0.0;
+            double W = Mj;
+            if (from_p) W = wk.run_pass(true, 0.0f);
+            else if (!tiles_valid) W = wk.run_pass(false, float(cj));
+            if (W < 0.0) { failed = true; break; }
+            drew = wk.draw(from_p, float(cj), W);
             break;
         }
-
-        double cj = 0.0, Mj = 1.0;   // r = max(0, p - cj q) / Mj; identical in every thread
-        bool tiles_valid = false;    // tile_sum holds the weights of the current r
-        bool accepted = false;
-        bool failed = false;
-        while (true) {
-            const int child = s_child;
-            if (threadIdx.x == 0) {
-                const int32_t t = tok[child];
-                bool acc = false;
-                if (t >= 0 && t < a.V) {
-                    const double pt = prob_of(load_elem<DT>(prow, t), c, s_tp);
-                    const double qt = prob_of(load_elem<DT>(qrow, t), c, s_dp);
-                    const double rt = fmax(pt - cj * qt, 0.0) / Mj;
-                    const float u = stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(child));
-                    acc = qt > 0.0 && double(u) <= rt / qt;
-                }
-                s_accept = acc;
-                if (acc) {
-                    a.out_path[int64_t(b) * N + s_nacc] = child;
-                    s_nacc = s_nacc + 1;
-                    s_node = child;
-                }
-            }
-            __syncthreads();
-            if (s_accept) { accepted = true; break; }
-
-            // Rejected: r <- norm(max(0, r - q)).
-            const double M = run_pass(node, kPassResidual, float(cj + Mj));
-            if (M < 0.0) { failed = true; break; }
-            if (M > 0.0) { cj = cj + Mj; Mj = M; tiles_valid = true; }
-            else tiles_valid = false;
-
-            if (wave_id() == 0) {
-                const int ch = next_child(par, N, node, child);
-                if (lane_id() == 0) s_child = ch;
-            }
-            __syncthreads();
-            if (s_child < 0) break;
-        }
-        if (failed) break;
-        if (accepted) continue;
-
-        // Every child rejected: draw the bonus from the last residual.
-        int32_t bonus = -1;
-        if (cj == 0.0) {  // no residual of positive mass was formed: r = p
-            if (run_pass(node, kPassTarget, 0.0f) >= 0.0) {
-                TargetWeights<DT> f;
-                f.p.init(prow, c, s_tp);
-                f.V = a.V;
-                bonus = sample_from_tiles(f, a.V, v, tile_sum);
-            }
-        } else {
-            ResidualWeights<DT> f;
-            f.p.init(prow, c, s_tp);
-            f.q.init(qrow, c, s_dp);
-            f.coef = float(cj);
-            f.V = a.V;
-            if (tiles_valid || run_pass(node, kPassResidual, float(cj)) >= 0.0)
-                bonus = sample_from_tiles(f, a.V, v, tile_sum);
-        }
-        if (threadIdx.x == 0) s_bonus = bonus;
-        __syncthreads();
-        break;
-    }
-
-    // Release the other walkers, wait until they are gone, then return every
-    // word this tree used to zero.
-    ++pass;
-    if (threadIdx.x == 0) {
-        publish(w.cmd + 1, uint64_t(pass) << 32);
-        publish(w.cmd, (uint64_t(pass) << 32) | (kPassDone << 16));
-    }
-    if (a.H > 1) {
-        __shared__ int s_acked;
-        if (wave_id() == 0) {
-            int ok = 0;
-            for (int spin = 0; spin < kMaxSpin; ++spin) {
-                const bool mine = lane_id() == 0 || lane_id() >= a.H || peek(w.ack + lane_id()) != 0ull;
-                if (__all(mine)) { ok = 1; break; }
-                __builtin_amdgcn_s_sleep(2);
-            }
-            if (lane_id() == 0) s_acked = ok;
-        }
-        __syncthreads();
-        if (!s_acked && threadIdx.x == 0) s_fail = 1;
+        if (failed && threadIdx.x == 0) s_fail = 1;
     }
     __syncthreads();
+
+    if (h != 0) {  // done with every word of the tree: acknowledge and leave
+        if (threadIdx.x == 0) publish(w.ack + h, 1ull);
+        return;
+    }
+    // Walker 0: wait for the other walkers (and the drawn token), write the
+    // outcome, return every word of the tree to zero.
+    __shared__ int s_done;
+    if (wave_id() == 0) {
+        int ok = 0;
+        for (int spin = 0; spin < kMaxSpin; ++spin) {
+            bool mine = lane_id() == 0 || lane_id() >= a.H || peek(w.ack + lane_id()) != 0ull;
+            if (lane_id() == 0 && drew) mine = peek(w.bonus) != 0ull;
+            if (__all(mine)) { ok = 1; break; }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane_id() == 0) s_done = ok;
+    }
+    __syncthreads();
+    if (drew && threadIdx.x == 0) bonus = s_done ? int32_t(uint32_t(peek(w.bonus))) : -1;
+    const bool fail = s_fail || !s_done;
     const int nacc = s_nacc;
     for (int j = nacc + threadIdx.x; j < N; j += kThreads) a.out_path[int64_t(b) * N + j] = -1;
     zero_slots(slots, int64_t(2) * N * a.S);
-    zero_slots(w.cmd, kWalkHeader + a.ntiles);
-    __syncthreads();
+    zero_slots(w.part, kWalkWords);
     if (threadIdx.x == 0) {
-        a.out_nacc[b] = s_fail ? -1 : nacc;
-        a.out_bonus[b] = s_fail ? -1 : s_bonus;
+        a.out_nacc[b] = fail ? -1 : nacc;
+        a.out_bonus[b] = fail ? -1 : bonus;
     }
 }
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeArgs a) {
-    const int b = int(blockIdx.x / a.H);
-    const int h = int(blockIdx.x % a.H);
-    if (h == 0) walk_tree<DT>(a, b);
-    else walk_helper<DT>(a, b, h);
+    tree_walk<DT>(a, int(blockIdx.x / a.H), int(blockIdx.x % a.H));
 }
 
 template <int DT>

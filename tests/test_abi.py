@@ -66,7 +66,8 @@ def test_workspace_sizes(lib):
     st, b = ws_size(lib, "specv_verify_workspace_size", 8, 4, 32000)
     assert st == 0 and b >= 8 * 9 * 8 and b % 256 == 0      # rows split into chunks
     st, t = ws_size(lib, "specv_tree_verify_workspace_size", 32, 64, 152064)
-    assert st == 0 and t == 32 * 128 * 8 + 32 * (18 + 297) * 8   # row words, then walk words per tree
+    # row words, then 49 walk words per tree (2 x 16 pass totals, 16 acknowledgements, the drawn token)
+    assert st == 0 and t == 32 * 128 * 8 + 32 * 49 * 8
     st, c = ws_size(lib, "specv_verify_workspace_size", 4, 2, 16000)   # 32 tiles: one bonus workgroup
     assert st == 0 and c % 256 == 0 and c < 4 * 5 * 64 * 8
     assert ws_size(lib, "specv_verify_workspace_size", 0, 8, 10)[0] == INVALID
