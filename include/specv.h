@@ -295,9 +295,9 @@ specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes,
  * [batch]. Workspace as for specv_verify (zero-filled before first use, left
  * zero-filled by every call).
  * Enqueues two kernels: the row statistics, then the walk, whose passes over
- * a node's rows are shared by up to 16 workgroups per tree (a cooperative
- * launch, so all of them are resident together; fewer per tree when the
- * batch is large).
+ * a node's rows are shared by up to 16 workgroups per tree that wait for each
+ * other (workgroups start in index order, so every tree gets all of its
+ * workgroups resident).
  */
 specv_status specv_tree_verify(specv_logits target, specv_logits draft,
                                const int32_t* parent, const int32_t* tokens,

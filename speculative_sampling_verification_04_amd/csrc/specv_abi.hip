@@ -38,6 +38,9 @@ int elem_size(int32_t dtype) { return dtype == SPECV_BF16 ? 2 : 4; }
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+static_assert(kMaxTreeNodes == SPECV_MAX_TREE_NODES, "the walk keeps a whole tree in LDS");
+static_assert(kMaxPositions == SPECV_MAX_GAMMA + 1, "per-position fan-out table");
+
 // Largest grid the launches accept (grid.x * 256 threads must fit 32 bits).
 constexpr int64_t kMaxGrid = (int64_t(1) << 32) / kThreads - 1;
 

@@ -69,6 +69,10 @@ struct ChainArgs {
 // `walk` (kWalkWords words per tree: the walkers' pass totals for two pass
 // parities, one acknowledgement per walker, the drawn token).
 constexpr int kMaxWalkers = 16;
+constexpr int kMaxTreeNodes = 4096;  // SPECV_MAX_TREE_NODES
+// Tiles of one walker's share: ceil(tiles / H) with H = tree_walkers(V) is at
+// most 32 while tiles <= 512, and at most kMaxTiles / kMaxWalkers beyond.
+constexpr int kMaxWalkTiles = kMaxTiles / kMaxWalkers;
 constexpr int kWalkWords = 3 * kMaxWalkers + 1;
 
 struct TreeArgs {

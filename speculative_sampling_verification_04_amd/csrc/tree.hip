@@ -9,9 +9,9 @@
 //    children (the distribution their children were drawn from); every
 //    workgroup publishes one 64-bit word.
 //
-// 2. tree_walk_kernel: H workgroups ("walkers") per tree, all resident at
-//    once (a cooperative launch when H > 1). Every walker of a tree runs the
-//    same walk on the same data and takes the same decisions; each full pass
+// 2. tree_walk_kernel: H workgroups ("walkers") per tree (launch_tree_dt
+//    says why they are all resident together). Every walker of a tree runs
+//    the same walk on the same data and takes the same decisions; each full pass
 //    over a node's rows that the walk needs is split between them: walker h
 //    sums the weights over its share of the 512-element tiles, keeps its tile
 //    sums in LDS and publishes its share's total as one word tagged with the
@@ -135,7 +135,11 @@ struct WalkLds {
     double pc[kThreads], qc[kThreads];  // p(t), q(t) of each child's token t
     float u[kThreads];            // each child's uniform
     float part[kMaxWalkers];      // the walkers' totals of the last pass
-    float tile[kMaxTiles];        // this walker's tile sums of the last pass
+    float tile[kMaxWalkTiles];    // this walker's tile sums of the last pass
+    int32_t par[kMaxTreeNodes];   // the tree's parents and tokens
+    int32_t tok[kMaxTreeNodes];
+    int32_t first[kMaxTreeNodes]; // each node's lowest-id child (N if none)
+    uint32_t acc1[kMaxTreeNodes / 32];  // bit n: the walk accepts that child (MSS)
     int nk, from;                 // batch size; next position of the child scan
     int ok;
 };
@@ -181,16 +185,16 @@ struct Walker {
         return total;
     }
 
-    // The next batch of the node's children (ascending ids from s.from) and
-    // their accept-test inputs. Whole workgroup.
-    __device__ __forceinline__ void next_batch(int node) {
-        const int32_t* par = a.parent + int64_t(b) * N;
-        const int32_t* tok = a.tokens + int64_t(b) * N;
+    // The next batch of the node's children (ascending ids; the first batch
+    // of a node starts after the node and also brings the node's statistics)
+    // and their accept-test inputs. The statistics words and the children's
+    // logits are read in one round trip. Whole workgroup.
+    __device__ __forceinline__ void next_batch(int node, bool first) {
         if (wave_id() == 0) {
-            int n = 0, base = s.from;
+            int n = 0, base = first ? node + 1 : s.from;
             for (; base < N && n <= kThreads - kWaveSize; base += kWaveSize) {
                 const int ch = base + lane_id();
-                const bool is = ch < N && par[ch] == node;
+                const bool is = ch < N && s.par[ch] == node;
                 const uint64_t m = __ballot(is);
                 if (is) s.kid[n + lanes_below(m)] = ch;
                 n += __popcll(m);
@@ -198,16 +202,21 @@ struct Walker {
             if (lane_id() == 0) { s.nk = n; s.from = base; }
         }
         __syncthreads();
-        if (threadIdx.x < s.nk) {
-            const int ch = s.kid[threadIdx.x];
-            const int32_t t = tok[ch];
-            double pt = 0.0, qt = 0.0;
-            if (t >= 0 && t < a.V) {
-                pt = prob_of(load_elem<DT>(prow, t), c, s.sp);
-                qt = prob_of(load_elem<DT>(qrow, t), c, s.sq);
-            }
-            s.pc[threadIdx.x] = pt;
-            s.qc[threadIdx.x] = qt;
+        const uint64_t* slots = a.slots + int64_t(b) * 2 * N * a.S;
+        if (first && threadIdx.x == 0) {
+            s.sp = merge_slots(slots + int64_t(node) * a.S, a.S, false, c);
+            s.sq = merge_slots(slots + int64_t(N + node) * a.S, a.S, false, c);
+        }
+        const bool mine = threadIdx.x < s.nk;
+        const int ch = mine ? s.kid[threadIdx.x] : 0;
+        const int32_t t = mine ? s.tok[ch] : -1;
+        const bool in_range = t >= 0 && t < a.V;
+        const float zp = in_range ? load_elem<DT>(prow, t) : -INFINITY;
+        const float zq = in_range ? load_elem<DT>(qrow, t) : -INFINITY;
+        __syncthreads();
+        if (mine) {
+            s.pc[threadIdx.x] = in_range ? prob_of(zp, c, s.sp) : 0.0;
+            s.qc[threadIdx.x] = in_range ? prob_of(zq, c, s.sq) : 0.0;
             s.u[threadIdx.x] = stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(ch));
         }
         __syncthreads();
@@ -272,14 +281,23 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
         return;
     }
     if (threadIdx.x == 0) { s_nacc = 0; s_fail = 0; }
+    for (int i = threadIdx.x; i < N; i += kThreads) {
+        s.par[i] = a.parent[int64_t(b) * N + i];
+        s.tok[i] = a.tokens[int64_t(b) * N + i];
+        s.first[i] = N;
+    }
+    for (int i = threadIdx.x; i < (N + 31) / 32; i += kThreads) s.acc1[i] = 0u;
+    __syncthreads();
+    for (int ch = 1 + threadIdx.x; ch < N; ch += kThreads) {
+        const int p = s.par[ch];
+        if (p >= 0 && p < N) atomicMin(&s.first[p], ch);
+    }
     __syncthreads();
 
     int32_t bonus = -1;
     bool drew = false;
     if (greedy) {  // VerifyGreedy
         int node = 0;
-        const int32_t* par = a.parent + int64_t(b) * N;
-        const int32_t* tok = a.tokens + int64_t(b) * N;
         while (true) {
             if (threadIdx.x == 0) s.sp = merge_slots(slots + int64_t(node) * a.S, a.S, true, 0.0f);
             __syncthreads();
@@ -288,7 +306,7 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
                 int ch = -1;
                 for (int base = node + 1; base < N && ch < 0; base += kWaveSize) {
                     const int c2 = base + lane_id();
-                    const uint64_t m = __ballot(c2 < N && par[c2] == node && tok[c2] == g);
+                    const uint64_t m = __ballot(c2 < N && s.par[c2] == node && s.tok[c2] == g);
                     if (m) ch = base + __builtin_ctzll(m);
                 }
                 if (lane_id() == 0) {
@@ -305,18 +323,36 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
         Walker<DT> wk{a, b, h, N, int(int64_t(a.ntiles) * h / a.H), int(int64_t(a.ntiles) * (h + 1) / a.H),
                       log2e_over(T), stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(N)), w, s,
                       nullptr, nullptr};
+        // The first child's test at every node uses r = p, whatever the walk
+        // did before: for trees of up to one node per thread, decide them all
+        // at once, in parallel, so that the walk runs down a chain of first
+        // children accepted without waiting (larger trees test every child
+        // when the walk reaches its node).
+        for (int n = threadIdx.x; N <= kThreads && n < N; n += kThreads) {
+            const int ch = s.first[n];
+            if (ch >= N) continue;
+            const int32_t t = s.tok[ch];
+            if (t < 0 || t >= a.V) continue;
+            const RowStats sp = merge_slots(slots + int64_t(n) * a.S, a.S, false, wk.c);
+            const RowStats sq = merge_slots(slots + int64_t(N + n) * a.S, a.S, false, wk.c);
+            const double pt = prob_of(load_elem<DT>(row_ptr(a.target, esz, b, n), t), wk.c, sp);
+            const double qt = prob_of(load_elem<DT>(row_ptr(a.draft, esz, b, n), t), wk.c, sq);
+            const float u = stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(ch));
+            if (qt > 0.0 && double(u) <= pt / qt) atomicOr(&s.acc1[n >> 5], 1u << (n & 31));
+        }
+        __syncthreads();
         int node = 0;
         bool failed = false;
         while (!failed) {
+            while (s.first[node] < N && ((s.acc1[node >> 5] >> (node & 31)) & 1u)) {
+                const int ch = s.first[node];
+                if (h == 0 && threadIdx.x == 0) a.out_path[int64_t(b) * N + s_nacc] = ch;
+                if (threadIdx.x == 0) s_nacc = s_nacc + 1;
+                node = ch;
+            }
             wk.prow = row_ptr(a.target, esz, b, node);
             wk.qrow = row_ptr(a.draft, esz, b, node);
-            if (threadIdx.x == 0) {
-                s.sp = merge_slots(slots + int64_t(node) * a.S, a.S, false, wk.c);
-                s.sq = merge_slots(slots + int64_t(N + node) * a.S, a.S, false, wk.c);
-                s.from = node + 1;
-                s.nk = 0;
-            }
-            __syncthreads();
+            wk.next_batch(node, true);
             double cj = 0.0, Mj = 1.0;   // r = max(0, p - cj q) / Mj; identical everywhere
             bool tiles_valid = false;    // the last pass's tiles hold the weights of the current r
             bool any_child = false, accepted = false;
@@ -325,7 +361,7 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
                 if (k == s.nk) {
                     if (s.from >= N) break;
                     __syncthreads();   // every thread is done with the previous batch
-                    wk.next_batch(node);
+                    wk.next_batch(node, false);
                     k = 0;
                     continue;
                 }
@@ -402,34 +438,19 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeArgs a) {
 }
 
 template <int DT>
-hipError_t launch_tree_dt(TreeArgs a, hipStream_t stream) {
+hipError_t launch_tree_dt(const TreeArgs& a, hipStream_t stream) {
     const int64_t grid = int64_t(a.B) * 2 * a.N * a.S;
     hipLaunchKernelGGL(tree_stats_kernel<DT>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-
-    // Every walker of every tree must be resident at once (walkers wait on
-    // each other), so H is capped by what the device holds.
-    int dev = 0, cus = 0, per_cu = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(tree_walk_kernel<DT>),
-                                                          kThreads, 0)) != hipSuccess)
-        return e;
-    const int64_t resident = int64_t(cus) * per_cu;
-    int64_t H = a.H;
-    if (int64_t(a.B) * H > resident) H = resident / a.B > 1 ? resident / a.B : 1;
-    a.H = int32_t(H);
-    const dim3 walk_grid(unsigned(int64_t(a.B) * a.H));
-    if (a.H > 1) {
-        void* args[] = {&a};
-        e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(tree_walk_kernel<DT>), walk_grid, dim3(kThreads),
-                                       args, 0, stream);
-    } else {
-        hipLaunchKernelGGL(tree_walk_kernel<DT>, walk_grid, dim3(kThreads), 0, stream, a);
-        e = hipGetLastError();
-    }
-    return e;
+    // An ordinary launch: the walkers of a tree wait only for each other, and
+    // workgroups start in index order, so the lowest tree with a walker not
+    // yet started has all the walkers of every lower tree started; those
+    // finish and free their slots, and the next walkers in line are its own.
+    // Every tree therefore gets all of its H <= 16 walkers resident, without
+    // the cost of a cooperative launch (~10-20 us here).
+    hipLaunchKernelGGL(tree_walk_kernel<DT>, dim3(unsigned(int64_t(a.B) * a.H)), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace
