@@ -417,22 +417,27 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
     return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-    for (int o = 1; o < kWaveSize; o <<= 1) {
-        const uint64_t y = __shfl_xor(x, o);
-        x = y > x ? y : x;
-    }
-    return x;
+// Wave maximum of unsigned 64-bit values through the same DPP steps as
+// wave_sum (disabled rows of a broadcast see 0, which never wins).
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = dpp_u32<kCtrl, kRowMask>(uint32_t(v));
+    const uint32_t hi = dpp_u32<kCtrl, kRowMask>(uint32_t(v >> 32));
+    return (uint64_t(hi) << 32) | lo;
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-    for (int o = 1; o < kWaveSize; o <<= 1) {
-        const uint32_t y = __shfl_xor(x, o);
-        x = y > x ? y : x;
-    }
-    return x;
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+    x = umax64(x, dpp_u64<kDppQuadXor1>(x));
+    x = umax64(x, dpp_u64<kDppQuadXor2>(x));
+    x = umax64(x, dpp_u64<kDppRowHalfMirror>(x));
+    x = umax64(x, dpp_u64<kDppRowMirror>(x));
+    x = umax64(x, dpp_u64<kDppRowBcast15, 0xa>(x));
+    x = umax64(x, dpp_u64<kDppRowBcast31, 0xc>(x));
+    const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(x)), kWaveSize - 1));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(x >> 32)), kWaveSize - 1));
+    return (uint64_t(hi) << 32) | lo;
 }
 
 // ------------------------------------------------------------ accumulators

@@ -24,7 +24,6 @@ namespace specv {
 constexpr int kCandCap = 256;                  // candidate groups per wave
 constexpr int32_t kSingle = 0x40000000;       // candidate holds one element, not 8
 
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 __device__ __forceinline__ uint64_t group_key(float vm, int64_t start) {
     return (uint64_t(logit_key(vm)) << 32) | uint64_t(~uint32_t(start));
