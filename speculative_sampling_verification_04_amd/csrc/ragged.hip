@@ -62,7 +62,8 @@ __global__ __launch_bounds__(kThreads) void ragged_verify_kernel(ChainArgs a) {
         q.out_tokens = a.out_tokens + int64_t(b) * (G + 1);
         q.out_len = G + 1;
         q.out_probs = a.out_probs ? a.out_probs + int64_t(o0) * 2 : nullptr;
-        chain_resolve<DT, NoDraft>(a, q, T, slots, RS, a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, h);
+        __shared__ ResolveLds lds;
+        chain_resolve<DT, NoDraft>(a, q, T, slots, RS, a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, h, lds);
         return;
     }
 

@@ -69,6 +69,13 @@ __device__ __forceinline__ SeqView dense_seq(const ChainArgs& a, int b) {
     return q;
 }
 
+// LDS of one bonus workgroup. A kernel whose row workgroups need LDS of their
+// own may overlay the two (a workgroup is one or the other).
+struct ResolveLds {
+    RowStats st[2 * 64 + 1];
+    float tile_sum[kMaxTiles];
+};
+
 // Bonus workgroup h of a sequence. slots: the sequence's nslots words (row r
 // chunk j at r * S + j: target row r for r <= G, draft row r - G - 1 after
 // that; then, with a.cache_words, three cache words per draft row from word
@@ -77,7 +84,7 @@ __device__ __forceinline__ SeqView dense_seq(const ChainArgs& a, int b) {
 // cache words exist (a.cache_words; specv_verify_cache only).
 template <int DT, bool NoDraft = false, bool Cache = false>
 __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView& q, float T, uint64_t* slots,
-                                              int64_t nslots, uint64_t* tiles, int h) {
+                                              int64_t nslots, uint64_t* tiles, int h, ResolveLds& lds) {
     const int b = q.b;
     const int gamma = q.gamma;
     const int G = q.G;
@@ -89,12 +96,12 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
 
     if (greedy && !last) return;  // the greedy bonus is an argmax: nothing to share
 
-    __shared__ RowStats st[2 * 64 + 1];
+    RowStats* st = lds.st;
+    float* tile_sum = lds.tile_sum;
     __shared__ int32_t s_k;
     __shared__ int32_t s_bonus;
     __shared__ float s_mass;
     __shared__ uint64_t s_cache_word;
-    __shared__ float tile_sum[kMaxTiles];
 
     if (!wait_slots(slots, nslots)) {  // never expected: see wait_slots
         if (last) {

@@ -110,16 +110,20 @@ struct TopKAcc {
     }
 };
 
-// Ends a row's selection (whole workgroup, after streaming): every wave
+// Ends a row's selection (whole workgroup, after streaming; keys: LDS of
+// topf_keys<K>() words): every wave
 // compacts its candidates to at most K groups, the keys that reach the largest
 // wave threshold are gathered, wave 0 pops the F + 1 largest, and thread 0
 // writes the first F ids (and logits) that are not `excl`, then -1 up to
 // Fmax entries. Returns the F + 1 largest keys of the row in LDS (0 = none),
 // before the exclusion; they stay valid until the caller's next barrier.
+template <int K>
+constexpr int topf_keys() { return kWaves * kLaneElems * K; }   // LDS words topf_finish needs
+
 template <int DT, int K>
 __device__ __forceinline__ const uint64_t* topf_finish(TopKAcc<DT, K>& acc, const void* rp, int64_t V, int F,
-                                                       int Fmax, int32_t excl, int32_t* out_ids, float* out_logits) {
-    __shared__ uint64_t keys[kWaves * kLaneElems * K];
+                                                       int Fmax, int32_t excl, int32_t* out_ids, float* out_logits,
+                                                       uint64_t* keys) {
     __shared__ uint64_t s_theta[kWaves];
     __shared__ uint64_t s_pick[K];
     __shared__ int s_nkeys;

@@ -35,7 +35,8 @@ __global__ __launch_bounds__(kThreads) void topf_kernel(TopFArgs a) {
     stream_chunk<DT, kU, kD>(rp, 0, a.V, acc);
     const int32_t excl = (a.tokens != nullptr && k < a.gamma) ? a.tokens[int64_t(b) * a.gamma + k] : -1;
     const int64_t out = (int64_t(b) * rows + k) * a.F;
-    topf_finish<DT, K>(acc, rp, a.V, a.F, a.F, excl, a.out_topk + out, a.out_logits ? a.out_logits + out : nullptr);
+    __shared__ uint64_t keys[topf_keys<K>()];
+    topf_finish<DT, K>(acc, rp, a.V, a.F, a.F, excl, a.out_topk + out, a.out_logits ? a.out_logits + out : nullptr, keys);
 }
 
 template <int DT>

@@ -35,8 +35,9 @@ __global__ __launch_bounds__(kThreads) void chain_verify_kernel(ChainArgs a) {
     const bool greedy = !(T > 0.0f);
     uint64_t* slots = a.slots + int64_t(sidx) * RS;
     if (w >= RS) {  // bonus workgroup: dispatched after every row of the sequence
+        __shared__ ResolveLds lds;
         chain_resolve<DT>(a, dense_seq<DT>(a, b), T, slots, RS, a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr,
-                          int(w - RS));
+                          int(w - RS), lds);
         return;
     }
     const int chunk = int(w % a.S);

@@ -40,8 +40,21 @@ struct SoftmaxTopK {
     }
 };
 
+// LDS of a workgroup: a bonus workgroup's, or a draft row's top-K lists and
+// final pick (a workgroup is one or the other).
+template <int K>
+union FusedLds {
+    ResolveLds resolve;
+    struct {
+        int32_t cand[kWaves][kCandCap];
+        uint64_t cand_key[kWaves][kCandCap];
+        uint64_t keys[topf_keys<K>()];
+    } rows;
+};
+
 template <int DT, int K, bool Cache>
 __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
+    __shared__ FusedLds<K> lds;
     constexpr int esz = ElemT<DT>::kBytes;
     const int R1 = 2 * a.gamma + 2;
     __shared__ uint64_t masks[kMaxOrderedBatch / kWaveSize];
@@ -57,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     uint64_t* slots = a.slots + int64_t(sidx) * words;
     if (slot >= R1) {  // bonus workgroup: dispatched after every row of the sequence
         chain_resolve<DT, false, Cache>(a, dense_seq<DT>(a, b), T, slots, words,
-                          a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, slot - R1);
+                                        a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, slot - R1, lds.resolve);
         return;
     }
     const bool draft_row = slot > a.gamma;
@@ -79,8 +92,8 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
             word = pack_softmax(acc.m, acc.s);
         }
     } else {
-        __shared__ int32_t cand[kWaves][kCandCap];
-        __shared__ uint64_t cand_key[kWaves][kCandCap];
+        auto& cand = lds.rows.cand;
+        auto& cand_key = lds.rows.cand_key;
         const void* rp = row_ptr(a.draft, esz, b, row);
         const int32_t excl = row < a.gamma ? a.tokens[int64_t(b) * a.gamma + row] : -1;
         const int Fk = a.Fk[row];
@@ -94,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
             stream_chunk<DT, kDraftU, kDraftD>(rp, 0, V, acc);
             block_merge_softmax(acc.sm.m, acc.sm.mc, acc.sm.s);
             word = pack_softmax(acc.sm.m, acc.sm.s);
-            pick = topf_finish<DT, K>(acc.tk, rp, V, Fk, a.F, excl, ids, vals);
+            pick = topf_finish<DT, K>(acc.tk, rp, V, Fk, a.F, excl, ids, vals, lds.rows.keys);
             if (Cache && a.C < 1.0f && Fk > 0 && threadIdx.x == 0) {
                 // sigma_{F,C}: the normaliser loses (1 - C) of the top-F terms,
                 // taken relative to the same reference m*c as the row sum.
@@ -110,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
             TopKAcc<DT, K> acc;
             acc.init(cand[wave_id()], cand_key[wave_id()]);
             stream_chunk<DT, kDraftU, kDraftD>(rp, 0, V, acc);
-            pick = topf_finish<DT, K>(acc, rp, V, Fk, a.F, excl, ids, vals);
+            pick = topf_finish<DT, K>(acc, rp, V, Fk, a.F, excl, ids, vals, lds.rows.keys);
         }
         if (Cache && threadIdx.x == 0) {
             uint64_t* extra = slots + R1 + 3 * row;
