@@ -180,7 +180,9 @@ def main():
         events[i][1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    step_kernel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    step_times = np.array([e[0].elapsed_time(e[1]) for e in events])
+    step_kernel_ms = float(step_times.mean())
+    step_pct = {f"p{q}_ms": float(np.percentile(step_times, q)) for q in (10, 50, 90)}
     mean_accepted = float(out["num_accepted"].float().mean().item())
 
     # Reference: the two entry points run separately (not part of the step).
@@ -293,7 +295,7 @@ def main():
         "hbm_pct_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "kernel": "verify_topf_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic, "algorithmic_bytes": step_bytes, "avg_ms": step_kernel_ms},
+                     "traffic": traffic, "algorithmic_bytes": step_bytes, "avg_ms": step_kernel_ms, **step_pct},
         "separate_kernels": {
             "chain_verify_kernel": {"avg_ms": verify_ms, "algorithmic_bytes": verify_bytes,
                                     "gbps": verify_bytes / (verify_ms * 1e-3) / 1e9},
