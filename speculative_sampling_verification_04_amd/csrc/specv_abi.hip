@@ -110,8 +110,9 @@ void set_plain(ChainArgs& a, int32_t F) {
     a.out_hit = nullptr;
 }
 
-void set_bonus(ChainArgs& a, const Layout& L, int64_t row_words, void* workspace) {
+void set_bonus(ChainArgs& a, const Layout& L, int64_t row_words, void* workspace, int esz) {
     a.D = bonus_delay(a.B, row_words);
+    a.cache_rows = cached_positions(a.D, int64_t(a.V) * esz, int64_t(a.gamma) + 1);
     a.S = L.S;
     a.chunk = L.chunk;
     a.H = L.H;
@@ -249,7 +250,7 @@ specv_status specv_verify(specv_logits target, specv_logits draft, const int32_t
     a.B = batch;
     a.gamma = gamma;
     a.V = vocab;
-    set_bonus(a, L, (2 * int64_t(gamma) + 1) * L.S, workspace);
+    set_bonus(a, L, (2 * int64_t(gamma) + 1) * L.S, workspace, elem_size(target.dtype));
     set_plain(a, 0);
     a.seed = seed;
     a.offset = offset;
@@ -296,7 +297,7 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
     a.B = batch;
     a.gamma = gamma;
     a.V = vocab;
-    set_bonus(a, L, fused ? 2 * int64_t(gamma) + 2 : (2 * int64_t(gamma) + 1) * L.S, workspace);
+    set_bonus(a, L, fused ? 2 * int64_t(gamma) + 2 : (2 * int64_t(gamma) + 1) * L.S, workspace, elem_size(target.dtype));
     a.seed = seed;
     a.offset = offset;
     a.out_tokens = out_tokens;
@@ -378,7 +379,7 @@ specv_status specv_verify_cache(specv_logits target, specv_logits draft, const i
     a.B = batch;
     a.gamma = gamma;
     a.V = vocab;
-    set_bonus(a, L, 2 * int64_t(gamma) + 2, workspace);
+    set_bonus(a, L, 2 * int64_t(gamma) + 2, workspace, elem_size(target.dtype));
     a.seed = seed;
     a.offset = offset;
     a.out_tokens = out_tokens;
@@ -439,7 +440,7 @@ specv_status specv_verify_ragged(specv_logits target, specv_logits draft, const 
     a.B = batch;
     a.gamma = max_gamma;
     a.V = vocab;
-    set_bonus(a, L, ragged_rows(max_gamma, has_draft) * L.S, workspace);
+    set_bonus(a, L, ragged_rows(max_gamma, has_draft) * L.S, workspace, elem_size(target.dtype));
     set_plain(a, 0);
     a.seed = seed;
     a.offset = offset;

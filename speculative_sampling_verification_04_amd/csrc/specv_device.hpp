@@ -55,17 +55,17 @@ __device__ __forceinline__ float load_elem(const void* row, int64_t j) {
 // two for fp32.
 template <int DT> struct Raw8 { uint4 w[ElemT<DT>::kBytes / 2]; };
 
-// Logit rows are read exactly once by the streaming pass, so the loads carry
-// the nontemporal hint: on gfx950 this streams at ~6.9 TB/s against ~6.0 TB/s
-// for ordinary loads of the same rows.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
+// Group loads outside the streaming loop (a bonus draw's pass over one or two
+// rows, a tile re-read): ordinary loads, which hit when the row is still in
+// the device's caches (see kPolicyCached).
 template <int DT>
 __device__ __forceinline__ void load_raw8(Raw8<DT>& r, const char* p) {
     const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
 #pragma unroll
     for (int i = 0; i < ElemT<DT>::kBytes / 2; ++i) {
-        const u32x4_t x = __builtin_nontemporal_load(q + i);
+        const u32x4_t x = q[i];
         r.w[i] = make_uint4(x.x, x.y, x.z, x.w);
     }
 }
@@ -77,17 +77,24 @@ __device__ __forceinline__ void load_raw8(Raw8<DT>& r, const char* p) {
 // unit moves the base. Only the per-lane offset is range checked (the scalar
 // offset operand is not), hence the base, not that operand, advances.
 constexpr int32_t kRsrcWord3 = 0x00020000;   // gfx9 raw buffer: 32-bit data format
-constexpr int kNontemporal = 2;              // cache-policy operand: nt
+
+// Cache policy of the streaming loads. Most logit rows are read exactly once,
+// so they carry the nontemporal hint: on gfx950 that streams at ~6.9 TB/s
+// against ~6.0 TB/s for ordinary loads. The rows a bonus draw will probably
+// read again (low positions of T > 0 sequences) are streamed with ordinary
+// loads instead, so that the second read finds them in the caches.
+constexpr int kPolicyStream = 2;             // cache-policy operand: nt
+constexpr int kPolicyCached = 0;             // ordinary load
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t step_rsrc(const char* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, int32_t(bytes), kRsrcWord3);
 }
 
-template <int DT>
+template <int DT, int kPolicy>
 __device__ __forceinline__ void buffer_raw8(Raw8<DT>& r, __amdgpu_buffer_rsrc_t rs, uint32_t voff) {
 #pragma unroll
     for (int i = 0; i < ElemT<DT>::kBytes / 2; ++i) {
-        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, int32_t(voff + 16u * i), 0, kNontemporal);
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, int32_t(voff + 16u * i), 0, kPolicy);
         r.w[i] = make_uint4(x.x, x.y, x.z, x.w);
     }
 }
@@ -185,7 +192,7 @@ __device__ __forceinline__ void visit_steps(const Raw8<DT> (&r)[U], int64_t lo, 
     acc.template block<U>(v, idx, valid);
 }
 
-template <int DT, int U, int D, class Acc>
+template <int DT, int U, int D, int kPolicy = kPolicyStream, class Acc>
 __device__ __forceinline__ void stream_chunk(const void* row, int64_t lo, int64_t hi, Acc& acc) {
     static_assert(U >= 1 && D >= 0, "U >= 1 steps per iteration; D = 0 (prefetch) or a ring of D >= 1");
     constexpr int kB = ElemT<DT>::kBytes;
@@ -210,7 +217,7 @@ __device__ __forceinline__ void stream_chunk(const void* row, int64_t lo, int64_
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int32_t start = int32_t(it * kStride + int64_t(u) * kThreads) * int32_t(kStepBytes);
-            buffer_raw8<DT>(r[u], step_rsrc(base + start, uint32_t(max(total - start, 0))), voff);
+            buffer_raw8<DT, kPolicy>(r[u], step_rsrc(base + start, uint32_t(max(total - start, 0))), voff);
         }
     };
 
@@ -255,6 +262,14 @@ __device__ __forceinline__ void stream_chunk(const void* row, int64_t lo, int64_
         const bool ok = j < n;
         acc.one(ok ? load_elem<DT>(row, lo + j) : -INFINITY, lo + j, ok);
     }
+}
+
+// stream_chunk with the cache policy chosen at run time (cached: ordinary
+// loads, for rows that will probably be read again).
+template <int DT, int U, int D, class Acc>
+__device__ __forceinline__ void stream_chunk_as(bool cached, const void* row, int64_t lo, int64_t hi, Acc& acc) {
+    if (cached) stream_chunk<DT, U, D, kPolicyCached>(row, lo, hi, acc);
+    else stream_chunk<DT, U, D, kPolicyStream>(row, lo, hi, acc);
 }
 
 // ------------------------------------------------------------------ Philox

@@ -42,6 +42,7 @@ struct ChainArgs {
     int32_t H, ntiles;
     uint64_t* tiles;
     int32_t D;               // bonus workgroups trail their rows by D sequences (see decode_chain)
+    int32_t cache_rows;      // rows 0 .. cache_rows-1 of T > 0 sequences: cacheable loads (cached_positions)
     // Fused top-F (verify_topf_kernel only): F_k candidates at position k
     // (Fk[k] <= F), written with row stride F.
     int32_t F;
@@ -120,6 +121,19 @@ inline int32_t bonus_helpers(int64_t V) {
     const int64_t ntiles = (V + kTileElems - 1) / kTileElems;
     const int64_t h = (ntiles + 31) / 32;
     return int32_t(h < 1 ? 1 : h > 16 ? 16 : h);
+}
+
+// Positions whose rows a T > 0 sequence streams with ordinary (cacheable)
+// loads: its bonus draw re-reads the rows of the first rejected position k,
+// about D sequences (the bonus delay) after its rows were read, and low
+// positions are the likely k's. The rows at those positions of D sequences
+// must fit a share (kCacheBudget) of the device's last-level cache (256 MB of
+// Infinity Cache on MI355X) for the re-read to hit there instead of HBM.
+constexpr int64_t kCacheBudget = int64_t(160) << 20;
+inline int32_t cached_positions(int64_t D, int64_t row_bytes, int64_t positions) {
+    const int64_t per = 2 * D * row_bytes;   // one position's target and draft row over D sequences
+    const int64_t p = per > 0 ? kCacheBudget / per : 0;
+    return int32_t(p < positions ? p : positions);
 }
 
 // Walkers per tree for a vocabulary of V: about 32 tiles each, at most

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
             word = pack_argmax(acc.best, acc.idx);
         } else {
             SoftmaxAcc acc(log2e_over(T));
-            stream_chunk<DT, kTargetU, kTargetD>(rp, 0, V, acc);
+            stream_chunk_as<DT, kTargetU, kTargetD>(row < a.cache_rows, rp, 0, V, acc);
             block_merge_softmax(acc.m, acc.mc, acc.s);
             word = pack_softmax(acc.m, acc.s);
         }
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
         if (!greedy && row < a.gamma) {
             SoftmaxTopK<DT, K> acc(log2e_over(T));
             acc.tk.init(cand[wave_id()], cand_key[wave_id()]);
-            stream_chunk<DT, kDraftU, kDraftD>(rp, 0, V, acc);
+            stream_chunk_as<DT, kDraftU, kDraftD>(row < a.cache_rows, rp, 0, V, acc);
             block_merge_softmax(acc.sm.m, acc.sm.mc, acc.sm.s);
             word = pack_softmax(acc.sm.m, acc.sm.s);
             pick = topf_finish<DT, K>(acc.tk, rp, V, Fk, a.F, excl, ids, vals, lds.rows.keys);
