@@ -552,6 +552,7 @@ specv_status specv_tree_verify(specv_logits target, specv_logits draft, const in
     a.slots = static_cast<uint64_t*>(workspace);
     a.H = tree_walkers(vocab);
     a.ntiles = int32_t((int64_t(vocab) + kTileElems - 1) / kTileElems);
+    a.cache_nodes = cached_positions(batch, int64_t(vocab) * elem_size(target.dtype), nodes);
     a.walk = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + tree_walk_offset(batch, nodes, vocab));
     const hipError_t e = launch_tree(a, target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32,
                                      static_cast<hipStream_t>(stream));

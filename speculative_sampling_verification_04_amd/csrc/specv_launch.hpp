@@ -90,6 +90,10 @@ struct TreeArgs {
     uint64_t* slots;
     int32_t H, ntiles;
     uint64_t* walk;
+    // Nodes 0 .. cache_nodes-1 of T > 0 trees are streamed with ordinary
+    // (cacheable) loads: the walk's passes re-read the rows of the nodes it
+    // visits, shallow ones first (cached_positions with D = the batch).
+    int32_t cache_nodes;
 };
 
 struct TopFArgs {

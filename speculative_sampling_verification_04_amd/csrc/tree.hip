@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void tree_stats_kernel(TreeArgs a) {
             word = pack_argmax(acc.best, acc.idx);
         } else {
             SoftmaxAcc acc(log2e_over(T));
-            stream_chunk<DT, kU, kD>(rp, lo, hi, acc);
+            stream_chunk_as<DT, kU, kD>(node < a.cache_nodes, rp, lo, hi, acc);
             block_merge_softmax(acc.m, acc.mc, acc.s);
             word = pack_softmax(acc.m, acc.s);
         }
