@@ -29,10 +29,12 @@ __global__ __launch_bounds__(kThreads) void ragged_verify_kernel(ChainArgs a) {
     const int G = a.gamma;
     const int R = NoDraft ? G + 1 : 2 * G + 1;
     const int64_t RS = int64_t(R) * a.S;
-    int sidx;
-    int64_t w;
-    decode_chain(blockIdx.x, a.B, RS, a.H, a.D, sidx, w);
-    const int b = sequence_for_slot(a.temperature, a.B, sidx);
+    const Placement pl = place(a.temperature, a.B, [&](int, int& s, int64_t& w) {
+        decode_chain(blockIdx.x, a.B, RS, a.H, a.D, s, w);
+    });
+    const int sidx = pl.sidx;   // dispatch slot of the sequence
+    const int64_t w = pl.w;
+    const int b = pl.b;
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
     const int32_t o0 = a.offsets[b], o1 = a.offsets[b + 1];

@@ -49,65 +49,64 @@ __device__ __forceinline__ void block_merge_argmax(float& v, int32_t& i) {
 
 constexpr int kMaxOrderedBatch = 4096;
 
-// Dispatch order of sequences: those with T > 0 first, then the greedy ones,
-// each group by increasing index (identity when B > kMaxOrderedBatch). Only
-// T > 0 sequences re-read a row to draw the bonus, so their bonus workgroups
-// start early and overlap the greedy sequences' rows.
-//
-// sampled_sequences: ballot masks of the T > 0 sequences into `masks` (LDS,
-// kMaxOrderedBatch / kWaveSize words) and their number, or -1 when B >
-// kMaxOrderedBatch (no reordering). Whole workgroup.
-__device__ int sampled_sequences(const float* temperature, int B, uint64_t* masks) {
-    if (B > kMaxOrderedBatch) return -1;
-    __shared__ int s_total;
-    const int nm = (B + kWaveSize - 1) / kWaveSize;
-    for (int c = wave_id(); c < nm; c += kWaves) {
-        const int i = c * kWaveSize + lane_id();
-        const uint64_t m = __ballot(i < B && temperature[i] > 0.0f);
-        if (lane_id() == 0) masks[c] = m;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int total = 0;
-        for (int c = 0; c < nm; ++c) total += __popcll(masks[c]);
-        s_total = total;
-    }
-    __syncthreads();
-    return s_total;
-}
+// Where a workgroup of a chain launch sits: its sequence slot, its index in
+// that slot's tasks, and the sequence in the slot.
+struct Placement {
+    int sidx;
+    int64_t w;
+    int b;
+};
 
-// The sequence in dispatch slot s, given sampled_sequences' masks and count.
-// Whole workgroup.
-__device__ int sequence_at(const uint64_t* masks, int B, int total, int s) {
-    if (total < 0) return s;
-    __shared__ int s_b;
-    if (threadIdx.x == 0) {
-        const int nm = (B + kWaveSize - 1) / kWaveSize;
-        const bool sampled = s < total;
-        int k = sampled ? s : s - total;
-        int b = s;
-        for (int c = 0; c < nm; ++c) {
-            uint64_t m = sampled ? masks[c] : ~masks[c];
-            const int valid = min(kWaveSize, B - c * kWaveSize);
-            if (valid < kWaveSize) m &= (1ull << valid) - 1ull;
-            const int cnt = __popcll(m);
-            if (k < cnt) {
-                for (int i = 0; i < k; ++i) m &= m - 1ull;
-                b = c * kWaveSize + __builtin_ctzll(m);
-                break;
-            }
-            k -= cnt;
-        }
-        s_b = b;
-    }
-    __syncthreads();
-    return s_b;
-}
-
-// The sequence handled by dispatch slot s (whole workgroup).
-__device__ int sequence_for_slot(const float* temperature, int B, int s) {
+// Placement of workgroup g. Sequences are dispatched T > 0 first, then the
+// greedy ones, each group by increasing index (identity when B >
+// kMaxOrderedBatch): only T > 0 sequences re-read a row to draw the bonus, so
+// their bonus workgroups start early and overlap the greedy sequences' rows.
+// decode(nS, sidx, w) maps g to its slot given the number nS of T > 0
+// sequences. Wave 0 computes everything (one round trip for the
+// temperatures, ballots, no serial search); whole workgroup, one barrier.
+template <class Decode>
+__device__ __forceinline__ Placement place(const float* temperature, int B, Decode decode) {
     __shared__ uint64_t masks[kMaxOrderedBatch / kWaveSize];
-    return sequence_at(masks, B, sampled_sequences(temperature, B, masks), s);
+    __shared__ Placement s_pl;
+    if (wave_id() == 0) {
+        const int lane = lane_id();
+        const int nm = (B + kWaveSize - 1) / kWaveSize;
+        const bool ordered = B <= kMaxOrderedBatch;
+        int nS = B;
+        if (ordered) {
+            nS = 0;
+            for (int c = 0; c < nm; ++c) {
+                const int i = c * kWaveSize + lane;
+                const uint64_t m = __ballot(i < B && temperature[i] > 0.0f);
+                if (lane == 0) masks[c] = m;
+                nS += __popcll(m);
+            }
+        }
+        int sidx;
+        int64_t w;
+        decode(nS, sidx, w);
+        int b = sidx;
+        if (ordered) {
+            const bool sampled = sidx < nS;
+            int k = sampled ? sidx : sidx - nS;
+            for (int c = 0; c < nm; ++c) {
+                uint64_t m = sampled ? masks[c] : ~masks[c];
+                const int valid = min(kWaveSize, B - c * kWaveSize);
+                if (valid < kWaveSize) m &= (1ull << valid) - 1ull;
+                const int cnt = __popcll(m);
+                if (k < cnt) {   // the k-th set bit of m
+                    const bool bit = (m >> lane) & 1ull;
+                    const uint64_t hit = __ballot(bit && lanes_below(m) == k);
+                    b = c * kWaveSize + __builtin_ctzll(hit);
+                    break;
+                }
+                k -= cnt;
+            }
+        }
+        if (lane == 0) s_pl = Placement{sidx, w, b};
+    }
+    __syncthreads();
+    return s_pl;
 }
 
 // Waits until the n slots are all published (wave 0 polls with agent-scope

@@ -2,7 +2,7 @@
 // sec. 2.2, 2.7, 3.1; Speculative Decoding (dl-note), sec. 2.2-2.3 and
 // Appendix "Implementation Details"].
 //
-// One launch. Sequences are taken T > 0 first (sequence_for_slot). Per
+// One launch. Sequences are taken T > 0 first (place). Per
 // sequence, row workgroups stream one chunk of one row each: target rows
 // 0..gamma and (for T > 0) draft rows 0..gamma-1, each read once from HBM
 // with 16-byte loads, and publish the chunk's statistics (online max and sum
@@ -27,10 +27,12 @@ __global__ __launch_bounds__(kThreads) void chain_verify_kernel(ChainArgs a) {
     constexpr int esz = ElemT<DT>::kBytes;
     const int R = 2 * a.gamma + 1;
     const int64_t RS = int64_t(R) * a.S;                 // row workgroups per sequence
-    int sidx;                                            // dispatch slot of the sequence
-    int64_t w;
-    decode_chain(blockIdx.x, a.B, RS, a.H, a.D, sidx, w);
-    const int b = sequence_for_slot(a.temperature, a.B, sidx);
+    const Placement pl = place(a.temperature, a.B, [&](int, int& s, int64_t& w) {
+        decode_chain(blockIdx.x, a.B, RS, a.H, a.D, s, w);
+    });
+    const int sidx = pl.sidx;   // dispatch slot of the sequence
+    const int64_t w = pl.w;
+    const int b = pl.b;
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
     uint64_t* slots = a.slots + int64_t(sidx) * RS;

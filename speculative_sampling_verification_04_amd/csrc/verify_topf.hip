@@ -57,13 +57,12 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     __shared__ FusedLds<K> lds;
     constexpr int esz = ElemT<DT>::kBytes;
     const int R1 = 2 * a.gamma + 2;
-    __shared__ uint64_t masks[kMaxOrderedBatch / kWaveSize];
-    const int nS = sampled_sequences(a.temperature, a.B, masks);
-    int sidx;
-    int64_t w;
-    decode_fused(blockIdx.x, a.B, nS < 0 ? a.B : nS, a.gamma + 1, a.H, a.D, sidx, w);
-    const int slot = int(w);
-    const int b = sequence_at(masks, a.B, nS, sidx);
+    const Placement pl = place(a.temperature, a.B, [&](int nS, int& sidx, int64_t& w) {
+        decode_fused(blockIdx.x, a.B, nS, a.gamma + 1, a.H, a.D, sidx, w);
+    });
+    const int sidx = pl.sidx;
+    const int slot = int(pl.w);
+    const int b = pl.b;
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
     const int64_t words = R1 + (Cache ? 3 * (a.gamma + 1) : 0);  // per sequence
