@@ -103,6 +103,7 @@ EDGE = [
     (5, 6, 70000, "bf16", "half0_half1", 4.0, 1.5, 12),   # H = 5
     (2, 4, 300000, "f32", "all0.8", 3.0, 1.0, 13),        # 586 tiles: H = 16
     (4, 3, 40000, "bf16", "all1", 3.0, 0.02, 14),         # nearly all accepted: p_t of row gamma
+    (4100, 1, 64, "f32", "half0_half1", 2.0, 1.0, 15),     # B > 4096: sequences taken in index order
 ]
 
 

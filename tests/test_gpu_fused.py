@@ -38,6 +38,7 @@ def run_both(w, F):
     ("fused-F16", 256, 8, 9000, "bf16", "all1", 16),
     ("split-small-batch", 4, 5, 50000, "bf16", "half0_half1", 4),
     ("split-tiny", 3, 2, 40, "f32", "all0.8", 7),
+    ("batch-over-4096", 4100, 1, 64, "f32", "half0_half1", 3),   # sequences taken in index order
 ])
 def test_fused_equals_separate_and_oracle(name, B, gamma, V, dtype, temps, F):
     if name == "headline":
