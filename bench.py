@@ -253,7 +253,7 @@ def main():
         tout = binding.tree_verify(tt, td, tpar, ttok, ttemp, tw.seed, 0, workspace=tws)
         tree_ms = timed(lambda i: binding.tree_verify(tt, td, tpar, ttok, ttemp, tw.seed, i, workspace=tws, out=tout))
         tree_bytes = tree_algorithmic_bytes(tw)
-        tree = {"workload": TREE_WORKLOAD, "kernels": "tree_stats_kernel + tree_walk_kernel", "B": tw.B, "N": tw.N, "V": tw.V,
+        tree = {"workload": TREE_WORKLOAD, "kernels": "tree_fused_kernel (rows and walks in one launch)", "B": tw.B, "N": tw.N, "V": tw.V,
                 "avg_ms": tree_ms, "algorithmic_bytes": tree_bytes, "gbps": tree_bytes / (tree_ms * 1e-3) / 1e9,
                 "trees_per_s": tw.B / (tree_ms * 1e-3),
                 "mean_accepted": float(tout["num_accepted"].float().mean().item())}

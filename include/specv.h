@@ -294,10 +294,13 @@ specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes,
  * in walk order, then -1; out_num_accepted int32 [batch]; out_bonus int32
  * [batch]. Workspace as for specv_verify (zero-filled before first use, left
  * zero-filled by every call).
- * Enqueues two kernels: the row statistics, then the walk, whose passes over
- * a node's rows are shared by up to 16 workgroups per tree that wait for each
- * other (workgroups start in index order, so every tree gets all of its
- * workgroups resident).
+ * Enqueues one kernel for trees of up to 256 nodes (the row statistics, and
+ * each tree's walk as soon as its rows are done) and two beyond (the row
+ * statistics, then the walks). A walk's passes over a node's rows are shared
+ * by up to 16 workgroups per tree that wait for each other and for the
+ * tree's rows (workgroups start in index order and those they wait for come
+ * earlier or beside them, so every tree gets all of its workgroups resident).
+ * A wait that times out (about a second) makes that tree report -1.
  */
 specv_status specv_tree_verify(specv_logits target, specv_logits draft,
                                const int32_t* parent, const int32_t* tokens,

@@ -529,8 +529,8 @@ specv_status specv_tree_verify(specv_logits target, specv_logits draft, const in
     if (!parent || !tokens || !temperature || !out_path || !out_num_accepted || !out_bonus)
         return fail(SPECV_ERR_INVALID_ARG, "parent, tokens, temperature and the outputs are required");
     const Layout L = layout_for(batch, 2 * int64_t(nodes), vocab);
-    const int64_t grid = int64_t(batch) * 2 * nodes * L.S;
-    if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch");
+    const int32_t H = tree_walkers(vocab);
+    if (tree_grid(batch, nodes, L.S, H) > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch");
     if ((st = check_workspace(workspace, workspace_bytes, tree_bytes(batch, nodes, vocab))) != SPECV_OK) return st;
 
     TreeArgs a;
@@ -550,8 +550,9 @@ specv_status specv_tree_verify(specv_logits target, specv_logits draft, const in
     a.out_nacc = out_num_accepted;
     a.out_bonus = out_bonus;
     a.slots = static_cast<uint64_t*>(workspace);
-    a.H = tree_walkers(vocab);
+    a.H = H;
     a.ntiles = int32_t((int64_t(vocab) + kTileElems - 1) / kTileElems);
+    a.D = tree_fused(nodes) ? bonus_delay(batch, 2 * int64_t(nodes) * L.S) : 0;
     a.cache_nodes = cached_positions(batch, int64_t(vocab) * elem_size(target.dtype), nodes);
     a.walk = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + tree_walk_offset(batch, nodes, vocab));
     const hipError_t e = launch_tree(a, target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32,

@@ -94,7 +94,20 @@ struct TreeArgs {
     // (cacheable) loads: the walk's passes re-read the rows of the nodes it
     // visits, shallow ones first (cached_positions with D = the batch).
     int32_t cache_nodes;
+    // One-launch form (tree_fused): the walkers of tree b follow the rows of
+    // tree b + D in dispatch order.
+    int32_t D;
 };
+
+// Trees of up to this many nodes are verified in one launch.
+constexpr int kFusedTreeNodes = 256;
+inline bool tree_fused(int64_t N) { return N <= kFusedTreeNodes; }
+
+// Workgroups of the tree launch that streams the rows: 2N row tasks of S
+// chunks per tree, and in the one-launch form the H walkers.
+inline int64_t tree_grid(int64_t B, int64_t N, int64_t S, int64_t H) {
+    return B * (2 * N * S + (tree_fused(N) ? H : 0));
+}
 
 struct TopFArgs {
     RowView draft;

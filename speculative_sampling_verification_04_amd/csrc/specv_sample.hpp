@@ -17,7 +17,17 @@
 namespace specv {
 
 constexpr int kTilesInFlight = 4;      // residual pass: tiles per wave per iteration
-constexpr int kMaxSpin = 1 << 24;      // bound on the resolver's wait (about a second)
+
+// Bound on every wait for another workgroup's word, in ticks of the
+// constant-rate clock read by wall_clock64 (100 MHz): 2^27 ticks, about 1.3 s.
+// A wait that reaches it gives up and its call reports failure (-1) instead of
+// hanging.
+constexpr uint64_t kMaxWaitTicks = uint64_t(1) << 27;
+struct WaitBound {
+    uint64_t t0;
+    __device__ WaitBound() : t0(wall_clock64()) {}
+    __device__ bool expired() const { return wall_clock64() - t0 > kMaxWaitTicks; }
+};
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWaveSize - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWaveSize; }
@@ -117,7 +127,7 @@ __device__ bool wait_slots(const uint64_t* slots, int64_t n) {
     __shared__ int s_ok;
     if (wave_id() == 0) {
         int ok = 0;
-        for (int spin = 0; spin < kMaxSpin; ++spin) {
+        for (const WaitBound t; !t.expired();) {
             bool mine = true;
             for (int64_t i = lane_id(); i < n; i += kWaveSize) mine = mine && slot_ready(peek(slots + i));
             if (__all(mine)) { ok = 1; break; }

@@ -2,15 +2,18 @@
 // sec. 6.2 and 6.4]: VerifyGreedy for T = 0, multi-step speculative sampling
 // (MSS) for T > 0.
 //
-// Two launches on the caller's stream.
+// Two kinds of workgroup, in one launch for trees of up to kFusedTreeNodes
+// nodes (tree_fused_kernel: each tree's walkers follow the rows of a later
+// tree in dispatch order, so walks overlap the stream) and in two launches
+// beyond (tree_stats_kernel, then tree_walk_kernel).
 //
-// 1. tree_stats_kernel: the row-statistics stream of the chain kernel over
+// 1. Rows (tree_row): the row-statistics stream of the chain kernel over
 //    every node's target row and over the draft rows of nodes that have
 //    children (the distribution their children were drawn from); every
 //    workgroup publishes one 64-bit word.
 //
-// 2. tree_walk_kernel: H workgroups ("walkers") per tree (launch_tree_dt
-//    says why they are all resident together). Every walker of a tree runs
+// 2. Walkers (tree_walk): H workgroups per tree (launch_tree_dt says why
+//    they are all resident together). Every walker of a tree runs
 //    the same walk on the same data and takes the same decisions; each full pass
 //    over a node's rows that the walk needs is split between them: walker h
 //    sums the weights over its share of the 512-element tiles, keeps its tile
@@ -39,7 +42,8 @@ namespace {
 
 constexpr int kU = 4;          // 16-byte steps per lane per iteration
 constexpr int kD = 0;          // prefetch form (see stream_chunk)
-constexpr int kWalkTiles = 8;  // tiles in flight per wave in a walk pass
+constexpr int kWalkTiles = 8;       // tiles in flight per wave in a walk pass (walk launch)
+constexpr int kFusedWalkTiles = 4;  // the same in the one-launch form
 
 __device__ __forceinline__ const void* row_ptr(const RowView& v, int esz, int64_t b, int64_t r) {
     return static_cast<const char*>(v.data) + (b * v.stride_seq + r * v.stride_row) * esz;
@@ -52,11 +56,8 @@ __device__ __forceinline__ float log2e_over(float T) { return float(1.4426950408
 // Row task w of tree b (w = task * S + chunk; task < N: target row of node
 // task, else draft row of node task - N) -> its statistics word.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void tree_stats_kernel(TreeArgs a) {
+__device__ __forceinline__ void tree_row(const TreeArgs& a, int b, int64_t w) {
     constexpr int esz = ElemT<DT>::kBytes;
-    const int64_t RS = int64_t(2) * a.N * a.S;
-    const int b = int(blockIdx.x / RS);
-    const int64_t w = blockIdx.x % RS;
     const int N = a.N;
     const int chunk = int(w % a.S);
     const int task = int(w / a.S);
@@ -93,6 +94,12 @@ __global__ __launch_bounds__(kThreads) void tree_stats_kernel(TreeArgs a) {
     if (threadIdx.x == 0) publish(a.slots + int64_t(b) * 2 * N * a.S + w, word);
 }
 
+template <int DT>
+__global__ __launch_bounds__(kThreads) void tree_stats_kernel(TreeArgs a) {
+    const int64_t RS = int64_t(2) * a.N * a.S;
+    tree_row<DT>(a, int(blockIdx.x / RS), blockIdx.x % RS);
+}
+
 // ------------------------------------------------------------------ walk
 
 // Walk words of one tree (a.walk + b * kWalkWords, zero at rest): the walkers'
@@ -116,7 +123,7 @@ __device__ bool wait_tagged(const uint64_t* w, int n, uint32_t p) {
     __shared__ int s_ok;
     if (wave_id() == 0) {
         int ok = 0;
-        for (int spin = 0; spin < kMaxSpin; ++spin) {
+        for (const WaitBound t; !t.expired();) {
             bool mine = true;
             for (int i = lane_id(); i < n; i += kWaveSize) mine = mine && uint32_t(peek(w + i) >> 32) == p;
             if (__all(mine)) { ok = 1; break; }
@@ -128,7 +135,9 @@ __device__ bool wait_tagged(const uint64_t* w, int n, uint32_t p) {
     return s_ok != 0;
 }
 
-// Per-walker state of one walk (LDS of the walker).
+// Per-walker state of one walk (LDS of the walker), for trees of up to NM
+// nodes.
+template <int NM>
 struct WalkLds {
     RowStats sp, sq;              // statistics of the current node's target and draft rows
     int32_t kid[kThreads];        // a batch of the current node's children, ascending
@@ -136,21 +145,22 @@ struct WalkLds {
     float u[kThreads];            // each child's uniform
     float part[kMaxWalkers];      // the walkers' totals of the last pass
     float tile[kMaxWalkTiles];    // this walker's tile sums of the last pass
-    int32_t par[kMaxTreeNodes];   // the tree's parents and tokens
-    int32_t tok[kMaxTreeNodes];
-    int32_t first[kMaxTreeNodes]; // each node's lowest-id child (N if none)
-    uint32_t acc1[kMaxTreeNodes / 32];  // bit n: the walk accepts that child (MSS)
+    int32_t par[NM];              // the tree's parents and tokens
+    int32_t tok[NM];
+    int32_t first[NM];            // each node's lowest-id child (N if none)
+    uint32_t acc1[(NM + 31) / 32];  // bit n: the walk accepts that child (MSS)
     int nk, from;                 // batch size; next position of the child scan
     int ok;
 };
 
-template <int DT>
+// TIF: tiles in flight per wave in a pass.
+template <int DT, int NM, int TIF>
 struct Walker {
     const TreeArgs& a;
     int b, h, N, lo, hi;
     float c, v;
     WalkWords w;
-    WalkLds& s;
+    WalkLds<NM>& s;
     const void* prow;
     const void* qrow;
     uint32_t pass = 0;
@@ -165,14 +175,14 @@ struct Walker {
             TargetWeights<DT> f;
             f.p.init(prow, c, s.sp);
             f.V = a.V;
-            weight_tile_range<kWalkTiles>(f, lo, hi, put);
+            weight_tile_range<TIF>(f, lo, hi, put);
         } else {
             ResidualWeights<DT> f;
             f.p.init(prow, c, s.sp);
             f.q.init(qrow, c, s.sq);
             f.coef = coef;
             f.V = a.V;
-            weight_tile_range<kWalkTiles>(f, lo, hi, put);
+            weight_tile_range<TIF>(f, lo, hi, put);
         }
         const double mine = tiles_total(s.tile, hi - lo);
         uint64_t* part = w.part + (pass & 1u) * kMaxWalkers;
@@ -264,11 +274,12 @@ struct Walker {
     }
 };
 
-// Walker h of tree b.
-template <int DT>
+// Walker h of tree b (N <= NM). kWaitRows: the tree's rows may still be
+// streaming (one-launch form).
+template <int DT, int NM, int TIF, bool kWaitRows>
 __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     constexpr int esz = ElemT<DT>::kBytes;
-    __shared__ WalkLds s;
+    __shared__ WalkLds<NM> s;
     __shared__ int s_nacc, s_fail;
     const int N = a.N;
     const float T = a.temperature[b];
@@ -294,9 +305,16 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     }
     __syncthreads();
 
+    // Every row word of the tree is published before any is read: the words
+    // are written once, so all walkers then see the same statistics and take
+    // the same walk, and walker 0's final zeroing cannot race a late row.
+    // Their writers come earlier in dispatch order and never wait.
+    const bool rows_ok = !kWaitRows || wait_slots(slots, int64_t(2) * N * a.S);
+    if (!rows_ok && threadIdx.x == 0) s_fail = 1;
+
     int32_t bonus = -1;
     bool drew = false;
-    if (greedy) {  // VerifyGreedy
+    if (rows_ok && greedy) {  // VerifyGreedy
         int node = 0;
         while (true) {
             if (threadIdx.x == 0) s.sp = merge_slots(slots + int64_t(node) * a.S, a.S, true, 0.0f);
@@ -319,8 +337,8 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
             if (s.ok < 0) { bonus = g; break; }
             node = s.ok;
         }
-    } else {  // MSS
-        Walker<DT> wk{a, b, h, N, int(int64_t(a.ntiles) * h / a.H), int(int64_t(a.ntiles) * (h + 1) / a.H),
+    } else if (rows_ok) {  // MSS
+        Walker<DT, NM, TIF> wk{a, b, h, N, int(int64_t(a.ntiles) * h / a.H), int(int64_t(a.ntiles) * (h + 1) / a.H),
                       log2e_over(T), stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(N)), w, s,
                       nullptr, nullptr};
         // The first child's test at every node uses r = p, whatever the walk
@@ -411,7 +429,7 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     __shared__ int s_done;
     if (wave_id() == 0) {
         int ok = 0;
-        for (int spin = 0; spin < kMaxSpin; ++spin) {
+        for (const WaitBound t; !t.expired();) {
             bool mine = lane_id() == 0 || lane_id() >= a.H || peek(w.ack + lane_id()) != 0ull;
             if (lane_id() == 0 && drew) mine = peek(w.bonus) != 0ull;
             if (__all(mine)) { ok = 1; break; }
@@ -434,11 +452,36 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeArgs a) {
-    tree_walk<DT>(a, int(blockIdx.x / a.H), int(blockIdx.x % a.H));
+    tree_walk<DT, kMaxTreeNodes, kWalkTiles, false>(a, int(blockIdx.x / a.H), int(blockIdx.x % a.H));
+}
+
+// Trees of up to kFusedTreeNodes nodes: rows and walkers in one launch, in the
+// dispatch order of the chain launches (decode_chain): the H walkers of tree b
+// follow the rows of tree b + D, so that each walk overlaps the rows of later
+// trees instead of waiting for the end of the whole stream. The walker's LDS
+// is sized for the small trees and its passes keep fewer tiles in flight, so
+// that the row workgroups keep their residency.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void tree_fused_kernel(TreeArgs a) {
+    const int64_t RS = int64_t(2) * a.N * a.S;
+    int b;
+    int64_t w;
+    decode_chain(blockIdx.x, a.B, RS, a.H, a.D, b, w);
+    if (w >= RS) tree_walk<DT, kFusedTreeNodes, kFusedWalkTiles, true>(a, b, int(w - RS));
+    else tree_row<DT>(a, b, w);
 }
 
 template <int DT>
 hipError_t launch_tree_dt(const TreeArgs& a, hipStream_t stream) {
+    if (tree_fused(a.N)) {
+        // One launch. A walker waits only for its tree's rows and walkers,
+        // all of which come before it or beside it in dispatch order, and row
+        // workgroups never wait: so the walkers of the lowest tree still
+        // walking always get their slots (as below).
+        hipLaunchKernelGGL(tree_fused_kernel<DT>, dim3(unsigned(tree_grid(a.B, a.N, a.S, a.H))), dim3(kThreads), 0,
+                           stream, a);
+        return hipGetLastError();
+    }
     const int64_t grid = int64_t(a.B) * 2 * a.N * a.S;
     hipLaunchKernelGGL(tree_stats_kernel<DT>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();

@@ -38,6 +38,11 @@ def test_named_tree_workload():
     (6, 16, 20000, "bf16", "all1", 4, 4, 1.0, 8),          # 40 tiles: H = 2
     (3, 24, 300000, "f32", "all0.8", 5, 4, 1.0, 9),        # 586 tiles: H = 16
     (400, 4, 20000, "bf16", "half0_half1", 3, 2, 1.0, 10),  # 400 trees x 2 walkers may exceed residency
+    # trees of 256 nodes or fewer: rows and walkers in one launch; larger: two
+    (4, 256, 3000, "bf16", "half0_half1", 8, 4, 0.5, 11),
+    (3, 257, 3000, "bf16", "half0_half1", 8, 4, 0.5, 12),
+    (2, 1500, 1000, "f32", "all1", 12, 6, 1.5, 13),
+    (1, 4096, 600, "bf16", "all0.7", 14, 8, 1.5, 14),
 ])
 def test_tree_shapes(B, N, V, dtype, temps, depth, branching, noise, seed):
     t = workloads.make_tree(B, N, V, depth=depth, branching=branching, dtype=dtype, sigma=3.0,
