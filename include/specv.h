@@ -295,12 +295,13 @@ specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes,
  * [batch]. Workspace as for specv_verify (zero-filled before first use, left
  * zero-filled by every call).
  * Enqueues one kernel for trees of up to 256 nodes (the row statistics, and
- * each tree's walk as soon as its rows are done) and two beyond (the row
- * statistics, then the walks). A walk's passes over a node's rows are shared
- * by up to 16 workgroups per tree that wait for each other and for the
- * tree's rows (workgroups start in index order and those they wait for come
- * earlier or beside them, so every tree gets all of its workgroups resident).
- * A wait that times out (about a second) makes that tree report -1.
+ * each tree's walk, which follows its tree's rows node by node) and two
+ * beyond (the row statistics, then the walks). A walk's passes over a node's
+ * rows are shared by up to 16 workgroups per tree that wait for each other
+ * and for the tree's rows (each XCD starts workgroups in index order and
+ * those they wait for come earlier or beside them, so every tree gets all of
+ * its workgroups resident). A wait that times out (about a second) makes that
+ * tree report -1.
  */
 specv_status specv_tree_verify(specv_logits target, specv_logits draft,
                                const int32_t* parent, const int32_t* tokens,

@@ -2,13 +2,17 @@
 // workgroup index stands for. Plain integer arithmetic with no GPU types, so
 // that the host (and a CPU test) can check it.
 //
-// Every launch relies on two properties of these maps, since workgroups are
-// started in index order and a waiting workgroup holds its CU slot:
+// Every launch relies on two properties of these maps:
 //   * each map is a bijection from [0, B * (RS + H)) onto the tasks;
 //   * every bonus workgroup of a sequence comes after all of its rows, and its
 //     H bonus workgroups come in order h = 0 .. H-1 (the last one collects
 //     what the others publish).
-// Then everything a workgroup waits for was started before it.
+// So a workgroup waits only for workgroups of lower index. Workgroups are
+// dealt to the XCDs in turn and each XCD starts its own in index order, and a
+// waiting workgroup holds its slot. Then the unfinished workgroup of lowest
+// index waits for nothing unfinished, and every workgroup already started on
+// its XCD has a lower index and has finished, so it starts and finishes: the
+// launch always drains.
 #pragma once
 
 #include <stdint.h>

@@ -135,6 +135,29 @@ __device__ bool wait_tagged(const uint64_t* w, int n, uint32_t p) {
     return s_ok != 0;
 }
 
+// Waits until the words of node `node`'s target row (and, with `draft`, its
+// draft row) are published (wave 0 polls). Whole workgroup; false if the
+// bound was reached.
+__device__ bool wait_node(const uint64_t* slots, int N, int S, int node, bool draft) {
+    __shared__ int s_ok;
+    if (wave_id() == 0) {
+        int ok = 0;
+        const int n = draft ? 2 * S : S;
+        for (const WaitBound t; !t.expired();) {
+            bool mine = true;
+            for (int i = lane_id(); i < n; i += kWaveSize) {
+                const int64_t k = i < S ? int64_t(node) * S + i : int64_t(N + node) * S + (i - S);
+                mine = mine && slot_ready(peek(slots + k));
+            }
+            if (__all(mine)) { ok = 1; break; }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane_id() == 0) s_ok = ok;
+    }
+    __syncthreads();
+    return s_ok != 0;
+}
+
 // Per-walker state of one walk (LDS of the walker), for trees of up to NM
 // nodes.
 template <int NM>
@@ -153,8 +176,9 @@ struct WalkLds {
     int ok;
 };
 
-// TIF: tiles in flight per wave in a pass.
-template <int DT, int NM, int TIF>
+// TIF: tiles in flight per wave in a pass. kStreaming: the tree's rows may
+// still be streaming, so a node's words are awaited before they are read.
+template <int DT, int NM, int TIF, bool kStreaming>
 struct Walker {
     const TreeArgs& a;
     int b, h, N, lo, hi;
@@ -198,8 +222,11 @@ struct Walker {
     // The next batch of the node's children (ascending ids; the first batch
     // of a node starts after the node and also brings the node's statistics)
     // and their accept-test inputs. The statistics words and the children's
-    // logits are read in one round trip. Whole workgroup.
-    __device__ __forceinline__ void next_batch(int node, bool first) {
+    // logits are read in one round trip. Whole workgroup; false if a wait for
+    // the node's words ran out.
+    __device__ __forceinline__ bool next_batch(int node, bool first) {
+        const uint64_t* slots = a.slots + int64_t(b) * 2 * N * a.S;
+        if (kStreaming && first && !wait_node(slots, N, a.S, node, true)) return false;
         if (wave_id() == 0) {
             int n = 0, base = first ? node + 1 : s.from;
             for (; base < N && n <= kThreads - kWaveSize; base += kWaveSize) {
@@ -212,7 +239,6 @@ struct Walker {
             if (lane_id() == 0) { s.nk = n; s.from = base; }
         }
         __syncthreads();
-        const uint64_t* slots = a.slots + int64_t(b) * 2 * N * a.S;
         if (first && threadIdx.x == 0) {
             s.sp = merge_slots(slots + int64_t(node) * a.S, a.S, false, c);
             s.sq = merge_slots(slots + int64_t(N + node) * a.S, a.S, false, c);
@@ -230,6 +256,7 @@ struct Walker {
             s.u[threadIdx.x] = stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(ch));
         }
         __syncthreads();
+        return true;
     }
 
     // Final draw from the weights of the last pass (their fp32 walker totals
@@ -274,9 +301,13 @@ struct Walker {
     }
 };
 
-// Walker h of tree b (N <= NM). kWaitRows: the tree's rows may still be
-// streaming (one-launch form).
-template <int DT, int NM, int TIF, bool kWaitRows>
+// Walker h of tree b (N <= NM). kStreaming: the tree's rows may still be
+// streaming (one-launch form): the walk waits for each node's words when it
+// reaches the node (rows are dispatched in node order, so the walk follows
+// the stream of its tree), and walker 0 waits for every word of the tree
+// before returning them to zero. The words are written once, so all walkers
+// see the same statistics and take the same walk.
+template <int DT, int NM, int TIF, bool kStreaming>
 __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     constexpr int esz = ElemT<DT>::kBytes;
     __shared__ WalkLds<NM> s;
@@ -305,18 +336,15 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     }
     __syncthreads();
 
-    // Every row word of the tree is published before any is read: the words
-    // are written once, so all walkers then see the same statistics and take
-    // the same walk, and walker 0's final zeroing cannot race a late row.
-    // Their writers come earlier in dispatch order and never wait.
-    const bool rows_ok = !kWaitRows || wait_slots(slots, int64_t(2) * N * a.S);
-    if (!rows_ok && threadIdx.x == 0) s_fail = 1;
-
     int32_t bonus = -1;
     bool drew = false;
-    if (rows_ok && greedy) {  // VerifyGreedy
+    if (greedy) {  // VerifyGreedy
         int node = 0;
         while (true) {
+            if (kStreaming && !wait_node(slots, N, a.S, node, false)) {
+                if (threadIdx.x == 0) s_fail = 1;
+                break;
+            }
             if (threadIdx.x == 0) s.sp = merge_slots(slots + int64_t(node) * a.S, a.S, true, 0.0f);
             __syncthreads();
             const int32_t g = s.sp.idx;
@@ -337,16 +365,17 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
             if (s.ok < 0) { bonus = g; break; }
             node = s.ok;
         }
-    } else if (rows_ok) {  // MSS
-        Walker<DT, NM, TIF> wk{a, b, h, N, int(int64_t(a.ntiles) * h / a.H), int(int64_t(a.ntiles) * (h + 1) / a.H),
+    } else {  // MSS
+        Walker<DT, NM, TIF, kStreaming> wk{a, b, h, N, int(int64_t(a.ntiles) * h / a.H), int(int64_t(a.ntiles) * (h + 1) / a.H),
                       log2e_over(T), stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(N)), w, s,
                       nullptr, nullptr};
         // The first child's test at every node uses r = p, whatever the walk
         // did before: for trees of up to one node per thread, decide them all
         // at once, in parallel, so that the walk runs down a chain of first
-        // children accepted without waiting (larger trees test every child
-        // when the walk reaches its node).
-        for (int n = threadIdx.x; N <= kThreads && n < N; n += kThreads) {
+        // children accepted without waiting (larger trees, and trees whose
+        // rows may still be streaming, test every child when the walk reaches
+        // its node).
+        for (int n = threadIdx.x; !kStreaming && N <= kThreads && n < N; n += kThreads) {
             const int ch = s.first[n];
             if (ch >= N) continue;
             const int32_t t = s.tok[ch];
@@ -370,7 +399,7 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
             }
             wk.prow = row_ptr(a.target, esz, b, node);
             wk.qrow = row_ptr(a.draft, esz, b, node);
-            wk.next_batch(node, true);
+            if (!wk.next_batch(node, true)) { failed = true; break; }
             double cj = 0.0, Mj = 1.0;   // r = max(0, p - cj q) / Mj; identical everywhere
             bool tiles_valid = false;    // the last pass's tiles hold the weights of the current r
             bool any_child = false, accepted = false;
@@ -379,7 +408,7 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
                 if (k == s.nk) {
                     if (s.from >= N) break;
                     __syncthreads();   // every thread is done with the previous batch
-                    wk.next_batch(node, false);
+                    wk.next_batch(node, false);   // no wait: the node's words were read already
                     k = 0;
                     continue;
                 }
@@ -439,7 +468,9 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     }
     __syncthreads();
     if (drew && threadIdx.x == 0) bonus = s_done ? int32_t(uint32_t(peek(w.bonus))) : -1;
-    const bool fail = s_fail || !s_done;
+    // No row of the tree may publish after its words are returned to zero.
+    const bool rows_done = !kStreaming || wait_slots(slots, int64_t(2) * N * a.S);
+    const bool fail = s_fail || !s_done || !rows_done;
     const int nacc = s_nacc;
     for (int j = nacc + threadIdx.x; j < N; j += kThreads) a.out_path[int64_t(b) * N + j] = -1;
     zero_slots(slots, int64_t(2) * N * a.S);
@@ -474,10 +505,13 @@ __global__ __launch_bounds__(kThreads) void tree_fused_kernel(TreeArgs a) {
 template <int DT>
 hipError_t launch_tree_dt(const TreeArgs& a, hipStream_t stream) {
     if (tree_fused(a.N)) {
-        // One launch. A walker waits only for its tree's rows and walkers,
-        // all of which come before it or beside it in dispatch order, and row
-        // workgroups never wait: so the walkers of the lowest tree still
-        // walking always get their slots (as below).
+        // One launch. Rows never wait; a walker waits for its tree's rows
+        // (lower indices) and for its tree's other walkers (its neighbours in
+        // index order). Each XCD starts its workgroups in index order, so
+        // when the unfinished workgroup of lowest index is a walker, the
+        // workgroups started on any XCD before one of its tree's walkers are
+        // finished ones or that tree's walkers (fewer than an XCD's slots):
+        // all of its tree's walkers get started, and the walk ends.
         hipLaunchKernelGGL(tree_fused_kernel<DT>, dim3(unsigned(tree_grid(a.B, a.N, a.S, a.H))), dim3(kThreads), 0,
                            stream, a);
         return hipGetLastError();
@@ -487,10 +521,9 @@ hipError_t launch_tree_dt(const TreeArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // An ordinary launch: the walkers of a tree wait only for each other, and
-    // workgroups start in index order, so the lowest tree with a walker not
-    // yet started has all the walkers of every lower tree started; those
-    // finish and free their slots, and the next walkers in line are its own.
-    // Every tree therefore gets all of its H <= 16 walkers resident, without
+    // each XCD starts its workgroups in index order, so the lowest tree still
+    // walking finds every workgroup started before its walkers finished, or
+    // one of its own walkers; all of its H <= 16 walkers get started, without
     // the cost of a cooperative launch (~10-20 us here).
     hipLaunchKernelGGL(tree_walk_kernel<DT>, dim3(unsigned(int64_t(a.B) * a.H)), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
