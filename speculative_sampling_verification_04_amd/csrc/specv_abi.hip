@@ -82,7 +82,7 @@ struct Layout {
 Layout layout_for(int64_t batch, int64_t row_tasks_per_seq, int64_t vocab) {
     Layout L;
     choose_split(batch * row_tasks_per_seq, vocab, &L.S, &L.chunk);
-    L.H = bonus_helpers(vocab);
+    L.H = bonus_helpers(vocab, batch);
     L.ntiles = int32_t((vocab + kTileElems - 1) / kTileElems);
     L.slot_bytes = round_up(size_t(batch) * row_tasks_per_seq * L.S * sizeof(uint64_t));
     L.tile_bytes = L.H > 1 ? round_up(size_t(batch) * L.ntiles * sizeof(uint64_t)) : 0;

@@ -110,10 +110,30 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
         }
         return;
     }
-    for (int r = threadIdx.x; r < R; r += kThreads) {
-        const bool draft_row = r > G;
-        st[r] = (greedy && draft_row) ? RowStats{-INFINITY, -INFINITY, -1, 0.0}
-                                      : merge_slots(slots + int64_t(r) * a.S, a.S, greedy, c);
+    // One word per row: thread r reads row r's. Several: row r's S chunk
+    // words are merged by one wave, four rows per wave at a time, with all
+    // their loads in flight together.
+    constexpr int kRowsPerStep = 4;
+    if (a.S == 1) {
+        for (int r = threadIdx.x; r < R; r += kThreads)
+            st[r] = (greedy && r > G) ? RowStats{-INFINITY, -INFINITY, -1, 0.0} : stats_of_word(peek(slots + r), greedy, c);
+    }
+    for (int r0 = wave_id(); a.S > 1 && r0 < R; r0 += kRowsPerStep * kWaves) {
+        uint64_t wv[kRowsPerStep];
+#pragma unroll
+        for (int j = 0; j < kRowsPerStep; ++j) {
+            const int r = r0 + j * kWaves;
+            const bool need = r < R && !(greedy && r > G) && lane_id() < a.S;
+            wv[j] = need ? peek(slots + int64_t(r) * a.S + lane_id()) : 0ull;
+        }
+#pragma unroll
+        for (int j = 0; j < kRowsPerStep; ++j) {
+            const int r = r0 + j * kWaves;
+            if (r >= R) break;
+            const RowStats x = (greedy && r > G) ? RowStats{-INFINITY, -INFINITY, -1, 0.0}
+                                                 : merge_chunk_words(wv[j], a.S, greedy, c);
+            if (lane_id() == 0) st[r] = x;
+        }
     }
     __syncthreads();
 

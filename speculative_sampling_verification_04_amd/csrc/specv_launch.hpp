@@ -133,10 +133,14 @@ inline void choose_split(int64_t row_tasks, int64_t V, int32_t* S, int64_t* chun
 }
 
 // Workgroups that share the bonus draw of one T > 0 sequence: about 32 tiles
-// (16K elements of the row pair) each, at most 16.
-inline int32_t bonus_helpers(int64_t V) {
+// (16K elements of the row pair) each, at most 16. Batches of up to 64
+// sequences leave most of the GPU idle while the draws run, so there each
+// takes about 16 tiles (a shorter draw; at larger batches the extra
+// workgroups cost more slots than they save).
+inline int32_t bonus_helpers(int64_t V, int64_t B) {
     const int64_t ntiles = (V + kTileElems - 1) / kTileElems;
-    const int64_t h = (ntiles + 31) / 32;
+    const int64_t per = B <= 64 ? 16 : 32;
+    const int64_t h = (ntiles + per - 1) / per;
     return int32_t(h < 1 ? 1 : h > 16 ? 16 : h);
 }
 

@@ -128,8 +128,16 @@ __device__ bool wait_slots(const uint64_t* slots, int64_t n) {
     if (wave_id() == 0) {
         int ok = 0;
         for (const WaitBound t; !t.expired();) {
+            // Four loads in flight per lane per step (no short-circuit, so
+            // that no load waits for another).
             bool mine = true;
-            for (int64_t i = lane_id(); i < n; i += kWaveSize) mine = mine && slot_ready(peek(slots + i));
+            int64_t i = lane_id();
+            for (; i + 3 * kWaveSize < n; i += 4 * kWaveSize) {
+                const uint64_t a0 = peek(slots + i), a1 = peek(slots + i + kWaveSize);
+                const uint64_t a2 = peek(slots + i + 2 * kWaveSize), a3 = peek(slots + i + 3 * kWaveSize);
+                mine &= slot_ready(a0) & slot_ready(a1) & slot_ready(a2) & slot_ready(a3);
+            }
+            for (; i < n; i += kWaveSize) mine &= slot_ready(peek(slots + i));
             if (__all(mine)) { ok = 1; break; }
             __builtin_amdgcn_s_sleep(2);
         }
@@ -152,20 +160,50 @@ struct RowStats {
     double Z;    // sum of 2^(z*c - mc)
 };
 
-__device__ __forceinline__ RowStats merge_slots(const uint64_t* p, int S, bool greedy, float c) {
-    RowStats r;
-    r.m = -INFINITY; r.mc = -INFINITY; r.idx = -1; r.Z = 0.0;
-    for (int k = 0; k < S; ++k) {
-        const uint64_t w = peek(p + k);
-        if (greedy) {
-            const float v = slot_hi(w);
-            const int32_t i = slot_idx(w);
-            if (argmax_better(v, i, r.m, r.idx)) { r.m = v; r.idx = i; }
-        } else {
-            const float m = slot_hi(w);
-            merge_softmax(r.m, r.mc, r.Z, m, m * c, double(slot_s(w)));
-        }
+// A row's statistics from its one word (S = 1): what merging that word alone
+// gives. Any thread.
+__device__ __forceinline__ RowStats stats_of_word(uint64_t w, bool greedy, float c) {
+    RowStats r{-INFINITY, -INFINITY, -1, 0.0};
+    const float v = slot_hi(w);
+    if (greedy) {
+        const int32_t i = slot_idx(w);
+        if (i >= 0) { r.m = v; r.idx = i; }
+    } else if (v != -INFINITY) {
+        r.m = v;
+        r.mc = v * c;
+        r.Z = double(slot_s(w));
     }
+    return r;
+}
+
+// A row's statistics from its S <= 64 chunk words, chunk j's word in lane j
+// (the words of lanes >= S are ignored). Greedy: the largest (value, lowest
+// index) over the chunks, an order-free maximum. Softmax: the largest chunk
+// maximum m, then the chunks' sums rescaled to it, 2^(m_j c - m c), and added
+// in the wave's fixed order, so that every workgroup that merges the same
+// words gets the same bits. Whole wave (every lane active); the result is
+// the same in every lane. The S loads are one round trip, issued by the
+// caller.
+__device__ __forceinline__ RowStats merge_chunk_words(uint64_t w, int S, bool greedy, float c) {
+    const bool mine = lane_id() < S;
+    RowStats r;
+    if (greedy) {
+        const int32_t i = slot_idx(w);
+        const uint64_t key = (mine && i >= 0) ? full_key(slot_hi(w), i) : 0ull;
+        const uint64_t best = wave_max_u64(key);
+        r.m = best ? key_logit(uint32_t(best >> 32)) : -INFINITY;
+        r.idx = best ? int32_t(~uint32_t(best)) : -1;
+        r.mc = -INFINITY;
+        r.Z = 0.0;
+        return r;
+    }
+    const float m = mine ? slot_hi(w) : -INFINITY;
+    const uint64_t top = wave_max_u64(uint64_t(logit_key(m)) << 32);
+    r.m = key_logit(uint32_t(top >> 32));
+    r.mc = r.m * c;
+    r.idx = -1;
+    const double part = (m == -INFINITY) ? 0.0 : double(slot_s(w)) * exp2(double(m * c) - double(r.mc));
+    r.Z = wave_sum(part);
     return r;
 }
 

@@ -125,7 +125,7 @@ __device__ bool wait_tagged(const uint64_t* w, int n, uint32_t p) {
         int ok = 0;
         for (const WaitBound t; !t.expired();) {
             bool mine = true;
-            for (int i = lane_id(); i < n; i += kWaveSize) mine = mine && uint32_t(peek(w + i) >> 32) == p;
+            for (int i = lane_id(); i < n; i += kWaveSize) mine &= uint32_t(peek(w + i) >> 32) == p;
             if (__all(mine)) { ok = 1; break; }
             __builtin_amdgcn_s_sleep(2);
         }
@@ -147,7 +147,7 @@ __device__ bool wait_node(const uint64_t* slots, int N, int S, int node, bool dr
             bool mine = true;
             for (int i = lane_id(); i < n; i += kWaveSize) {
                 const int64_t k = i < S ? int64_t(node) * S + i : int64_t(N + node) * S + (i - S);
-                mine = mine && slot_ready(peek(slots + k));
+                mine &= slot_ready(peek(slots + k));
             }
             if (__all(mine)) { ok = 1; break; }
             __builtin_amdgcn_s_sleep(2);
@@ -170,8 +170,6 @@ struct WalkLds {
     float tile[kMaxWalkTiles];    // this walker's tile sums of the last pass
     int32_t par[NM];              // the tree's parents and tokens
     int32_t tok[NM];
-    int32_t first[NM];            // each node's lowest-id child (N if none)
-    uint32_t acc1[(NM + 31) / 32];  // bit n: the walk accepts that child (MSS)
     int nk, from;                 // batch size; next position of the child scan
     int ok;
 };
@@ -238,11 +236,15 @@ struct Walker {
             }
             if (lane_id() == 0) { s.nk = n; s.from = base; }
         }
-        __syncthreads();
-        if (first && threadIdx.x == 0) {
-            s.sp = merge_slots(slots + int64_t(node) * a.S, a.S, false, c);
-            s.sq = merge_slots(slots + int64_t(N + node) * a.S, a.S, false, c);
+        if (first && wave_id() == 1) {  // the node's statistics, beside wave 0's scan
+            const bool lane_ok = lane_id() < a.S;
+            const uint64_t wp = lane_ok ? peek(slots + int64_t(node) * a.S + lane_id()) : 0ull;
+            const uint64_t wq = lane_ok ? peek(slots + int64_t(N + node) * a.S + lane_id()) : 0ull;
+            const RowStats sp = merge_chunk_words(wp, a.S, false, c);
+            const RowStats sq = merge_chunk_words(wq, a.S, false, c);
+            if (lane_id() == 0) { s.sp = sp; s.sq = sq; }
         }
+        __syncthreads();
         const bool mine = threadIdx.x < s.nk;
         const int ch = mine ? s.kid[threadIdx.x] : 0;
         const int32_t t = mine ? s.tok[ch] : -1;
@@ -326,13 +328,6 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     for (int i = threadIdx.x; i < N; i += kThreads) {
         s.par[i] = a.parent[int64_t(b) * N + i];
         s.tok[i] = a.tokens[int64_t(b) * N + i];
-        s.first[i] = N;
-    }
-    for (int i = threadIdx.x; i < (N + 31) / 32; i += kThreads) s.acc1[i] = 0u;
-    __syncthreads();
-    for (int ch = 1 + threadIdx.x; ch < N; ch += kThreads) {
-        const int p = s.par[ch];
-        if (p >= 0 && p < N) atomicMin(&s.first[p], ch);
     }
     __syncthreads();
 
@@ -345,7 +340,11 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
                 if (threadIdx.x == 0) s_fail = 1;
                 break;
             }
-            if (threadIdx.x == 0) s.sp = merge_slots(slots + int64_t(node) * a.S, a.S, true, 0.0f);
+            if (wave_id() == 0) {
+                const uint64_t wg = lane_id() < a.S ? peek(slots + int64_t(node) * a.S + lane_id()) : 0ull;
+                const RowStats sg = merge_chunk_words(wg, a.S, true, 0.0f);
+                if (lane_id() == 0) s.sp = sg;
+            }
             __syncthreads();
             const int32_t g = s.sp.idx;
             if (wave_id() == 0) {
@@ -369,34 +368,9 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
         Walker<DT, NM, TIF, kStreaming> wk{a, b, h, N, int(int64_t(a.ntiles) * h / a.H), int(int64_t(a.ntiles) * (h + 1) / a.H),
                       log2e_over(T), stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(N)), w, s,
                       nullptr, nullptr};
-        // The first child's test at every node uses r = p, whatever the walk
-        // did before: for trees of up to one node per thread, decide them all
-        // at once, in parallel, so that the walk runs down a chain of first
-        // children accepted without waiting (larger trees, and trees whose
-        // rows may still be streaming, test every child when the walk reaches
-        // its node).
-        for (int n = threadIdx.x; !kStreaming && N <= kThreads && n < N; n += kThreads) {
-            const int ch = s.first[n];
-            if (ch >= N) continue;
-            const int32_t t = s.tok[ch];
-            if (t < 0 || t >= a.V) continue;
-            const RowStats sp = merge_slots(slots + int64_t(n) * a.S, a.S, false, wk.c);
-            const RowStats sq = merge_slots(slots + int64_t(N + n) * a.S, a.S, false, wk.c);
-            const double pt = prob_of(load_elem<DT>(row_ptr(a.target, esz, b, n), t), wk.c, sp);
-            const double qt = prob_of(load_elem<DT>(row_ptr(a.draft, esz, b, n), t), wk.c, sq);
-            const float u = stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(ch));
-            if (qt > 0.0 && double(u) <= pt / qt) atomicOr(&s.acc1[n >> 5], 1u << (n & 31));
-        }
-        __syncthreads();
         int node = 0;
         bool failed = false;
         while (!failed) {
-            while (s.first[node] < N && ((s.acc1[node >> 5] >> (node & 31)) & 1u)) {
-                const int ch = s.first[node];
-                if (h == 0 && threadIdx.x == 0) a.out_path[int64_t(b) * N + s_nacc] = ch;
-                if (threadIdx.x == 0) s_nacc = s_nacc + 1;
-                node = ch;
-            }
             wk.prow = row_ptr(a.target, esz, b, node);
             wk.qrow = row_ptr(a.draft, esz, b, node);
             if (!wk.next_batch(node, true)) { failed = true; break; }

@@ -68,7 +68,7 @@ def test_workspace_sizes(lib):
     st, t = ws_size(lib, "specv_tree_verify_workspace_size", 32, 64, 152064)
     # row words, then 49 walk words per tree (2 x 16 pass totals, 16 acknowledgements, the drawn token)
     assert st == 0 and t == 32 * 128 * 8 + 32 * 49 * 8
-    st, c = ws_size(lib, "specv_verify_workspace_size", 4, 2, 16000)   # 32 tiles: one bonus workgroup
+    st, c = ws_size(lib, "specv_verify_workspace_size", 4, 2, 16000)   # 32 tiles, 2 bonus workgroups at B = 4
     assert st == 0 and c % 256 == 0 and c < 4 * 5 * 64 * 8
     assert ws_size(lib, "specv_verify_workspace_size", 0, 8, 10)[0] == INVALID
     assert ws_size(lib, "specv_verify_workspace_size", 1, 65, 10)[0] == INVALID

@@ -98,10 +98,12 @@ EDGE = [
     (16, 8, 513, "bf16", "all0", 4.0, 1.5, 8),
     (2, 64, 1000, "f32", "all1", 0.5, 0.2, 9),
     (300, 2, 300, "bf16", "all0.7", 4.0, 1.0, 10),
-    # the bonus pass shared by H = ceil(tiles / 32) workgroups (at most 16)
-    (3, 3, 16385, "bf16", "all1", 3.0, 1.0, 11),          # 33 tiles: H = 2, uneven split
-    (5, 6, 70000, "bf16", "half0_half1", 4.0, 1.5, 12),   # H = 5
+    # the bonus pass shared by H = ceil(tiles / 16) workgroups up to 64
+    # sequences, ceil(tiles / 32) above (at most 16)
+    (3, 3, 16385, "bf16", "all1", 3.0, 1.0, 11),          # 33 tiles: H = 3, uneven split
+    (5, 6, 70000, "bf16", "half0_half1", 4.0, 1.5, 12),   # 137 tiles: H = 9
     (2, 4, 300000, "f32", "all0.8", 3.0, 1.0, 13),        # 586 tiles: H = 16
+    (80, 2, 20000, "bf16", "half0_half1", 3.0, 1.0, 16),  # 40 tiles above 64 sequences: H = 2
     (4, 3, 40000, "bf16", "all1", 3.0, 0.02, 14),         # nearly all accepted: p_t of row gamma
     (4100, 1, 64, "f32", "half0_half1", 2.0, 1.0, 15),     # B > 4096: sequences taken in index order
 ]
