@@ -90,8 +90,13 @@ struct TopKAcc {
         count = n;
     }
 
+    // One block pushes up to kWaveSize * U groups, onto at most
+    // kCandCap - kWaveSize * U (before a compaction) or K (after one): both
+    // must fit the list.
     template <int U>
     __device__ __forceinline__ void block(const float (&v)[U][kLaneElems], const int64_t* base, const bool* valid) {
+        static_assert(kWaveSize * U + K <= kCandCap && kWaveSize * U < kCandCap,
+                      "a block's candidates must fit the per-wave list after a compaction");
         float vm[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) vm[u] = max8(v[u]);
