@@ -40,6 +40,7 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 static_assert(kMaxTreeNodes == SPECV_MAX_TREE_NODES, "the walk keeps a whole tree in LDS");
 static_assert(kMaxPositions == SPECV_MAX_GAMMA + 1, "per-position fan-out table");
+static_assert(kTopfKeyWords == SPECV_MAX_TOPF + 1, "F + 1 chunk keys per top-F chunk");
 
 // Largest grid the launches accept (grid.x * 256 threads must fit 32 bits).
 constexpr int64_t kMaxGrid = (int64_t(1) << 32) / kThreads - 1;
@@ -139,8 +140,17 @@ bool fused_fits(int64_t batch, int64_t gamma, int64_t vocab) {
     return S == 1;
 }
 
+// The split path's top-F keys: kTopfKeyWords words per chunk of every draft
+// row when the rows are chunked (topf_split), after the verify kernel's words.
+size_t topf_key_bytes(int64_t batch, int64_t gamma, int64_t vocab) {
+    int32_t S;
+    int64_t chunk;
+    topf_split(batch, gamma, vocab, &S, &chunk);
+    return S > 1 ? round_up(size_t(batch) * (gamma + 1) * S * kTopfKeyWords * sizeof(uint64_t)) : 0;
+}
+
 size_t verify_topk_bytes(int64_t batch, int64_t gamma, int64_t vocab) {
-    const size_t plain = layout_for(batch, 2 * gamma + 1, vocab).total();
+    const size_t plain = layout_for(batch, 2 * gamma + 1, vocab).total() + topf_key_bytes(batch, gamma, vocab);
     const size_t fused = fused_layout(batch, gamma, vocab).total();
     return plain > fused ? plain : fused;
 }
@@ -323,6 +333,8 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
             t.F = F;
             t.out_topk = out_topk;
             t.out_logits = out_topk_logits;
+            topf_split(batch, gamma, vocab, &t.S, &t.chunk);
+            t.keys = t.S > 1 ? reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.total()) : nullptr;
             e = launch_topf(t, dt, static_cast<hipStream_t>(stream));
         }
     }
@@ -511,6 +523,9 @@ specv_status specv_bonus_topk(specv_logits draft, const int32_t* draft_tokens, i
     a.F = F;
     a.out_topk = out_topk;
     a.out_logits = out_topk_logits;
+    a.S = 1;          // no workspace here: one workgroup per row
+    a.chunk = vocab;
+    a.keys = nullptr;
     const hipError_t e = launch_topf(a, draft.dtype == SPECV_BF16 ? DT_BF16 : DT_F32, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_bonus_topk launch failed: %s", hipGetErrorString(e));
     return ok();

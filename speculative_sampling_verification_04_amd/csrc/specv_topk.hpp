@@ -115,20 +115,17 @@ struct TopKAcc {
     }
 };
 
-// Ends a row's selection (whole workgroup, after streaming; keys: LDS of
-// topf_keys<K>() words): every wave
-// compacts its candidates to at most K groups, the keys that reach the largest
-// wave threshold are gathered, wave 0 pops the F + 1 largest, and thread 0
-// writes the first F ids (and logits) that are not `excl`, then -1 up to
-// Fmax entries. Returns the F + 1 largest keys of the row in LDS (0 = none),
-// before the exclusion; they stay valid until the caller's next barrier.
+// LDS words that topf_pick (and topf_finish) need for their key list.
 template <int K>
-constexpr int topf_keys() { return kWaves * kLaneElems * K; }   // LDS words topf_finish needs
+constexpr int topf_keys() { return kWaves * kLaneElems * K; }
 
+// The `need` <= K largest keys of what acc streamed, largest first, in LDS
+// (0 = none): every wave compacts its candidates to at most K groups, the
+// keys that reach the largest wave threshold are gathered and wave 0 pops the
+// largest. Whole workgroup.
 template <int DT, int K>
-__device__ __forceinline__ const uint64_t* topf_finish(TopKAcc<DT, K>& acc, const void* rp, int64_t V, int F,
-                                                       int Fmax, int32_t excl, int32_t* out_ids, float* out_logits,
-                                                       uint64_t* keys) {
+__device__ __forceinline__ const uint64_t* topf_pick(TopKAcc<DT, K>& acc, const void* rp, int64_t V, int need,
+                                                     uint64_t* keys) {
     __shared__ uint64_t s_theta[kWaves];
     __shared__ uint64_t s_pick[K];
     __shared__ int s_nkeys;
@@ -157,7 +154,6 @@ __device__ __forceinline__ const uint64_t* topf_finish(TopKAcc<DT, K>& acc, cons
     }
     __syncthreads();
 
-    const int need = F + 1;
     if (wave_id() == 0) {
         const int n = s_nkeys;
         for (int r = 0; r < need; ++r) {
@@ -170,25 +166,44 @@ __device__ __forceinline__ const uint64_t* topf_finish(TopKAcc<DT, K>& acc, cons
         }
     }
     __syncthreads();
-
-    if (threadIdx.x == 0) {
-        int n = 0;
-        for (int r = 0; r < need && n < F; ++r) {
-            const uint64_t key = s_pick[r];
-            if (key == 0) break;
-            const int32_t idx = int32_t(~uint32_t(key));
-            if (idx == excl) continue;
-            out_ids[n] = idx;
-            if (out_logits) out_logits[n] = key_logit(uint32_t(key >> 32));
-            ++n;
-        }
-        for (; n < Fmax; ++n) {  // unused entries (and fewer candidates than F, only when vocab <= F)
-            out_ids[n] = -1;
-            if (out_logits) out_logits[n] = -INFINITY;
-        }
-    }
-    __syncthreads();
     return s_pick;
+}
+
+// Writes the first F of the `need` picked keys that are not `excl` (ids and
+// logits), then -1 up to Fmax entries. One thread.
+__device__ __forceinline__ void topf_write(const uint64_t* pick, int need, int F, int Fmax, int32_t excl,
+                                           int32_t* out_ids, float* out_logits) {
+    int n = 0;
+    for (int r = 0; r < need && n < F; ++r) {
+        const uint64_t key = pick[r];
+        if (key == 0) break;
+        const int32_t idx = int32_t(~uint32_t(key));
+        if (idx == excl) continue;
+        out_ids[n] = idx;
+        if (out_logits) out_logits[n] = key_logit(uint32_t(key >> 32));
+        ++n;
+    }
+    for (; n < Fmax; ++n) {  // unused entries (and fewer candidates than F, only when vocab <= F)
+        out_ids[n] = -1;
+        if (out_logits) out_logits[n] = -INFINITY;
+    }
+}
+
+// Ends a row's selection (whole workgroup, after streaming; keys: LDS of
+// topf_keys<K>() words): every wave compacts its candidates to at most K
+// groups, the keys that reach the largest wave threshold are gathered, wave 0
+// pops the F + 1 largest, and thread 0 writes the first F ids (and logits)
+// that are not `excl`, then -1 up to Fmax entries. Returns the F + 1 largest
+// keys of the row in LDS (0 = none), before the exclusion; they stay valid
+// until the caller's next barrier.
+template <int DT, int K>
+__device__ __forceinline__ const uint64_t* topf_finish(TopKAcc<DT, K>& acc, const void* rp, int64_t V, int F,
+                                                       int Fmax, int32_t excl, int32_t* out_ids, float* out_logits,
+                                                       uint64_t* keys) {
+    const uint64_t* pick = topf_pick<DT, K>(acc, rp, V, F + 1, keys);
+    if (threadIdx.x == 0) topf_write(pick, F + 1, F, Fmax, excl, out_ids, out_logits);
+    __syncthreads();
+    return pick;
 }
 
 // The F-th largest key of the row (no exclusion), or 0 when F = 0: a key is

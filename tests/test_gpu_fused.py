@@ -1,6 +1,7 @@
 """GPU parity of specv_verify_topk: the same outputs as specv_verify followed
 by specv_bonus_topk, and as the oracle. Large batches take the fused kernel
-(one pass over the draft rows); small ones take the two-kernel path."""
+(one pass over the draft rows); small ones take the two-kernel path, whose
+top-F search splits each draft row into chunks and merges their keys."""
 import numpy as np
 import pytest
 import torch
@@ -36,7 +37,10 @@ def run_both(w, F):
     ("headline", None, None, None, None, None, 4),
     ("fused-f32-mixed", 300, 6, 7000, "f32", "half0_half1", 3),
     ("fused-F16", 256, 8, 9000, "bf16", "all1", 16),
-    ("split-small-batch", 4, 5, 50000, "bf16", "half0_half1", 4),
+    ("split-small-batch", 4, 5, 50000, "bf16", "half0_half1", 4),       # top-F rows in 3 chunks
+    ("split-one-sequence", 1, 8, 128256, "bf16", "all1", 4),        # 7 chunks per draft row
+    ("split-F31", 2, 3, 40000, "f32", "half0_half1", 31),           # K = 32, 2 chunks
+    ("split-31-chunks", 1, 2, 600000, "bf16", "half0_half1", 9),    # the most chunks
     ("split-tiny", 3, 2, 40, "f32", "all0.8", 7),
     ("batch-over-4096", 4100, 1, 64, "f32", "half0_half1", 3),   # sequences taken in index order
 ])
@@ -69,7 +73,7 @@ def test_fused_equals_separate_and_oracle(name, B, gamma, V, dtype, temps, F):
 
 def test_fused_leaves_workspace_zero():
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
-    for i, (B, gamma, V) in enumerate([(300, 3, 5000), (8, 2, 9000), (260, 3, 20000), (260, 7, 3000)]):
+    for i, (B, gamma, V) in enumerate([(300, 3, 5000), (8, 2, 9000), (260, 3, 20000), (260, 7, 3000), (2, 2, 40000)]):
         w = workloads.make_chain(B, gamma, V, dtype="bf16", temps="half0_half1", gen_seed=50 + i, philox_seed=i)
         log(f"fused shared workspace {i}: B={B} gamma={gamma} V={V}")
         d = chain_to_dev(w)
