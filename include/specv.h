@@ -154,10 +154,10 @@ specv_status specv_verify_topk_workspace_size(int32_t batch, int32_t gamma,
 
 /*
  * specv_verify and specv_bonus_topk(draft, draft_tokens, ...) in one call,
- * with the same outputs as the two calls. When every row fits one workgroup
- * (large batches) a single kernel streams every draft row once for both the
- * softmax statistics and the top-F candidates; otherwise the two kernels run
- * in turn. draft must have gamma + 1 rows per sequence. Arguments and outputs
+ * with the same outputs as the two calls. One kernel streams every draft row
+ * once for both the softmax statistics and the top-F candidates (in small
+ * batches each row in chunks, whose top-F keys are merged through the
+ * workspace). draft must have gamma + 1 rows per sequence. Arguments and outputs
  * as for specv_verify and specv_bonus_topk (draft_tokens is required here and
  * serves both); workspace as for specv_verify, sized by
  * specv_verify_topk_workspace_size.

@@ -77,7 +77,8 @@ struct Layout {
     int32_t ntiles;
     size_t slot_bytes;
     size_t tile_bytes;
-    size_t total() const { return slot_bytes + tile_bytes; }
+    size_t key_bytes = 0;    // fused kernel with S > 1: the draft-row chunks' top-F keys
+    size_t total() const { return slot_bytes + tile_bytes + key_bytes; }
 };
 
 Layout layout_for(int64_t batch, int64_t row_tasks_per_seq, int64_t vocab) {
@@ -90,14 +91,21 @@ Layout layout_for(int64_t batch, int64_t row_tasks_per_seq, int64_t vocab) {
     return L;
 }
 
-// Layout of the fused kernel: 2*gamma + 2 unsplit rows per sequence, plus
-// three cache words per draft row when the cache outputs are on.
+// Layout of the fused kernel: 2*gamma + 2 rows per sequence in S chunks
+// (small_split; S = 1 with the cache outputs), then the tile words, then,
+// with S > 1, the draft-row chunks' top-F keys; plus three cache words per
+// draft row when the cache outputs are on.
 Layout fused_layout(int64_t batch, int64_t gamma, int64_t vocab, bool cache_words = false) {
     Layout L = layout_for(batch, 2 * gamma + 2, vocab);
-    L.S = 1;
-    L.chunk = vocab;
-    const int64_t words = 2 * gamma + 2 + (cache_words ? 3 * (gamma + 1) : 0);
+    if (cache_words) {
+        L.S = 1;
+        L.chunk = vocab;
+    } else {
+        small_split(batch * (2 * gamma + 2), vocab, &L.S, &L.chunk);
+    }
+    const int64_t words = (2 * gamma + 2) * L.S + (cache_words ? 3 * (gamma + 1) : 0);
     L.slot_bytes = round_up(size_t(batch) * words * sizeof(uint64_t));
+    L.key_bytes = L.S > 1 ? round_up(size_t(batch) * (gamma + 1) * L.S * kTopfKeyWords * sizeof(uint64_t)) : 0;
     return L;
 }
 
@@ -131,28 +139,8 @@ specv_status check_chain_sizes(int32_t batch, int32_t gamma, int32_t vocab) {
     return SPECV_OK;
 }
 
-// The fused kernel runs when every row fits one workgroup; its workspace has
-// 2*gamma + 2 slots per sequence. Otherwise the verify and top-F kernels run.
-bool fused_fits(int64_t batch, int64_t gamma, int64_t vocab) {
-    int32_t S;
-    int64_t chunk;
-    choose_split(batch * (2 * gamma + 2), vocab, &S, &chunk);
-    return S == 1;
-}
-
-// The split path's top-F keys: kTopfKeyWords words per chunk of every draft
-// row when the rows are chunked (topf_split), after the verify kernel's words.
-size_t topf_key_bytes(int64_t batch, int64_t gamma, int64_t vocab) {
-    int32_t S;
-    int64_t chunk;
-    topf_split(batch, gamma, vocab, &S, &chunk);
-    return S > 1 ? round_up(size_t(batch) * (gamma + 1) * S * kTopfKeyWords * sizeof(uint64_t)) : 0;
-}
-
 size_t verify_topk_bytes(int64_t batch, int64_t gamma, int64_t vocab) {
-    const size_t plain = layout_for(batch, 2 * gamma + 1, vocab).total() + topf_key_bytes(batch, gamma, vocab);
-    const size_t fused = fused_layout(batch, gamma, vocab).total();
-    return plain > fused ? plain : fused;
+    return fused_layout(batch, gamma, vocab).total();
 }
 
 // Tree workspace: the row words, then per tree the walk words (the walkers'
@@ -291,10 +279,8 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
     if (!draft_tokens || !temperature || !out_tokens || !out_num_accepted || !out_topk)
         return fail(SPECV_ERR_INVALID_ARG,
                     "draft_tokens, temperature, out_tokens, out_num_accepted and out_topk are required");
-    const bool fused = fused_fits(batch, gamma, vocab);
-    const Layout L = fused ? fused_layout(batch, gamma, vocab) : layout_for(batch, 2 * int64_t(gamma) + 1, vocab);
-    const int64_t grid = fused ? int64_t(batch) * (2 * gamma + 2 + L.H)
-                               : int64_t(batch) * ((2 * gamma + 1) * int64_t(L.S) + L.H);
+    const Layout L = fused_layout(batch, gamma, vocab);
+    const int64_t grid = int64_t(batch) * ((2 * gamma + 2) * int64_t(L.S) + L.H);
     if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch");
     if ((st = check_workspace(workspace, workspace_bytes, verify_topk_bytes(batch, gamma, vocab))) != SPECV_OK)
         return st;
@@ -307,7 +293,8 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
     a.B = batch;
     a.gamma = gamma;
     a.V = vocab;
-    set_bonus(a, L, fused ? 2 * int64_t(gamma) + 2 : (2 * int64_t(gamma) + 1) * L.S, workspace, elem_size(target.dtype));
+    set_bonus(a, L, (2 * int64_t(gamma) + 2) * L.S, workspace, elem_size(target.dtype));
+    if (L.S > 1) a.topf_keys = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.slot_bytes + L.tile_bytes);
     a.seed = seed;
     a.offset = offset;
     a.out_tokens = out_tokens;
@@ -317,27 +304,8 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
     set_plain(a, F);
     a.out_topk = out_topk;
     a.out_topk_logits = out_topk_logits;
-    const int dt = target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32;
-    hipError_t e;
-    if (fused) {
-        e = launch_verify_topf(a, dt, static_cast<hipStream_t>(stream));
-    } else {
-        e = launch_chain(a, dt, static_cast<hipStream_t>(stream));
-        if (e == hipSuccess) {
-            TopFArgs t;
-            t.draft = view(draft);
-            t.tokens = draft_tokens;
-            t.B = batch;
-            t.gamma = gamma;
-            t.V = vocab;
-            t.F = F;
-            t.out_topk = out_topk;
-            t.out_logits = out_topk_logits;
-            topf_split(batch, gamma, vocab, &t.S, &t.chunk);
-            t.keys = t.S > 1 ? reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.total()) : nullptr;
-            e = launch_topf(t, dt, static_cast<hipStream_t>(stream));
-        }
-    }
+    const hipError_t e = launch_verify_topf(a, target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32,
+                                            static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_verify_topk launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -523,9 +491,6 @@ specv_status specv_bonus_topk(specv_logits draft, const int32_t* draft_tokens, i
     a.F = F;
     a.out_topk = out_topk;
     a.out_logits = out_topk_logits;
-    a.S = 1;          // no workspace here: one workgroup per row
-    a.chunk = vocab;
-    a.keys = nullptr;
     const hipError_t e = launch_topf(a, draft.dtype == SPECV_BF16 ? DT_BF16 : DT_F32, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_bonus_topk launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -49,6 +49,10 @@ struct ChainArgs {
     int32_t* out_topk;
     float* out_topk_logits;
     int32_t Fk[kMaxPositions];
+    // With S > 1 (small batches, no cache outputs): every draft-row chunk's
+    // Fk + 1 largest keys, kTopfKeyWords words per chunk, merged by the
+    // sequence's bonus workgroups; zero at rest.
+    uint64_t* topf_keys;
     // SSD cache extensions (verify_topf_kernel only; off when cache_words = 0):
     // draft distribution sigma_{F_k,C} (C = 1: softmax), lenience l, and the
     // hit flag. With cache_words, every draft row also publishes three words
@@ -115,13 +119,6 @@ struct TopFArgs {
     int32_t B, gamma, V, F;
     int32_t* out_topk;
     float* out_logits;       // may be null
-    // Rows in S > 1 chunks (topf_split; needs a workspace): every chunk's
-    // F + 1 largest keys go to `keys` (kTopfKeyWords words per chunk, zero at
-    // rest), and one more workgroup per row merges them. S = 1: one
-    // workgroup per row, no workspace.
-    int32_t S;
-    int64_t chunk;
-    uint64_t* keys;
 };
 
 // Split of a row into chunks so that small batches still fill the GPU:
@@ -139,17 +136,16 @@ inline void choose_split(int64_t row_tasks, int64_t V, int32_t* S, int64_t* chun
     *chunk = c;
 }
 
-// Chunks of a draft row for the top-F search of a small batch. A chunk's
-// workgroup is bound by its chain of round trips more than by its bytes, so
-// the split aims at ~1024 workgroups (not the ~2048 of choose_split) with
-// chunks of at least 16384 elements, and at most kMaxTopfChunks so that a
-// row's chunk keys fit the merging workgroup's LDS. (Measured at gamma = 8,
-// V = 128256: B = 1, 4, 16 take 41, 45, 56 us for the whole call against 49,
-// 53, 59 with one workgroup per row; B = 64 is the same either way.)
+// Chunks per row of the fused verify + top-F kernel (its 2 * gamma + 2 rows
+// per sequence), so that small batches still spread over the GPU. A draft-row
+// chunk's top-K workgroup is bound by its chain of round trips more than by
+// its bytes, so the split aims at ~1024 workgroups (not the ~2048 of
+// choose_split) with chunks of at least 16384 elements (one chunk per row
+// from ~57 sequences of gamma = 8 up), and at most kMaxTopfChunks so that a
+// row's chunk keys (kTopfKeyWords each) fit the merging workgroup's LDS.
 constexpr int kTopfKeyWords = 32;   // the largest F + 1
 constexpr int kMaxTopfChunks = 31;
-inline void topf_split(int64_t B, int64_t gamma, int64_t V, int32_t* S, int64_t* chunk) {
-    const int64_t rows = B * (gamma + 1);
+inline void small_split(int64_t rows, int64_t V, int32_t* S, int64_t* chunk) {
     int64_t s = (1024 + rows - 1) / rows;
     const int64_t by_len = V / 16384 > 0 ? V / 16384 : 1;
     if (s > by_len) s = by_len;

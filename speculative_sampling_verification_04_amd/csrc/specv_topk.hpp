@@ -196,6 +196,32 @@ __device__ __forceinline__ void topf_write(const uint64_t* pick, int need, int F
 // that are not `excl`, then -1 up to Fmax entries. Returns the F + 1 largest
 // keys of the row in LDS (0 = none), before the exclusion; they stay valid
 // until the caller's next barrier.
+// The F1 largest keys of a row searched in chunks, from the chunks' published
+// lists (n words at kw: each chunk's F1 largest keys + 1, 1 for none, 0 =
+// not yet written): waits for the n words, loads them into mk (LDS, n words)
+// and pops the F1 largest, which are the row's own (each of them is among
+// its chunk's F1 largest). Returns them in LDS, largest first (0 = none; all
+// 0 if the wait ran out). Whole workgroup.
+template <int kMaxKeys>
+__device__ __forceinline__ const uint64_t* topf_merge_chunks(const uint64_t* kw, int n, int F1, uint64_t* mk) {
+    __shared__ uint64_t s_pick[kMaxKeys];
+    const bool ok = wait_slots(kw, n);
+    for (int i = threadIdx.x; i < n; i += kThreads) mk[i] = ok ? peek(kw + i) - 1ull : 0ull;
+    __syncthreads();
+    if (wave_id() == 0) {
+        for (int r = 0; r < F1; ++r) {
+            uint64_t l = 0;
+            for (int i = lane_id(); i < n; i += kWaveSize) l = umax64(l, mk[i]);
+            const uint64_t w = wave_max_u64(l);
+            for (int i = lane_id(); i < n; i += kWaveSize)
+                if (w != 0 && mk[i] == w) mk[i] = 0;   // keys are unique: one owner
+            if (lane_id() == 0) s_pick[r] = w;
+        }
+    }
+    __syncthreads();
+    return s_pick;
+}
+
 template <int DT, int K>
 __device__ __forceinline__ const uint64_t* topf_finish(TopKAcc<DT, K>& acc, const void* rp, int64_t V, int F,
                                                        int Fmax, int32_t excl, int32_t* out_ids, float* out_logits,

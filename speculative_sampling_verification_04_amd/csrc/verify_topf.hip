@@ -10,8 +10,14 @@
 // statistics; target rows are as in the verify kernel. Per sequence the
 // slots are target rows 0..gamma, then draft rows 0..gamma; the sequence's H
 // bonus workgroups come after its rows (decode_fused) and resolve it
-// (chain_resolve). Used when every row fits one workgroup (S = 1); otherwise
-// the library runs the two kernels.
+// (chain_resolve).
+//
+// Small batches (small_split; never with the cache outputs) split every row
+// into S chunks, one workgroup each: a draft-row chunk publishes its
+// statistics word and its F_k + 1 largest keys, and bonus workgroup h first
+// merges the keys of draft rows h, h + H, ... into their outputs
+// (topf_merge_chunks; each of a row's F_k + 1 largest keys is among its
+// chunk's), which are exactly those of the one-workgroup search.
 #include "specv_chain.hpp"
 #include "specv_topk.hpp"
 
@@ -40,11 +46,13 @@ struct SoftmaxTopK {
     }
 };
 
-// LDS of a workgroup: a bonus workgroup's, or a draft row's top-K lists and
-// final pick (a workgroup is one or the other).
+// LDS of a workgroup: a bonus workgroup's (its top-F merges, then its
+// resolve), or a draft row's top-K lists and final pick (a workgroup is one
+// or the other).
 template <int K>
 union FusedLds {
     ResolveLds resolve;
+    uint64_t merge[kMaxTopfChunks * kTopfKeyWords];
     struct {
         int32_t cand[kWaves][kCandCap];
         uint64_t cand_key[kWaves][kCandCap];
@@ -57,36 +65,61 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     __shared__ FusedLds<K> lds;
     constexpr int esz = ElemT<DT>::kBytes;
     const int R1 = 2 * a.gamma + 2;
+    const int S = Cache ? 1 : a.S;           // chunks per row: S > 1 only for small batches
+    const int half = (a.gamma + 1) * S;      // target-row tasks of a sequence (as many draft-row tasks)
     const Placement pl = place(a.temperature, a.B, [&](int nS, int& sidx, int64_t& w) {
-        decode_fused(blockIdx.x, a.B, nS, a.gamma + 1, a.H, a.D, sidx, w);
+        decode_fused(blockIdx.x, a.B, nS, half, a.H, a.D, sidx, w);
     });
     const int sidx = pl.sidx;
-    const int slot = int(pl.w);
+    const int slot = int(pl.w);              // row task: row slot * S + chunk, then the bonus workgroups
     const int b = pl.b;
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
-    const int64_t words = R1 + (Cache ? 3 * (a.gamma + 1) : 0);  // per sequence
+    const int64_t words = int64_t(R1) * S + (Cache ? 3 * (a.gamma + 1) : 0);  // per sequence
     uint64_t* slots = a.slots + int64_t(sidx) * words;
-    if (slot >= R1) {  // bonus workgroup: dispatched after every row of the sequence
+    if (slot >= 2 * half) {  // bonus workgroup: dispatched after every row of the sequence
+        const int h = slot - 2 * half;
+        if (!Cache && S > 1) {
+            // Top-F of the draft rows searched in chunks: bonus workgroup h
+            // merges rows h, h + H, ... (all of a sequence's chunks came
+            // before it) and writes their outputs.
+            for (int row = h; row <= a.gamma; row += a.H) {
+                const int F1 = a.Fk[row] + 1;
+                uint64_t* kw = a.topf_keys + (int64_t(b) * (a.gamma + 1) + row) * S * kTopfKeyWords;
+                const uint64_t* pick = topf_merge_chunks<kTopfKeyWords>(kw, S * F1, F1, lds.merge);
+                if (threadIdx.x == 0) {
+                    const int64_t out = (int64_t(b) * (a.gamma + 1) + row) * a.F;
+                    const int32_t excl = row < a.gamma ? a.tokens[int64_t(b) * a.gamma + row] : -1;
+                    topf_write(pick, F1, F1 - 1, a.F, excl, a.out_topk + out,
+                               a.out_topk_logits ? a.out_topk_logits + out : nullptr);
+                }
+                zero_slots(kw, S * F1);
+                __syncthreads();
+            }
+        }
         chain_resolve<DT, false, Cache>(a, dense_seq<DT>(a, b), T, slots, words,
-                                        a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, slot - R1, lds.resolve);
+                                        a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, h, lds.resolve);
         return;
     }
-    const bool draft_row = slot > a.gamma;
-    const int row = draft_row ? slot - (a.gamma + 1) : slot;
+    const int task = slot / S;               // row slot: target rows 0..gamma, then draft rows
+    const int chunk = slot - task * S;
+    const bool draft_row = task > a.gamma;
+    const int row = draft_row ? task - (a.gamma + 1) : task;
     const int64_t V = a.V;
+    const int64_t lo = int64_t(chunk) * a.chunk;
+    const int64_t hi = min(V, lo + a.chunk);
 
     uint64_t word = pack_skipped();
     if (!draft_row) {
         const void* rp = row_ptr(a.target, esz, b, row);
         if (greedy) {
             ArgmaxAcc acc;
-            stream_chunk<DT, kTargetU, kTargetD>(rp, 0, V, acc);
+            stream_chunk<DT, kTargetU, kTargetD>(rp, lo, hi, acc);
             block_merge_argmax(acc.best, acc.idx);
             word = pack_argmax(acc.best, acc.idx);
         } else {
             SoftmaxAcc acc(log2e_over(T));
-            stream_chunk_as<DT, kTargetU, kTargetD>(row < a.cache_rows, rp, 0, V, acc);
+            stream_chunk_as<DT, kTargetU, kTargetD>(row < a.cache_rows, rp, lo, hi, acc);
             block_merge_softmax(acc.m, acc.mc, acc.s);
             word = pack_softmax(acc.m, acc.s);
         }
@@ -103,10 +136,11 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
         if (!greedy && row < a.gamma) {
             SoftmaxTopK<DT, K> acc(log2e_over(T));
             acc.tk.init(cand[wave_id()], cand_key[wave_id()]);
-            stream_chunk_as<DT, kDraftU, kDraftD>(row < a.cache_rows, rp, 0, V, acc);
+            stream_chunk_as<DT, kDraftU, kDraftD>(row < a.cache_rows, rp, lo, hi, acc);
             block_merge_softmax(acc.sm.m, acc.sm.mc, acc.sm.s);
             word = pack_softmax(acc.sm.m, acc.sm.s);
-            pick = topf_finish<DT, K>(acc.tk, rp, V, Fk, a.F, excl, ids, vals, lds.rows.keys);
+            pick = S > 1 ? topf_pick<DT, K>(acc.tk, rp, V, Fk + 1, lds.rows.keys)
+                         : topf_finish<DT, K>(acc.tk, rp, V, Fk, a.F, excl, ids, vals, lds.rows.keys);
             if (Cache && a.C < 1.0f && Fk > 0 && threadIdx.x == 0) {
                 // sigma_{F,C}: the normaliser loses (1 - C) of the top-F terms,
                 // taken relative to the same reference m*c as the row sum.
@@ -121,8 +155,13 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
         } else {
             TopKAcc<DT, K> acc;
             acc.init(cand[wave_id()], cand_key[wave_id()]);
-            stream_chunk<DT, kDraftU, kDraftD>(rp, 0, V, acc);
-            pick = topf_finish<DT, K>(acc, rp, V, Fk, a.F, excl, ids, vals, lds.rows.keys);
+            stream_chunk<DT, kDraftU, kDraftD>(rp, lo, hi, acc);
+            pick = S > 1 ? topf_pick<DT, K>(acc, rp, V, Fk + 1, lds.rows.keys)
+                         : topf_finish<DT, K>(acc, rp, V, Fk, a.F, excl, ids, vals, lds.rows.keys);
+        }
+        if (S > 1 && threadIdx.x <= Fk) {  // this chunk's Fk + 1 largest keys, for the merge
+            uint64_t* kw = a.topf_keys + (int64_t(b) * (a.gamma + 1) + row) * S * kTopfKeyWords + chunk * (Fk + 1);
+            publish(kw + threadIdx.x, pick[threadIdx.x] + 1ull);
         }
         if (Cache && threadIdx.x == 0) {
             uint64_t* extra = slots + R1 + 3 * row;
@@ -136,7 +175,9 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
 
 template <int DT, bool Cache>
 hipError_t launch_dt(const ChainArgs& a, hipStream_t stream) {
-    const dim3 grid(unsigned(int64_t(a.B) * (2 * a.gamma + 2 + a.H)));
+    if (!Cache && a.S > 1 && (a.S > kMaxTopfChunks || a.F + 1 > kTopfKeyWords || a.topf_keys == nullptr))
+        return hipErrorInvalidValue;   // the merge's LDS and key area
+    const dim3 grid(unsigned(int64_t(a.B) * ((2 * a.gamma + 2) * int64_t(Cache ? 1 : a.S) + a.H)));
     const int K = a.F + 1;
     if (K <= 2) hipLaunchKernelGGL((verify_topf_kernel<DT, 2, Cache>), grid, dim3(kThreads), 0, stream, a);
     else if (K <= 4) hipLaunchKernelGGL((verify_topf_kernel<DT, 4, Cache>), grid, dim3(kThreads), 0, stream, a);

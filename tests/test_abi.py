@@ -112,11 +112,14 @@ def test_verify_validation(lib):
 def test_verify_topk_validation(lib):
     st, n = ws_size(lib, "specv_verify_topk_workspace_size", 256, 8, 128256)
     assert st == 0 and n == 256 * 18 * 8 + 256 * 251 * 8   # fused: 2*gamma + 2 row words per sequence
+    # 8 sequences, one chunk per row: 10 row words each, then the tiles of the 4
+    # bonus workgroups (16 tiles each up to 64 sequences: 63 tiles at V = 32000)
     st, m = ws_size(lib, "specv_verify_topk_workspace_size", 8, 4, 32000)
-    assert st == 0 and m == ws_size(lib, "specv_verify_workspace_size", 8, 4, 32000)[1]   # two kernels
-    # two kernels, the top-F rows in 6 chunks: the verify words, then 32 key words per chunk
+    assert st == 0 and m == 768 + 8 * 63 * 8 + 64
+    # 2 sequences, rows in 6 chunks: row words, tile words (196 tiles), then
+    # 32 top-F key words per draft-row chunk
     st, m = ws_size(lib, "specv_verify_topk_workspace_size", 2, 3, 100000)
-    assert st == 0 and m == ws_size(lib, "specv_verify_workspace_size", 2, 3, 100000)[1] + 2 * 4 * 6 * 32 * 8
+    assert st == 0 and m == 768 + (2 * 196 * 8 + 192) + 2 * 4 * 6 * 32 * 8
 
     def call(F=2, B=2, topk=FAKE, tokens=FAKE, ws_bytes=1 << 20, ws=FAKE):
         return lib.specv_verify_topk(L(), L(), tokens, FAKE, B, 3, 10, F, 1, 0, FAKE, FAKE, None, None,

@@ -1,7 +1,7 @@
 """GPU parity of specv_verify_topk: the same outputs as specv_verify followed
-by specv_bonus_topk, and as the oracle. Large batches take the fused kernel
-(one pass over the draft rows); small ones take the two-kernel path, whose
-top-F search splits each draft row into chunks and merges their keys."""
+by specv_bonus_topk, and as the oracle. One kernel streams every draft row
+once; small batches split each row into chunks and merge the draft rows'
+top-F keys in the bonus workgroups."""
 import numpy as np
 import pytest
 import torch
@@ -37,7 +37,7 @@ def run_both(w, F):
     ("headline", None, None, None, None, None, 4),
     ("fused-f32-mixed", 300, 6, 7000, "f32", "half0_half1", 3),
     ("fused-F16", 256, 8, 9000, "bf16", "all1", 16),
-    ("split-small-batch", 4, 5, 50000, "bf16", "half0_half1", 4),       # top-F rows in 3 chunks
+    ("split-small-batch", 4, 5, 50000, "bf16", "half0_half1", 4),       # rows in 3 chunks
     ("split-one-sequence", 1, 8, 128256, "bf16", "all1", 4),        # 7 chunks per draft row
     ("split-F31", 2, 3, 40000, "f32", "half0_half1", 31),           # K = 32, 2 chunks
     ("split-31-chunks", 1, 2, 600000, "bf16", "half0_half1", 9),    # the most chunks
