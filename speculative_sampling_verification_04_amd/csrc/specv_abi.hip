@@ -92,17 +92,11 @@ Layout layout_for(int64_t batch, int64_t row_tasks_per_seq, int64_t vocab) {
 }
 
 // Layout of the fused kernel: 2*gamma + 2 rows per sequence in S chunks
-// (small_split; S = 1 with the cache outputs), then the tile words, then,
-// with S > 1, the draft-row chunks' top-F keys; plus three cache words per
-// draft row when the cache outputs are on.
+// (small_split) and, with the cache outputs, three cache words per draft row;
+// then the tile words; then, with S > 1, the draft-row chunks' top-F keys.
 Layout fused_layout(int64_t batch, int64_t gamma, int64_t vocab, bool cache_words = false) {
     Layout L = layout_for(batch, 2 * gamma + 2, vocab);
-    if (cache_words) {
-        L.S = 1;
-        L.chunk = vocab;
-    } else {
-        small_split(batch * (2 * gamma + 2), vocab, &L.S, &L.chunk);
-    }
+    small_split(batch * (2 * gamma + 2), vocab, &L.S, &L.chunk);
     const int64_t words = (2 * gamma + 2) * L.S + (cache_words ? 3 * (gamma + 1) : 0);
     L.slot_bytes = round_up(size_t(batch) * words * sizeof(uint64_t));
     L.key_bytes = L.S > 1 ? round_up(size_t(batch) * (gamma + 1) * L.S * kTopfKeyWords * sizeof(uint64_t)) : 0;
@@ -347,7 +341,7 @@ specv_status specv_verify_cache(specv_logits target, specv_logits draft, const i
         return fail(SPECV_ERR_INVALID_ARG,
                     "draft_tokens, temperature, out_tokens, out_num_accepted and out_topk are required");
     const Layout L = fused_layout(batch, gamma, vocab, true);
-    const int64_t grid = int64_t(batch) * (2 * gamma + 2 + L.H);
+    const int64_t grid = int64_t(batch) * ((2 * gamma + 2) * int64_t(L.S) + L.H);
     if (grid > kMaxGrid) return fail(SPECV_ERR_INVALID_ARG, "batch too large for one launch");
     if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
 
@@ -359,7 +353,8 @@ specv_status specv_verify_cache(specv_logits target, specv_logits draft, const i
     a.B = batch;
     a.gamma = gamma;
     a.V = vocab;
-    set_bonus(a, L, 2 * int64_t(gamma) + 2, workspace, elem_size(target.dtype));
+    set_bonus(a, L, (2 * int64_t(gamma) + 2) * L.S, workspace, elem_size(target.dtype));
+    if (L.S > 1) a.topf_keys = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.slot_bytes + L.tile_bytes);
     a.seed = seed;
     a.offset = offset;
     a.out_tokens = out_tokens;

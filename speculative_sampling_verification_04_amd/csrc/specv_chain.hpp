@@ -92,7 +92,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
     const bool greedy = !(T > 0.0f);
     const bool last = h == a.H - 1;
     const float c = greedy ? 0.0f : log2e_over(T);
-    const uint64_t* extra = slots + 2 * G + 2;  // the cache words, when a.cache_words
+    const uint64_t* extra = slots + int64_t(2 * G + 2) * a.S;  // the cache words, when a.cache_words
 
     if (greedy && !last) return;  // the greedy bonus is an argmax: nothing to share
 

@@ -60,12 +60,23 @@ union FusedLds {
     } rows;
 };
 
+// The sigma_{F,C} normaliser word of a draft row: its softmax sum Z (relative
+// to the reference m*c) loses (1 - C) of its F largest terms; 2 << 32 (no
+// scaling) if nothing would be left.
+__device__ __forceinline__ uint64_t sigma_word(const uint64_t* pick, int F, float c, float mc, double Z, float C) {
+    double top = 0.0;
+    for (int r = 0; r < F; ++r)
+        if (pick[r] != 0ull) top += exp2(double(key_logit(uint32_t(pick[r] >> 32))) * double(c) - double(mc));
+    const double zs = Z - (1.0 - double(C)) * top;
+    return zs > 0.0 ? (1ull << 32) | uint64_t(__float_as_uint(float(zs))) : 2ull << 32;
+}
+
 template <int DT, int K, bool Cache>
 __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     __shared__ FusedLds<K> lds;
     constexpr int esz = ElemT<DT>::kBytes;
     const int R1 = 2 * a.gamma + 2;
-    const int S = Cache ? 1 : a.S;           // chunks per row: S > 1 only for small batches
+    const int S = a.S;                       // chunks per row: S > 1 only for small batches
     const int half = (a.gamma + 1) * S;      // target-row tasks of a sequence (as many draft-row tasks)
     const Placement pl = place(a.temperature, a.B, [&](int nS, int& sidx, int64_t& w) {
         decode_fused(blockIdx.x, a.B, nS, half, a.H, a.D, sidx, w);
@@ -79,19 +90,40 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     uint64_t* slots = a.slots + int64_t(sidx) * words;
     if (slot >= 2 * half) {  // bonus workgroup: dispatched after every row of the sequence
         const int h = slot - 2 * half;
-        if (!Cache && S > 1) {
+        if (S > 1) {
             // Top-F of the draft rows searched in chunks: bonus workgroup h
             // merges rows h, h + H, ... (all of a sequence's chunks came
-            // before it) and writes their outputs.
+            // before it) and writes their outputs; with the cache outputs it
+            // also publishes each row's three cache words, which the
+            // sequence's resolve waits for with the row words.
             for (int row = h; row <= a.gamma; row += a.H) {
-                const int F1 = a.Fk[row] + 1;
+                const int Fk = a.Fk[row];
+                const int F1 = Fk + 1;
                 uint64_t* kw = a.topf_keys + (int64_t(b) * (a.gamma + 1) + row) * S * kTopfKeyWords;
                 const uint64_t* pick = topf_merge_chunks<kTopfKeyWords>(kw, S * F1, F1, lds.merge);
+                const int32_t excl = row < a.gamma ? a.tokens[int64_t(b) * a.gamma + row] : -1;
                 if (threadIdx.x == 0) {
                     const int64_t out = (int64_t(b) * (a.gamma + 1) + row) * a.F;
-                    const int32_t excl = row < a.gamma ? a.tokens[int64_t(b) * a.gamma + row] : -1;
-                    topf_write(pick, F1, F1 - 1, a.F, excl, a.out_topk + out,
+                    topf_write(pick, F1, Fk, a.F, excl, a.out_topk + out,
                                a.out_topk_logits ? a.out_topk_logits + out : nullptr);
+                }
+                if (Cache) {
+                    const bool scaled = !greedy && row < a.gamma && a.C < 1.0f && Fk > 0;
+                    const uint64_t* rw = slots + int64_t(a.gamma + 1 + row) * S;   // the row's chunk words
+                    __shared__ uint64_t s_zword;
+                    if (threadIdx.x == 0) s_zword = 2ull << 32;
+                    if (scaled && wait_slots(rw, S) && wave_id() == 0) {
+                        const RowStats st = merge_chunk_words(lane_id() < S ? peek(rw + lane_id()) : 0ull, S, false,
+                                                              log2e_over(T));
+                        if (lane_id() == 0) s_zword = sigma_word(pick, Fk, log2e_over(T), st.mc, st.Z, a.C);
+                    }
+                    __syncthreads();
+                    if (threadIdx.x == 0) {
+                        uint64_t* extra = slots + int64_t(R1) * S + 3 * row;
+                        publish(extra + 0, s_zword);
+                        publish(extra + 1, Fk > 0 ? topf_sigma_key(pick, Fk) + 1ull : ~0ull);
+                        publish(extra + 2, Fk > 0 ? topf_cache_key(pick, Fk, excl) + 1ull : ~0ull);
+                    }
                 }
                 zero_slots(kw, S * F1);
                 __syncthreads();
@@ -141,17 +173,8 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
             word = pack_softmax(acc.sm.m, acc.sm.s);
             pick = S > 1 ? topf_pick<DT, K>(acc.tk, rp, V, Fk + 1, lds.rows.keys)
                          : topf_finish<DT, K>(acc.tk, rp, V, Fk, a.F, excl, ids, vals, lds.rows.keys);
-            if (Cache && a.C < 1.0f && Fk > 0 && threadIdx.x == 0) {
-                // sigma_{F,C}: the normaliser loses (1 - C) of the top-F terms,
-                // taken relative to the same reference m*c as the row sum.
-                const float c = log2e_over(T);
-                double top = 0.0;
-                for (int r = 0; r < Fk; ++r)
-                    if (pick[r] != 0ull)
-                        top += exp2(double(key_logit(uint32_t(pick[r] >> 32))) * double(c) - double(acc.sm.mc));
-                const double zs = acc.sm.s - (1.0 - double(a.C)) * top;
-                if (zs > 0.0) zword = (1ull << 32) | uint64_t(__float_as_uint(float(zs)));
-            }
+            if (Cache && S == 1 && a.C < 1.0f && Fk > 0 && threadIdx.x == 0)
+                zword = sigma_word(pick, Fk, log2e_over(T), acc.sm.mc, acc.sm.s, a.C);
         } else {
             TopKAcc<DT, K> acc;
             acc.init(cand[wave_id()], cand_key[wave_id()]);
@@ -163,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
             uint64_t* kw = a.topf_keys + (int64_t(b) * (a.gamma + 1) + row) * S * kTopfKeyWords + chunk * (Fk + 1);
             publish(kw + threadIdx.x, pick[threadIdx.x] + 1ull);
         }
-        if (Cache && threadIdx.x == 0) {
+        if (Cache && S == 1 && threadIdx.x == 0) {
             uint64_t* extra = slots + R1 + 3 * row;
             publish(extra + 0, zword);
             publish(extra + 1, Fk > 0 ? topf_sigma_key(pick, Fk) + 1ull : ~0ull);
@@ -175,9 +198,9 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
 
 template <int DT, bool Cache>
 hipError_t launch_dt(const ChainArgs& a, hipStream_t stream) {
-    if (!Cache && a.S > 1 && (a.S > kMaxTopfChunks || a.F + 1 > kTopfKeyWords || a.topf_keys == nullptr))
+    if (a.S > 1 && (a.S > kMaxTopfChunks || a.F + 1 > kTopfKeyWords || a.topf_keys == nullptr))
         return hipErrorInvalidValue;   // the merge's LDS and key area
-    const dim3 grid(unsigned(int64_t(a.B) * ((2 * a.gamma + 2) * int64_t(Cache ? 1 : a.S) + a.H)));
+    const dim3 grid(unsigned(int64_t(a.B) * ((2 * a.gamma + 2) * int64_t(a.S) + a.H)));
     const int K = a.F + 1;
     if (K <= 2) hipLaunchKernelGGL((verify_topf_kernel<DT, 2, Cache>), grid, dim3(kThreads), 0, stream, a);
     else if (K <= 4) hipLaunchKernelGGL((verify_topf_kernel<DT, 4, Cache>), grid, dim3(kThreads), 0, stream, a);

@@ -75,6 +75,10 @@ CASES = [
     ("greedy-cache", 20, 4, 5000, "bf16", "all0", (5, 4, 3, 2, 1), 0.3, 0.7),
     ("tiny-vocab", 6, 3, 3, "f32", "half0_half1", (2, 2, 2, 2), 0.5, 1.0),
     ("max-fanout", 8, 2, 40, "bf16", "all1", (31, 31, 20), 0.6, 1.0),    # F_k up to SPECV_MAX_TOPF
+    # small batches: rows in chunks, cache words published by the bonus workgroups
+    ("small-batch-chunks", 2, 5, 70000, "bf16", "half0_half1", (6, 5, 4, 3, 2, 2), 0.3, 0.9),   # 4 chunks
+    ("one-greedy-sequence", 1, 3, 40000, "f32", "all0", (3, 3, 3, 3), 0.5, 1.0),               # 2 chunks
+    ("max-fanout-chunks", 2, 2, 50000, "bf16", "all1", (31, 31, 20), 0.6, 1.0),                 # 3 chunks
 ]
 
 
@@ -91,9 +95,10 @@ def test_verify_cache_matches_oracle(name, B, gamma, V, dtype, temps, fanout, C,
     assert bad <= max(1, B // 10)
 
 
-def test_plain_settings_equal_verify_topk():
+@pytest.mark.parametrize("B,V", [(48, 12000), (3, 40000)])   # one chunk per row; two
+def test_plain_settings_equal_verify_topk(B, V):
     # C = 1, l = 1, uniform F: the same outputs as specv_verify_topk.
-    w = workloads.make_chain(48, 4, 12000, dtype="bf16", sigma=3.0, temps="half0_half1", gen_seed=77,
+    w = workloads.make_chain(B, 4, V, dtype="bf16", sigma=3.0, temps="half0_half1", gen_seed=77,
                              philox_seed=7, F=4)
     d = chain_to_dev(w)
     log("cache plain settings vs verify_topk")
