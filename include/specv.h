@@ -60,7 +60,9 @@ typedef enum {
  * Strides are in elements (not bytes), may be 0 (broadcast) and must be >= 0;
  * the vocabulary dimension is contiguous. Rows whose start is 16-byte aligned
  * are read with 16-byte vector loads, others element by element. Logits may
- * be -inf but never NaN (results are unspecified for NaN logits). */
+ * be -inf but never NaN (results are unspecified for NaN logits). A caller
+ * that holds probabilities rather than logits passes their natural logarithms
+ * (log 0 = -inf) with temperature 1: softmax(log p) = p. */
 typedef struct {
     const void* data;
     int32_t dtype;        /* specv_dtype */

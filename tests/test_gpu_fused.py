@@ -41,6 +41,7 @@ def run_both(w, F):
     ("split-one-sequence", 1, 8, 128256, "bf16", "all1", 4),        # 7 chunks per draft row
     ("split-F31", 2, 3, 40000, "f32", "half0_half1", 31),           # K = 32, 2 chunks
     ("split-31-chunks", 1, 2, 600000, "bf16", "half0_half1", 9),    # the most chunks
+    ("split-greedy", 2, 3, 40000, "bf16", "all0", 5),                # greedy only, 2 chunks
     ("split-tiny", 3, 2, 40, "f32", "all0.8", 7),
     ("batch-over-4096", 4100, 1, 64, "f32", "half0_half1", 3),   # sequences taken in index order
 ])
@@ -69,6 +70,20 @@ def test_fused_equals_separate_and_oracle(name, B, gamma, V, dtype, temps, F):
         ids, vals = oracle.topf.bonus_topf_batch(w.draft[b:b + 1].astype(np.float64), w.draft_tokens[b:b + 1], F)
         np.testing.assert_array_equal(f["topk"][b], ids[0], err_msg=f"{name}: top-F of sequence {b}")
         np.testing.assert_array_equal(f["topk_logits"][b].astype(np.float64), vals[0])
+
+
+def test_fused_small_batch_nearly_all_accepted():
+    # Draft = target up to tiny noise: almost every draft is accepted and the
+    # bonus comes from p_t of row gamma, merged from chunk words (2 chunks).
+    w = workloads.make_chain(3, 4, 40000, dtype="bf16", sigma=3.0, noise=0.02, temps="all1", gen_seed=61,
+                             philox_seed=61)
+    log("fused small batch, nearly all accepted")
+    f, s = run_both(w, 6)
+    ref, seqs = run_chain_oracle(w)
+    compare_chain(f, ref, seqs, w.gamma, "fused nearly all accepted")
+    assert (f["num_accepted"] == w.gamma).sum() >= 2
+    for k in ("topk", "topk_logits"):
+        np.testing.assert_array_equal(f[k], s[k], err_msg=f"nearly all accepted: {k}")
 
 
 def test_fused_leaves_workspace_zero():
