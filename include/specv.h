@@ -323,6 +323,18 @@ specv_status specv_uniforms(uint64_t seed, uint64_t offset, int32_t tag,
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* specv_last_error(void);
 
+/*
+ * For tests of the failure path. The kernels' workgroups wait for each
+ * other's published words (row statistics, tile sums, top-F keys, a tree's
+ * pass totals); every wait is bounded, by default by 2^27 ticks of the
+ * GPU's 100 MHz constant clock (about 1.3 s), and a wait that runs out makes
+ * its sequence or tree report -1 instead of hanging. This sets the bound for
+ * later calls from any thread (0 restores the default) and returns the
+ * previous one. A call whose waits ran out may leave words in its
+ * workspace: zero it before the next call. Not for production use.
+ */
+uint64_t specv_debug_set_wait_bound(uint64_t ticks);
+
 /* Library version string. */
 const char* specv_version(void);
 

@@ -23,7 +23,7 @@ EXPORTED = ("specv_verify_workspace_size", "specv_verify", "specv_bonus_topk",
             "specv_tree_verify_workspace_size", "specv_tree_verify",
             "specv_verify_cache_workspace_size", "specv_verify_cache", "specv_geometric_fanout",
             "specv_verify_ragged_workspace_size", "specv_verify_ragged",
-            "specv_uniforms", "specv_last_error", "specv_version")
+            "specv_uniforms", "specv_last_error", "specv_version", "specv_debug_set_wait_bound")
 
 
 class SpecvError(RuntimeError):
@@ -82,8 +82,16 @@ def load_library(path=LIB_PATH):
         lib.specv_last_error.argtypes = []
         lib.specv_version.restype = ctypes.c_char_p
         lib.specv_version.argtypes = []
+        lib.specv_debug_set_wait_bound.restype = ctypes.c_uint64
+        lib.specv_debug_set_wait_bound.argtypes = [ctypes.c_uint64]
         _lib = lib
         return lib
+
+
+def set_wait_bound(ticks):
+    """specv_debug_set_wait_bound: the kernels' wait bound in 100 MHz ticks for
+    later calls (0: the default); returns the previous bound. Tests only."""
+    return int(load_library().specv_debug_set_wait_bound(int(ticks)))
 
 
 def _check(status):

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void ragged_verify_kernel(ChainArgs a) {
         const int h = int(w - RS);
         if (!valid) {
             if (h == a.H - 1) {
-                if (wait_slots(slots, RS)) zero_slots(slots, RS);
+                if (wait_slots(slots, RS, a.wait_ticks)) zero_slots(slots, RS);
                 for (int j = threadIdx.x; j <= G; j += kThreads) a.out_tokens[int64_t(b) * (G + 1) + j] = -1;
                 if (threadIdx.x == 0) a.out_nacc[b] = -2;
             }

@@ -6,6 +6,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "specv.h"
@@ -32,6 +33,11 @@ specv_status ok() {
     g_error.clear();
     return SPECV_OK;
 }
+
+// Bound on the kernels' waits for each other's words (WaitBound ticks); only
+// tests change it (specv_debug_set_wait_bound).
+std::atomic<uint64_t> g_wait_ticks{kMaxWaitTicks};
+uint64_t wait_ticks() { return g_wait_ticks.load(std::memory_order_relaxed); }
 
 int elem_size(int32_t dtype) { return dtype == SPECV_BF16 ? 2 : 4; }
 
@@ -189,6 +195,10 @@ using namespace specv;
 
 extern "C" {
 
+uint64_t specv_debug_set_wait_bound(uint64_t ticks) {
+    return g_wait_ticks.exchange(ticks == 0 ? kMaxWaitTicks : ticks);
+}
+
 const char* specv_last_error(void) { return g_error.c_str(); }
 
 const char* specv_version(void) { return "specv 0.1 (gfx950)"; }
@@ -235,6 +245,7 @@ specv_status specv_verify(specv_logits target, specv_logits draft, const int32_t
     if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
 
     ChainArgs a{};
+    a.wait_ticks = wait_ticks();
     a.target = view(target);
     a.draft = view(draft);
     a.tokens = draft_tokens;
@@ -280,6 +291,7 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
         return st;
 
     ChainArgs a{};
+    a.wait_ticks = wait_ticks();
     a.target = view(target);
     a.draft = view(draft);
     a.tokens = draft_tokens;
@@ -346,6 +358,7 @@ specv_status specv_verify_cache(specv_logits target, specv_logits draft, const i
     if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
 
     ChainArgs a{};
+    a.wait_ticks = wait_ticks();
     a.target = view(target);
     a.draft = view(draft);
     a.tokens = draft_tokens;
@@ -408,6 +421,7 @@ specv_status specv_verify_ragged(specv_logits target, specv_logits draft, const 
     if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
 
     ChainArgs a{};
+    a.wait_ticks = wait_ticks();
     a.target = view(target);
     a.draft = view(draft);
     a.tokens = draft_tokens;
@@ -509,6 +523,7 @@ specv_status specv_tree_verify(specv_logits target, specv_logits draft, const in
     if ((st = check_workspace(workspace, workspace_bytes, tree_bytes(batch, nodes, vocab))) != SPECV_OK) return st;
 
     TreeArgs a;
+    a.wait_ticks = wait_ticks();
     a.target = view(target);
     a.draft = view(draft);
     a.parent = parent;

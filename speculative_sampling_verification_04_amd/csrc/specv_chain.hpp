@@ -103,7 +103,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
     __shared__ float s_mass;
     __shared__ uint64_t s_cache_word;
 
-    if (!wait_slots(slots, nslots)) {  // never expected: see wait_slots
+    if (!wait_slots(slots, nslots, a.wait_ticks)) {  // never expected: see wait_slots
         if (last) {
             if (threadIdx.x == 0) a.out_nacc[b] = -1;
             zero_slots(slots, nslots);
@@ -228,7 +228,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
             // Each helper read the row words before publishing its tiles, so
             // once every tile word is seen the row words may be zeroed.
             if (!last) return;
-            if (!wait_slots(tiles, ntiles)) {
+            if (!wait_slots(tiles, ntiles, a.wait_ticks)) {
                 if (threadIdx.x == 0) a.out_nacc[b] = -1;
                 zero_slots(tiles, ntiles);
                 zero_slots(slots, nslots);

@@ -24,6 +24,7 @@ constexpr int kWaves = kThreads / kWaveSize;
 constexpr int kLaneElems = 8;               // elements per lane per step
 constexpr int kTileElems = kWaveSize * kLaneElems;  // residual tile: 512
 constexpr int kMaxTiles = 2048;             // vocab <= 2048 * 512
+constexpr uint64_t kMaxWaitTicks = uint64_t(1) << 27;   // default wait bound: ~1.3 s at 100 MHz (WaitBound)
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
 

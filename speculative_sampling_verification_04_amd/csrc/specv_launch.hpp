@@ -66,6 +66,7 @@ struct ChainArgs {
     // tokens[offsets[b] .. offsets[b+1]); gamma is the largest allowed count.
     const int32_t* offsets;
     int32_t num_draft;
+    uint64_t wait_ticks;     // bound on every wait for another workgroup's word (WaitBound)
 };
 
 // Tree verification. Per tree there are 2N row tasks (target rows of every
@@ -101,6 +102,7 @@ struct TreeArgs {
     // One-launch form (tree_fused): the walkers of tree b follow the rows of
     // tree b + D in dispatch order.
     int32_t D;
+    uint64_t wait_ticks;     // bound on every wait for another workgroup's word (WaitBound)
 };
 
 // Trees of up to this many nodes are verified in one launch.

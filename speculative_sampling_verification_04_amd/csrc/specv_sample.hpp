@@ -19,14 +19,14 @@ namespace specv {
 constexpr int kTilesInFlight = 4;      // residual pass: tiles per wave per iteration
 
 // Bound on every wait for another workgroup's word, in ticks of the
-// constant-rate clock read by wall_clock64 (100 MHz): 2^27 ticks, about 1.3 s.
-// A wait that reaches it gives up and its call reports failure (-1) instead of
+// constant-rate clock read by wall_clock64 (100 MHz): by default 2^27 ticks,
+// about 1.3 s, kMaxWaitTicks (the launches pass it in their arguments). A
+// wait that reaches it gives up and its call reports failure (-1) instead of
 // hanging.
-constexpr uint64_t kMaxWaitTicks = uint64_t(1) << 27;
 struct WaitBound {
-    uint64_t t0;
-    __device__ WaitBound() : t0(wall_clock64()) {}
-    __device__ bool expired() const { return wall_clock64() - t0 > kMaxWaitTicks; }
+    uint64_t t0, ticks;
+    __device__ explicit WaitBound(uint64_t n) : t0(wall_clock64()), ticks(n) {}
+    __device__ bool expired() const { return wall_clock64() - t0 > ticks; }
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWaveSize - 1); }
@@ -123,11 +123,11 @@ __device__ __forceinline__ Placement place(const float* temperature, int B, Deco
 // atomic loads). Every slot's writer is a workgroup with a lower index, which
 // is dispatched before the caller and never waits itself, so the wait ends;
 // the spin is bounded anyway. Returns false if the bound was reached.
-__device__ bool wait_slots(const uint64_t* slots, int64_t n) {
+__device__ bool wait_slots(const uint64_t* slots, int64_t n, uint64_t ticks) {
     __shared__ int s_ok;
     if (wave_id() == 0) {
         int ok = 0;
-        for (const WaitBound t; !t.expired();) {
+        for (const WaitBound t(ticks); !t.expired();) {
             // Four loads in flight per lane per step (no short-circuit, so
             // that no load waits for another).
             bool mine = true;

@@ -203,9 +203,10 @@ __device__ __forceinline__ void topf_write(const uint64_t* pick, int need, int F
 // its chunk's F1 largest). Returns them in LDS, largest first (0 = none; all
 // 0 if the wait ran out). Whole workgroup.
 template <int kMaxKeys>
-__device__ __forceinline__ const uint64_t* topf_merge_chunks(const uint64_t* kw, int n, int F1, uint64_t* mk) {
+__device__ __forceinline__ const uint64_t* topf_merge_chunks(const uint64_t* kw, int n, int F1, uint64_t* mk,
+                                                             uint64_t ticks) {
     __shared__ uint64_t s_pick[kMaxKeys];
-    const bool ok = wait_slots(kw, n);
+    const bool ok = wait_slots(kw, n, ticks);
     for (int i = threadIdx.x; i < n; i += kThreads) mk[i] = ok ? peek(kw + i) - 1ull : 0ull;
     __syncthreads();
     if (wave_id() == 0) {

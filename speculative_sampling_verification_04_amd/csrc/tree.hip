@@ -119,11 +119,11 @@ __device__ __forceinline__ WalkWords walk_of(const TreeArgs& a, int b) {
 
 // Waits until each of the n words carries tag `p` in its high half (wave 0
 // polls; bounded like wait_slots). Whole workgroup.
-__device__ bool wait_tagged(const uint64_t* w, int n, uint32_t p) {
+__device__ bool wait_tagged(const uint64_t* w, int n, uint32_t p, uint64_t ticks) {
     __shared__ int s_ok;
     if (wave_id() == 0) {
         int ok = 0;
-        for (const WaitBound t; !t.expired();) {
+        for (const WaitBound t(ticks); !t.expired();) {
             bool mine = true;
             for (int i = lane_id(); i < n; i += kWaveSize) mine &= uint32_t(peek(w + i) >> 32) == p;
             if (__all(mine)) { ok = 1; break; }
@@ -138,12 +138,12 @@ __device__ bool wait_tagged(const uint64_t* w, int n, uint32_t p) {
 // Waits until the words of node `node`'s target row (and, with `draft`, its
 // draft row) are published (wave 0 polls). Whole workgroup; false if the
 // bound was reached.
-__device__ bool wait_node(const uint64_t* slots, int N, int S, int node, bool draft) {
+__device__ bool wait_node(const uint64_t* slots, int N, int S, int node, bool draft, uint64_t ticks) {
     __shared__ int s_ok;
     if (wave_id() == 0) {
         int ok = 0;
         const int n = draft ? 2 * S : S;
-        for (const WaitBound t; !t.expired();) {
+        for (const WaitBound t(ticks); !t.expired();) {
             bool mine = true;
             for (int i = lane_id(); i < n; i += kWaveSize) {
                 const int64_t k = i < S ? int64_t(node) * S + i : int64_t(N + node) * S + (i - S);
@@ -209,7 +209,7 @@ struct Walker {
         const double mine = tiles_total(s.tile, hi - lo);
         uint64_t* part = w.part + (pass & 1u) * kMaxWalkers;
         if (threadIdx.x == 0) publish(part + h, (uint64_t(pass) << 32) | __float_as_uint(float(mine)));
-        if (!wait_tagged(part, a.H, pass)) return -1.0;
+        if (!wait_tagged(part, a.H, pass, a.wait_ticks)) return -1.0;
         if (threadIdx.x < a.H) s.part[threadIdx.x] = __uint_as_float(uint32_t(peek(part + threadIdx.x)));
         __syncthreads();
         double total = 0.0;
@@ -224,7 +224,7 @@ struct Walker {
     // the node's words ran out.
     __device__ __forceinline__ bool next_batch(int node, bool first) {
         const uint64_t* slots = a.slots + int64_t(b) * 2 * N * a.S;
-        if (kStreaming && first && !wait_node(slots, N, a.S, node, true)) return false;
+        if (kStreaming && first && !wait_node(slots, N, a.S, node, true, a.wait_ticks)) return false;
         if (wave_id() == 0) {
             int n = 0, base = first ? node + 1 : s.from;
             for (; base < N && n <= kThreads - kWaveSize; base += kWaveSize) {
@@ -336,7 +336,7 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     if (greedy) {  // VerifyGreedy
         int node = 0;
         while (true) {
-            if (kStreaming && !wait_node(slots, N, a.S, node, false)) {
+            if (kStreaming && !wait_node(slots, N, a.S, node, false, a.wait_ticks)) {
                 if (threadIdx.x == 0) s_fail = 1;
                 break;
             }
@@ -432,7 +432,7 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     __shared__ int s_done;
     if (wave_id() == 0) {
         int ok = 0;
-        for (const WaitBound t; !t.expired();) {
+        for (const WaitBound t(a.wait_ticks); !t.expired();) {
             bool mine = lane_id() == 0 || lane_id() >= a.H || peek(w.ack + lane_id()) != 0ull;
             if (lane_id() == 0 && drew) mine = peek(w.bonus) != 0ull;
             if (__all(mine)) { ok = 1; break; }
@@ -443,7 +443,7 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     __syncthreads();
     if (drew && threadIdx.x == 0) bonus = s_done ? int32_t(uint32_t(peek(w.bonus))) : -1;
     // No row of the tree may publish after its words are returned to zero.
-    const bool rows_done = !kStreaming || wait_slots(slots, int64_t(2) * N * a.S);
+    const bool rows_done = !kStreaming || wait_slots(slots, int64_t(2) * N * a.S, a.wait_ticks);
     const bool fail = s_fail || !s_done || !rows_done;
     const int nacc = s_nacc;
     for (int j = nacc + threadIdx.x; j < N; j += kThreads) a.out_path[int64_t(b) * N + j] = -1;

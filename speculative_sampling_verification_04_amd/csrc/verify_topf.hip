@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
                 const int Fk = a.Fk[row];
                 const int F1 = Fk + 1;
                 uint64_t* kw = a.topf_keys + (int64_t(b) * (a.gamma + 1) + row) * S * kTopfKeyWords;
-                const uint64_t* pick = topf_merge_chunks<kTopfKeyWords>(kw, S * F1, F1, lds.merge);
+                const uint64_t* pick = topf_merge_chunks<kTopfKeyWords>(kw, S * F1, F1, lds.merge, a.wait_ticks);
                 const int32_t excl = row < a.gamma ? a.tokens[int64_t(b) * a.gamma + row] : -1;
                 if (threadIdx.x == 0) {
                     const int64_t out = (int64_t(b) * (a.gamma + 1) + row) * a.F;
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
                     const uint64_t* rw = slots + int64_t(a.gamma + 1 + row) * S;   // the row's chunk words
                     __shared__ uint64_t s_zword;
                     if (threadIdx.x == 0) s_zword = 2ull << 32;
-                    if (scaled && wait_slots(rw, S) && wave_id() == 0) {
+                    if (scaled && wait_slots(rw, S, a.wait_ticks) && wave_id() == 0) {
                         const RowStats st = merge_chunk_words(lane_id() < S ? peek(rw + lane_id()) : 0ull, S, false,
                                                               log2e_over(T));
                         if (lane_id() == 0) s_zword = sigma_word(pick, Fk, log2e_over(T), st.mc, st.Z, a.C);

@@ -27,7 +27,7 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:specv_status|const char\*)\s+(specv_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:specv_status|const char\*|uint64_t)\s+(specv_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -35,8 +35,17 @@ def test_header_declares_the_entry_points():
     for n in ("specv_verify", "specv_bonus_topk", "specv_tree_verify", "specv_verify_topk",
               "specv_verify_workspace_size", "specv_tree_verify_workspace_size",
               "specv_verify_topk_workspace_size", "specv_verify_cache", "specv_verify_cache_workspace_size",
-              "specv_geometric_fanout", "specv_uniforms", "specv_last_error", "specv_version"):
+              "specv_geometric_fanout", "specv_uniforms", "specv_last_error", "specv_version",
+              "specv_debug_set_wait_bound"):
         assert n in names
+
+
+def test_wait_bound_setter(lib):
+    # Host-side state only: set, read back through the next exchange, restore.
+    default = 1 << 27
+    assert binding.set_wait_bound(5) == default
+    assert binding.set_wait_bound(0) == 5
+    assert binding.set_wait_bound(0) == default
 
 
 def test_every_declared_symbol_is_exported(lib):
