@@ -106,6 +106,8 @@ EDGE = [
     (80, 2, 20000, "bf16", "half0_half1", 3.0, 1.0, 16),  # 40 tiles above 64 sequences: H = 2
     (4, 3, 40000, "bf16", "all1", 3.0, 0.02, 14),         # nearly all accepted: p_t of row gamma
     (4100, 1, 64, "f32", "half0_half1", 2.0, 1.0, 15),     # B > 4096: sequences taken in index order
+    (2, 2, 1048576, "bf16", "half0_half1", 4.0, 1.0, 17),  # the largest vocabulary: 2048 tiles, 16 bonus workgroups
+    (1, 64, 30000, "f32", "all1", 2.0, 0.05, 18),          # the longest draft, nearly all accepted
 ]
 
 

@@ -42,6 +42,8 @@ def run_both(w, F):
     ("split-F31", 2, 3, 40000, "f32", "half0_half1", 31),           # K = 32, 2 chunks
     ("split-31-chunks", 1, 2, 600000, "bf16", "half0_half1", 9),    # the most chunks
     ("split-greedy", 2, 3, 40000, "bf16", "all0", 5),                # greedy only, 2 chunks
+    ("largest-vocab", 1, 2, 1048576, "bf16", "half0_half1", 31),    # V = 2^20, 31 chunks, F = 31
+    ("longest-draft", 2, 64, 20000, "f32", "all1", 6),               # gamma = 64
     ("split-tiny", 3, 2, 40, "f32", "all0.8", 7),
     ("batch-over-4096", 4100, 1, 64, "f32", "half0_half1", 3),   # sequences taken in index order
 ])

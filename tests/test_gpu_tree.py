@@ -43,6 +43,7 @@ def test_named_tree_workload():
     (3, 257, 3000, "bf16", "half0_half1", 8, 4, 0.5, 12),
     (2, 1500, 1000, "f32", "all1", 12, 6, 1.5, 13),
     (1, 4096, 600, "bf16", "all0.7", 14, 8, 1.5, 14),
+    (2, 12, 1048576, "bf16", "all1", 4, 3, 1.0, 15),      # V = 2^20: 16 walkers of 128 tiles
 ])
 def test_tree_shapes(B, N, V, dtype, temps, depth, branching, noise, seed):
     t = workloads.make_tree(B, N, V, depth=depth, branching=branching, dtype=dtype, sigma=3.0,
