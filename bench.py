@@ -90,31 +90,53 @@ def measured_traffic(kernel):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s=20.0):
+def cpu_baseline(w, budget_s=20.0, gpu=None):
     """The oracle, as written, on a bounded sample of the workload: whole
     sequences (verify + top-F), alternating greedy and sampled ones, until
-    the time budget is spent."""
+    the time budget is spent. With `gpu` (the fused step's outputs at the
+    workload's offset, on the host), the sampled sequences' outcomes are then
+    compared with the oracle's, outside the timed loop."""
     import oracle
 
     order = []
     half = w.B // 2
     for i in range(half):
         order += [i, half + i]
+    results = []
     t0 = time.perf_counter()
     done = 0
     for b in order:
         u, v = oracle.philox.chain_uniforms(w.seed, w.offset, b, w.gamma)
-        oracle.sampling.verify_sequence(w.target[b].astype(np.float64), w.draft[b].astype(np.float64),
-                                        w.draft_tokens[b], float(w.temperature[b]), u, v)
-        oracle.topf.bonus_topf_batch(w.draft[b:b + 1].astype(np.float64), w.draft_tokens[b:b + 1], w.F)
+        r = oracle.sampling.verify_sequence(w.target[b].astype(np.float64), w.draft[b].astype(np.float64),
+                                            w.draft_tokens[b], float(w.temperature[b]), u, v)
+        ids, _ = oracle.topf.bonus_topf_batch(w.draft[b:b + 1].astype(np.float64), w.draft_tokens[b:b + 1], w.F)
+        results.append((b, r, ids))
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     rows = done * (w.gamma + 1)
-    return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+    line = {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} of {w.B} sequences (alternating greedy / T=1), verify + top-F, "
                       f"{rows} rows in {dt:.1f} s, numpy fp64 on one host thread"}
+    if gpu is not None:
+        equal = near = differ = topf_equal = 0
+        for b, r, ids in results:
+            toks = np.full(w.gamma + 1, -1, np.int64)
+            toks[:len(r.tokens)] = r.tokens
+            same = int(gpu["num_accepted"][b]) == r.k and np.array_equal(gpu["tokens"][b], toks)
+            if r.near_tie:
+                near += 1
+            elif same:
+                equal += 1
+            else:
+                differ += 1
+            topf_equal += int(np.array_equal(gpu["topk"][b], ids[0]))
+        line["parity"] = {"sequences": len(results), "outcome_equal": equal, "near_ties": near,
+                          "outcome_differs": differ, "topf_equal": topf_equal,
+                          "note": "the fused step's outcome (k, tokens) and top-F ids against the oracle's on the "
+                                  "sampled sequences; near ties are decisions within 1e-6 of a tie"}
+    return line
 
 
 def main():
@@ -309,7 +331,10 @@ def main():
         "tree": tree,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        ref_out = binding.verify_topk(target, draft, tokens, temp, F, w.seed, w.offset)
+        torch.cuda.synchronize()
+        gpu = {k: ref_out[k].cpu().numpy() for k in ("tokens", "num_accepted", "topk")}
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, gpu)
     print(json.dumps(line), flush=True)
 
 
