@@ -77,7 +77,7 @@ struct ChainArgs {
 constexpr int kMaxWalkers = 16;
 constexpr int kMaxTreeNodes = 4096;  // SPECV_MAX_TREE_NODES
 // Tiles of one walker's share: ceil(tiles / H) with H = tree_walkers(V) is at
-// most 16 while tiles <= 256, and at most kMaxTiles / kMaxWalkers beyond.
+// most 32 while tiles <= 512, and at most kMaxTiles / kMaxWalkers beyond.
 constexpr int kMaxWalkTiles = kMaxTiles / kMaxWalkers;
 constexpr int kWalkWords = 3 * kMaxWalkers + 1;
 
@@ -184,13 +184,11 @@ inline int32_t cached_positions(int64_t D, int64_t row_bytes, int64_t positions)
     return int32_t(p < positions ? p : positions);
 }
 
-// Walkers per tree for a vocabulary of V: about 16 tiles each, at most
-// kMaxWalkers (a pass's time is mostly its share's arithmetic and one round
-// of loads; more walkers per tree measured 3 us faster for 1-4 trees of 64
-// nodes at V = 152064 and the same for 32).
+// Walkers per tree for a vocabulary of V: about 32 tiles each, at most
+// kMaxWalkers.
 inline int32_t tree_walkers(int64_t V) {
     const int64_t ntiles = (V + kTileElems - 1) / kTileElems;
-    const int64_t h = (ntiles + 15) / 16;
+    const int64_t h = (ntiles + 31) / 32;
     return int32_t(h < 1 ? 1 : h > kMaxWalkers ? kMaxWalkers : h);
 }
 

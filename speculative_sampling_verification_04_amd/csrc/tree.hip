@@ -43,7 +43,7 @@ namespace {
 constexpr int kU = 4;          // 16-byte steps per lane per iteration
 constexpr int kD = 0;          // prefetch form (see stream_chunk)
 constexpr int kWalkTiles = 8;       // tiles in flight per wave in a walk pass (walk launch)
-constexpr int kFusedWalkTiles = 5;  // the same in the one-launch form (a share of ~19 tiles in one round)
+constexpr int kFusedWalkTiles = 4;  // the same in the one-launch form
 
 __device__ __forceinline__ const void* row_ptr(const RowView& v, int esz, int64_t b, int64_t r) {
     return static_cast<const char*>(v.data) + (b * v.stride_seq + r * v.stride_row) * esz;
