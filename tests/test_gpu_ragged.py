@@ -81,6 +81,7 @@ def compare(gpu, ref, r, name):
     (300, 3, 2000, "bf16", "mixed", 4),
     (5, 0, 1000, "f32", "mixed", 6),          # no draft tokens at all: the bonus comes from p_t of row 0
     (2, 4, 1048576, "bf16", "mixed", 7),      # the largest vocabulary
+    (2, 0, 40000, "bf16", "mixed", 8),        # no drafts, rows in chunks
 ])
 def test_ragged_matches_oracle(B, G, V, dtype, temps, seed, with_draft):
     r = make_ragged(B, G, V, dtype, temps, seed)
