@@ -123,42 +123,6 @@ struct TopFArgs {
     float* out_logits;       // may be null
 };
 
-// Split of a row into chunks so that small batches still fill the GPU:
-// aim for ~2048 workgroups, never chunks shorter than 4096 elements.
-inline void choose_split(int64_t row_tasks, int64_t V, int32_t* S, int64_t* chunk) {
-    int64_t s = (2048 + row_tasks - 1) / row_tasks;
-    const int64_t by_len = V / 4096 > 0 ? V / 4096 : 1;
-    if (s > by_len) s = by_len;
-    if (s > 64) s = 64;
-    if (s < 1) s = 1;
-    int64_t c = (V + s - 1) / s;
-    c = (c + 7) / 8 * 8;
-    s = (V + c - 1) / c;
-    *S = int32_t(s);
-    *chunk = c;
-}
-
-// Chunks per row of the fused verify + top-F kernel (its 2 * gamma + 2 rows
-// per sequence), so that small batches still spread over the GPU. A draft-row
-// chunk's top-K workgroup is bound by its chain of round trips more than by
-// its bytes, so the split aims at ~1024 workgroups (not the ~2048 of
-// choose_split) with chunks of at least 16384 elements (one chunk per row
-// from ~57 sequences of gamma = 8 up), and at most kMaxTopfChunks so that a
-// row's chunk keys (kTopfKeyWords each) fit the merging workgroup's LDS.
-constexpr int kTopfKeyWords = 32;   // the largest F + 1
-constexpr int kMaxTopfChunks = 31;
-inline void small_split(int64_t rows, int64_t V, int32_t* S, int64_t* chunk) {
-    int64_t s = (1024 + rows - 1) / rows;
-    const int64_t by_len = V / 16384 > 0 ? V / 16384 : 1;
-    if (s > by_len) s = by_len;
-    if (s > kMaxTopfChunks) s = kMaxTopfChunks;
-    if (s < 1) s = 1;
-    int64_t c = (V + s - 1) / s;
-    c = (c + 7) / 8 * 8;
-    *chunk = c;
-    *S = int32_t((V + c - 1) / c);
-}
-
 // Workgroups that share the bonus draw of one T > 0 sequence: about 32 tiles
 // (16K elements of the row pair) each, at most 16. Batches of up to 64
 // sequences leave most of the GPU idle while the draws run, so there each

@@ -3,7 +3,10 @@
 // rows of its sequence and the H bonus workgroups of a sequence come in
 // order; in the fused order the T > 0 sequences' rows come first, the greedy
 // sequences' draft rows all come before their target rows, and the greedy
-// bonus workgroups come last. Prints "ok" or the first failure.
+// bonus workgroups come last. Also the row splits (choose_split,
+// small_split): chunks cover the row exactly once, are multiples of 8
+// elements, respect their minimum length and the count limits. Prints "ok"
+// or the first failure.
 #include <cstdio>
 #include <vector>
 
@@ -70,7 +73,29 @@ static int check(long B, long nS, long RS, long H, bool fused) {
     return 0;
 }
 
+// One split of a row of V elements for `rows` row tasks: S chunks of `chunk`
+// elements (the last one shorter) that cover [0, V) exactly.
+static int check_split(const char* name, long rows, long V, int32_t S, int64_t chunk, long max_s, long min_chunk,
+                       long target) {
+    const bool ok = S >= 1 && S <= max_s && chunk % 8 == 0 && int64_t(S) * chunk >= V &&
+                    int64_t(S - 1) * chunk < V && (S == 1 || chunk >= min_chunk) && rows * S <= target + rows;
+    if (!ok) std::printf("FAIL %s rows=%ld V=%ld S=%d chunk=%lld\n", name, rows, V, S, (long long)chunk);
+    return ok ? 0 : 1;
+}
+
 int main() {
+    const long rowss[] = {1, 2, 3, 5, 9, 17, 18, 100, 513, 1023, 1024, 1025, 2047, 2048, 2049, 5000, 100000};
+    const long Vs[] = {1, 2, 7, 8, 9, 4095, 4096, 4097, 8191, 16383, 16384, 16385, 32000, 128256, 152064, 600000,
+                       1048576};
+    for (long rows : rowss)
+        for (long V : Vs) {
+            int32_t S;
+            int64_t chunk;
+            specv::choose_split(rows, V, &S, &chunk);
+            if (check_split("choose_split", rows, V, S, chunk, 64, 4096, 2048)) return 1;
+            specv::small_split(rows, V, &S, &chunk);
+            if (check_split("small_split", rows, V, S, chunk, specv::kMaxTopfChunks, 16384, 1024)) return 1;
+        }
     const long Bs[] = {1, 2, 3, 7, 64, 91, 92, 256, 300};
     const long RSs[] = {2, 3, 17, 18, 34, 130};
     const long Hs[] = {1, 2, 8, 16};

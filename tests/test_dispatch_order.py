@@ -1,6 +1,8 @@
-"""The dispatch maps of the chain launches (csrc/specv_dispatch.hpp), checked
-on the CPU: bijections onto the tasks, bonus workgroups after their rows and in
-order, and the longest-first layout of the fused launch's greedy sequences."""
+"""The launch shapes of csrc/specv_dispatch.hpp, checked on the CPU: the
+dispatch maps of the chain launches (bijections onto the tasks, bonus
+workgroups after their rows and in order, the longest-first layout of the
+fused launch's greedy sequences) and the row splits (exact cover, chunk
+lengths, count limits)."""
 import os
 import shutil
 import subprocess
