@@ -145,3 +145,25 @@ def test_cache_unaligned_strided_rows():
     ref = oracle.ssd.verify_cached_batch(w.target.astype(np.float64), w.draft.astype(np.float64), w.draft_tokens,
                                          w.temperature, w.seed, 0, fan, C=0.5)
     assert check(gpu, ref, w, "cache unaligned") <= 2
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cache_random_shapes(seed):
+    # Seeded random batch, draft length, vocabulary, fan-out, C and lenience.
+    rng = np.random.default_rng(9900 + seed)
+    gamma = int(rng.integers(1, 9))
+    V = int(rng.integers(16384, 60001)) if rng.random() < 0.5 else int(rng.integers(40, 16384))
+    B = max(1, min(int(np.exp(rng.uniform(0.0, np.log(120)))), 1_200_000 // ((gamma + 1) * V)))
+    fan = tuple(int(f) for f in rng.integers(0, min(31, V - 1) + 1, gamma + 1))
+    if max(fan) == 0:
+        fan = (1,) + fan[1:]
+    C = float(rng.choice([1.0, 0.5, 0.2, float(rng.uniform(0.05, 1.0))]))
+    lenience = float(rng.choice([1.0, 0.8, float(rng.uniform(0.5, 1.0))]))
+    temps = ("half0_half1", "all1", "all0.7", "all0")[seed % 4]
+    w = workloads.make_chain(B, gamma, V, dtype="bf16" if seed % 2 else "f32", sigma=3.0, noise=1.0, temps=temps,
+                             gen_seed=9950 + seed, philox_seed=seed, F=max(fan))
+    w = saguaro_tokens(w, fan, C, seed=9990 + seed)
+    log(f"cache random {seed}: B={B} gamma={gamma} V={V} F={list(fan)} C={C:.3f} l={lenience:.3f} {temps}")
+    gpu, ref = run_case(w, fan, C, lenience)
+    assert check(gpu, ref, w, f"cache random {seed}") <= max(1, B // 10)
+

@@ -127,3 +127,21 @@ def test_ragged_bad_offsets_are_reported():
     for b in (0, 3):
         if not ref["near_tie"][b]:
             assert nacc[b] == ref["num_accepted"][b]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_ragged_random_shapes(seed):
+    # Seeded random batch size, maximum count, vocabulary, dtype and
+    # temperatures, with and without draft logits.
+    rng = np.random.default_rng(9700 + seed)
+    G = int(rng.integers(0, 17))
+    V = int(rng.integers(16384, 60001)) if rng.random() < 0.5 else int(np.exp(rng.uniform(0.0, np.log(16384))))
+    B = max(1, min(int(np.exp(rng.uniform(0.0, np.log(200)))), 1_200_000 // ((2 * G + 2) * V)))
+    dtype = "bf16" if seed % 2 else "f32"
+    temps = ("mixed", "1.0", "0.0", "0.7")[seed % 4]
+    r = make_ragged(B, G, V, dtype, temps, 9800 + seed)
+    for with_draft in (True, False):
+        log(f"ragged random {seed}: B={B} G={G} V={V} {dtype} T={temps} draft={with_draft}")
+        gpu, ref = run(r, with_draft)
+        assert compare(gpu, ref, r, f"ragged random {seed} draft={with_draft}") <= max(1, B // 10)
+
