@@ -2,12 +2,13 @@
 running the oracle on the same inputs, and comparing outcomes.
 
 Parity bar:
-* accept lengths, bonus tokens, tree paths and top-F ids: bit-exact, except
-  for sequences where the oracle reports a near tie (a threshold comparison
-  within 1e-6 of equality: |u - ratio| <= 1e-6, or v*W within 1e-6*W of a
-  bucket edge) or an ill-conditioned residual (mass below 1e-3, where fp32
-  rounding of p_t - p_d is large relative to the mass); those are counted and
-  reported, and must stay rare;
+* accept lengths, bonus tokens, tree paths and top-F ids: bit-exact. The one
+  allowance is a sequence where the oracle reports a near tie (a threshold
+  comparison within 1e-6 of equality: |u - ratio| <= 1e-6, or v*W within
+  1e-6*W of a bucket edge) or an ill-conditioned residual (mass below 1e-3,
+  where fp32 rounding of p_t - p_d is large relative to the mass): such a
+  sequence is still compared, and only if its outcome differs is it counted
+  as excused; excused sequences must stay rare;
 * p_t(x), p_d(x) and the bonus mass: within 1e-5 absolute.
 """
 import numpy as np
@@ -63,24 +64,40 @@ def run_chain_oracle(w, seqs=None):
     return {k: np.array(v) for k, v in res.items()}, seqs
 
 
+def chain_outcome_equal(gpu, ref, b, n):
+    return gpu["num_accepted"][b] == ref["num_accepted"][n] and np.array_equal(gpu["tokens"][b], ref["tokens"][n])
+
+
+def excused_bound(n):
+    """Near ties whose outcome may differ: at most a tenth of the batch (one
+    at small batches)."""
+    return max(1, n // 10)
+
+
 def compare_chain(gpu, ref, seqs, gamma, name):
-    """Asserts the parity bar; returns (compared, excluded)."""
-    excluded = []
+    """Asserts the parity bar; returns (matched, excused): excused sequences
+    are near ties (or ill-conditioned residuals) whose outcome differs."""
+    excused, near_equal = [], 0
     for n, b in enumerate(seqs):
         k = ref["num_accepted"][n]
         ill = k < gamma and ref["bonus_mass"][n] < ILL_MASS
         np.testing.assert_allclose(gpu["probs"][b], ref["probs"][n], atol=PROB_TOL,
                                    err_msg=f"{name}: probs of sequence {b}")
         if ref["near_tie"][n] or ill:
-            excluded.append(b)
+            if chain_outcome_equal(gpu, ref, b, n):
+                near_equal += 1
+            else:
+                excused.append(b)
             continue
         assert gpu["num_accepted"][b] == k, f"{name}: k of sequence {b}: {gpu['num_accepted'][b]} vs {k}"
         np.testing.assert_array_equal(gpu["tokens"][b], ref["tokens"][n],
                                       err_msg=f"{name}: tokens of sequence {b}")
         assert abs(gpu["bonus_mass"][b] - ref["bonus_mass"][n]) <= PROB_TOL, \
             f"{name}: bonus mass of sequence {b}: {gpu['bonus_mass'][b]} vs {ref['bonus_mass'][n]}"
-    log(f"{name}: {len(seqs) - len(excluded)} sequences bit-exact, {len(excluded)} near ties excluded {excluded}")
-    return len(seqs) - len(excluded), len(excluded)
+    log(f"{name}: {len(seqs) - len(excused)} sequences bit-exact ({near_equal} of them near ties), "
+        f"{len(excused)} near ties differ {excused}")
+    assert len(excused) <= excused_bound(len(seqs)), f"{name}: {len(excused)} near ties differ"
+    return len(seqs) - len(excused), len(excused)
 
 
 def run_topf_gpu(draft_dev, tokens_dev, F):
@@ -122,13 +139,22 @@ def run_tree_oracle(t, seqs=None):
 
 
 def compare_tree(gpu, ref, seqs, name):
-    excluded = []
+    """Asserts the parity bar; returns (matched, excused): excused trees are
+    near ties whose outcome differs."""
+    excused, near_equal = [], 0
     for n, b in enumerate(seqs):
         if ref["near_tie"][n]:
-            excluded.append(b)
+            same = (np.array_equal(gpu["path"][b], ref["path"][n]) and gpu["num_accepted"][b] == ref["num_accepted"][n]
+                    and gpu["bonus"][b] == ref["bonus"][n])
+            if same:
+                near_equal += 1
+            else:
+                excused.append(b)
             continue
         np.testing.assert_array_equal(gpu["path"][b], ref["path"][n], err_msg=f"{name}: path of tree {b}")
         assert gpu["num_accepted"][b] == ref["num_accepted"][n], f"{name}: accepted of tree {b}"
         assert gpu["bonus"][b] == ref["bonus"][n], f"{name}: bonus of tree {b}: {gpu['bonus'][b]} vs {ref['bonus'][n]}"
-    log(f"{name}: {len(seqs) - len(excluded)} trees bit-exact, {len(excluded)} near ties excluded {excluded}")
-    return len(seqs) - len(excluded), len(excluded)
+    log(f"{name}: {len(seqs) - len(excused)} trees bit-exact ({near_equal} of them near ties), "
+        f"{len(excused)} near ties differ {excused}")
+    assert len(excused) <= excused_bound(len(seqs)), f"{name}: {len(excused)} near ties differ"
+    return len(seqs) - len(excused), len(excused)

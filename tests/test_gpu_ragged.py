@@ -56,21 +56,27 @@ def run(r, with_draft):
 
 
 def compare(gpu, ref, r, name):
-    bad = []
+    """Parity bar of the chain tests: every sequence compared; a near tie (or an
+    ill-conditioned residual) whose outcome differs is excused, and counted."""
+    excused, near_equal = [], 0
     for b in range(r["B"]):
         o0, o1 = r["offsets"][b], r["offsets"][b + 1]
         np.testing.assert_allclose(gpu["probs"][o0:o1], ref["probs"][o0:o1], atol=PROB_TOL,
                                    err_msg=f"{name}: probs of sequence {b}")
         k = ref["num_accepted"][b]
+        same = gpu["num_accepted"][b] == k and np.array_equal(gpu["tokens"][b], ref["tokens"][b])
         if ref["near_tie"][b] or (k < o1 - o0 and ref["bonus_mass"][b] < ILL_MASS):
-            bad.append(b)
+            if same:
+                near_equal += 1
+            else:
+                excused.append(b)
             continue
         assert gpu["num_accepted"][b] == k, f"{name}: k of sequence {b}"
         np.testing.assert_array_equal(gpu["tokens"][b], ref["tokens"][b], err_msg=f"{name}: tokens of {b}")
         assert abs(gpu["bonus_mass"][b] - ref["bonus_mass"][b]) <= PROB_TOL
-    log(f"{name}: {r['B'] - len(bad)} sequences bit-exact, {len(bad)} near ties {bad}, "
-        f"mean accepted {ref['num_accepted'].mean():.2f}")
-    return len(bad)
+    log(f"{name}: {r['B'] - len(excused)} sequences bit-exact ({near_equal} of them near ties), "
+        f"{len(excused)} near ties differ {excused}, mean accepted {ref['num_accepted'].mean():.2f}")
+    return len(excused)
 
 
 @pytest.mark.parametrize("with_draft", [True, False])
