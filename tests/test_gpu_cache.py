@@ -79,6 +79,7 @@ CASES = [
     # small batches: rows in chunks, cache words published by the bonus workgroups
     ("small-batch-chunks", 2, 5, 70000, "bf16", "half0_half1", (6, 5, 4, 3, 2, 2), 0.3, 0.9),   # 4 chunks
     ("one-greedy-sequence", 1, 3, 40000, "f32", "all0", (3, 3, 3, 3), 0.5, 1.0),               # 2 chunks
+    ("batch-over-4096", 4200, 2, 64, "bf16", "half0_half1", (3, 2, 2), 0.5, 0.9),   # index order
     ("max-fanout-chunks", 2, 2, 50000, "bf16", "all1", (31, 31, 20), 0.6, 1.0),                 # 3 chunks
     ("zero-fanout-chunks", 2, 3, 40000, "bf16", "all1", (2, 0, 3, 1), 0.5, 0.9),                # F_k = 0, 2 chunks
 ]

@@ -88,6 +88,7 @@ def compare(gpu, ref, r, name):
     (5, 0, 1000, "f32", "mixed", 6),          # no draft tokens at all: the bonus comes from p_t of row 0
     (2, 4, 1048576, "bf16", "mixed", 7),      # the largest vocabulary
     (2, 0, 40000, "bf16", "mixed", 8),        # no drafts, rows in chunks
+    (4200, 3, 64, "f32", "mixed", 9),         # more than 4096 sequences: taken in index order
 ])
 def test_ragged_matches_oracle(B, G, V, dtype, temps, seed, with_draft):
     r = make_ragged(B, G, V, dtype, temps, seed)

@@ -44,6 +44,7 @@ def test_named_tree_workload():
     (2, 1500, 1000, "f32", "all1", 12, 6, 1.5, 13),
     (1, 4096, 600, "bf16", "all0.7", 14, 8, 1.5, 14),
     (2, 12, 1048576, "bf16", "all1", 4, 3, 1.0, 15),      # V = 2^20: 16 walkers of 128 tiles
+    (4200, 6, 40, "f32", "half0_half1", 2, 4, 1.0, 16),   # more than 4096 trees: taken in index order
 ])
 def test_tree_shapes(B, N, V, dtype, temps, depth, branching, noise, seed):
     t = workloads.make_tree(B, N, V, depth=depth, branching=branching, dtype=dtype, sigma=3.0,
