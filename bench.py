@@ -218,10 +218,16 @@ def main():
     mean_accepted = float(out["num_accepted"].float().mean().item())
 
     # Reference: the two entry points run separately (not part of the step).
-    def timed(fn, n=20):
+    def timed(fn, n=50):
+        # Same settle as the step: building each line's inputs leaves the GPU
+        # idle for seconds, and the first calls after that run at low clocks.
+        t_s, i = time.perf_counter(), 0
+        while time.perf_counter() - t_s < SETTLE_S / 2:
+            for _ in range(10):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
-        for i in range(3):
-            fn(i)
         for i in range(n):
             ev[i][0].record()
             fn(i)
