@@ -86,7 +86,7 @@ def kernel_source_hash():
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
-    path = os.path.join(PROFILES, "hbm_traffic.json")
+    path = os.path.join(PROFILES, "bench_kernels_v128256_b256_g8_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     try:
