@@ -130,43 +130,56 @@ def _int32(t, shape, name):
 
 
 class _WorkspaceCache:
-    """One zero-filled workspace per device, grown on demand. The kernels leave
-    it zero-filled, so calls ordered on one stream can share it."""
+    """Default workspaces: one zero-filled buffer per (device, stream), grown
+    on demand. Calls that share a stream are ordered, and the kernels return
+    the words they consume to zero, so those calls can share one buffer;
+    calls on different streams may overlap and get separate buffers. Every
+    call tags what it publishes with its own epoch, so words that a call whose
+    bounded wait ran out left behind are never taken for the next call's."""
 
     def __init__(self):
         self._bufs = {}
+        self._lock = threading.Lock()
 
     def get(self, nbytes, device):
-        key = torch.device(device)
-        buf = self._bufs.get(key)
-        if buf is None or buf.numel() < nbytes:
-            buf = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
-            self._bufs[key] = buf
-        return buf
+        dev = torch.device(device)
+        key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device(),
+               torch.cuda.current_stream(dev).cuda_stream)
+        with self._lock:
+            buf = self._bufs.get(key)
+            if buf is None or buf.numel() < nbytes:
+                buf = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
+                self._bufs[key] = buf
+            return buf
 
 
 _workspaces = _WorkspaceCache()
+_sizes = {}
+
+
+def _size(fn_name, *args):
+    """A workspace-size query of the library, cached per shape (the sizes are
+    plain functions of the shape)."""
+    key = (fn_name,) + args
+    n = _sizes.get(key)
+    if n is None:
+        lib = load_library()
+        out = ctypes.c_size_t(0)
+        _check(getattr(lib, fn_name)(*args, ctypes.byref(out)))
+        n = _sizes[key] = out.value
+    return n
 
 
 def verify_workspace_bytes(batch, gamma, vocab):
-    lib = load_library()
-    n = ctypes.c_size_t(0)
-    _check(lib.specv_verify_workspace_size(batch, gamma, vocab, ctypes.byref(n)))
-    return n.value
+    return _size("specv_verify_workspace_size", int(batch), int(gamma), int(vocab))
 
 
 def verify_topk_workspace_bytes(batch, gamma, vocab):
-    lib = load_library()
-    n = ctypes.c_size_t(0)
-    _check(lib.specv_verify_topk_workspace_size(batch, gamma, vocab, ctypes.byref(n)))
-    return n.value
+    return _size("specv_verify_topk_workspace_size", int(batch), int(gamma), int(vocab))
 
 
 def tree_workspace_bytes(batch, nodes, vocab):
-    lib = load_library()
-    n = ctypes.c_size_t(0)
-    _check(lib.specv_tree_verify_workspace_size(batch, nodes, vocab, ctypes.byref(n)))
-    return n.value
+    return _size("specv_tree_verify_workspace_size", int(batch), int(nodes), int(vocab))
 
 
 def verify(target, draft, draft_tokens, temperature, seed, offset=0, *,
@@ -232,10 +245,7 @@ def verify_topk(target, draft, draft_tokens, temperature, F, seed, offset=0, *,
 
 
 def verify_cache_workspace_bytes(batch, gamma, vocab):
-    lib = load_library()
-    n = ctypes.c_size_t()
-    _check(lib.specv_verify_cache_workspace_size(batch, gamma, vocab, ctypes.byref(n)))
-    return n.value
+    return _size("specv_verify_cache_workspace_size", int(batch), int(gamma), int(vocab))
 
 
 def verify_cache(target, draft, draft_tokens, temperature, fanout, seed, offset=0, *, saguaro_C=1.0,
@@ -279,10 +289,7 @@ def verify_cache(target, draft, draft_tokens, temperature, fanout, seed, offset=
 
 
 def verify_ragged_workspace_bytes(batch, max_gamma, vocab, has_draft=True):
-    lib = load_library()
-    n = ctypes.c_size_t()
-    _check(lib.specv_verify_ragged_workspace_size(batch, max_gamma, vocab, int(has_draft), ctypes.byref(n)))
-    return n.value
+    return _size("specv_verify_ragged_workspace_size", int(batch), int(max_gamma), int(vocab), int(bool(has_draft)))
 
 
 def packed_view(t):

@@ -40,13 +40,13 @@ __global__ __launch_bounds__(kThreads) void ragged_verify_kernel(ChainArgs a) {
     const int32_t o0 = a.offsets[b], o1 = a.offsets[b + 1];
     const bool valid = o0 >= 0 && o0 <= o1 && o1 <= a.num_draft && o1 - o0 <= G;
     const int gb = valid ? o1 - o0 : 0;
-    uint64_t* slots = a.slots + int64_t(sidx) * RS;
+    uint64_t* slots = a.slots + 2 * int64_t(sidx) * RS;
 
     if (w >= RS) {  // bonus workgroup
         const int h = int(w - RS);
         if (!valid) {
             if (h == a.H - 1) {
-                if (wait_slots(slots, RS, a.wait_ticks)) zero_slots(slots, RS);
+                if (wait_pairs(slots, RS, a.epoch, a.wait_ticks)) zero_pairs(slots, RS);
                 for (int j = threadIdx.x; j <= G; j += kThreads) a.out_tokens[int64_t(b) * (G + 1) + j] = -1;
                 if (threadIdx.x == 0) a.out_nacc[b] = -2;
             }
@@ -65,7 +65,8 @@ __global__ __launch_bounds__(kThreads) void ragged_verify_kernel(ChainArgs a) {
         q.out_len = G + 1;
         q.out_probs = a.out_probs ? a.out_probs + int64_t(o0) * 2 : nullptr;
         __shared__ ResolveLds lds;
-        chain_resolve<DT, NoDraft>(a, q, T, slots, RS, a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, h, lds);
+        chain_resolve<DT, NoDraft>(a, q, T, slots, RS, a.tiles ? a.tiles + 4 * int64_t(sidx) * a.ntiles : nullptr,
+                                   a.parts ? a.parts + 4 * int64_t(sidx) * a.H : nullptr, h, lds);
         return;
     }
 
@@ -93,14 +94,15 @@ __global__ __launch_bounds__(kThreads) void ragged_verify_kernel(ChainArgs a) {
             word = pack_softmax(acc.m, acc.s);
         }
     }
-    if (threadIdx.x == 0) publish(slots + w, word);
+    if (threadIdx.x == 0) publish_pair(slots + 2 * w, word, a.epoch);
 }
 
 template <int DT, bool NoDraft>
 hipError_t launch_dt(const ChainArgs& a, hipStream_t stream) {
     const int64_t R = NoDraft ? a.gamma + 1 : 2 * a.gamma + 1;
     const int64_t grid = int64_t(a.B) * (R * a.S + a.H);
-    hipLaunchKernelGGL((ragged_verify_kernel<DT, NoDraft>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((ragged_verify_kernel<DT, NoDraft>), dim3(unsigned(grid)), dim3(kThreads),
+                       tile_lds_bytes(a.ntiles), stream, a);
     return hipGetLastError();
 }
 

@@ -39,6 +39,19 @@ specv_status ok() {
 std::atomic<uint64_t> g_wait_ticks{kMaxWaitTicks};
 uint64_t wait_ticks() { return g_wait_ticks.load(std::memory_order_relaxed); }
 
+// Every call tags the values its workgroups publish with a new epoch, so a
+// word left in a workspace by an earlier call (a writer that published after
+// its reader's bounded wait gave up) never reads as published. Epochs skip
+// values whose low 16 bits are 0 (the tree's pass tags keep those bits).
+std::atomic<uint32_t> g_epoch{0};
+uint32_t next_epoch() {
+    uint32_t e;
+    do {
+        e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    } while ((e & 0xffffu) == 0);
+    return e;
+}
+
 int elem_size(int32_t dtype) { return dtype == SPECV_BF16 ? 2 : 4; }
 
 constexpr size_t kAlign = 256;
@@ -73,9 +86,11 @@ specv_status check_workspace(void* ws, size_t have, size_t need) {
 
 RowView view(const specv_logits& l) { return RowView{l.data, l.stride_seq, l.stride_row}; }
 
-// Workspace: one 64-bit word per row chunk (its statistics), then, when the
-// bonus draw is shared by H > 1 workgroups, one word per residual tile of
-// every sequence.
+// Workspace (every value a tagged pair of 64-bit words, kPair bytes): one
+// pair per row chunk (its statistics); then, when the bonus draw is shared by
+// H > 1 workgroups, two pairs per residual tile of every sequence (the tile's
+// sums of w~ and q~) and two per bonus workgroup (its correction sums).
+constexpr size_t kPair = 2 * sizeof(uint64_t);
 struct Layout {
     int32_t S;
     int64_t chunk;
@@ -83,8 +98,9 @@ struct Layout {
     int32_t ntiles;
     size_t slot_bytes;
     size_t tile_bytes;
+    size_t part_bytes;
     size_t key_bytes = 0;    // fused kernel with S > 1: the draft-row chunks' top-F keys
-    size_t total() const { return slot_bytes + tile_bytes + key_bytes; }
+    size_t total() const { return slot_bytes + tile_bytes + part_bytes + key_bytes; }
 };
 
 Layout layout_for(int64_t batch, int64_t row_tasks_per_seq, int64_t vocab) {
@@ -92,8 +108,9 @@ Layout layout_for(int64_t batch, int64_t row_tasks_per_seq, int64_t vocab) {
     choose_split(batch * row_tasks_per_seq, vocab, &L.S, &L.chunk);
     L.H = bonus_helpers(vocab, batch);
     L.ntiles = int32_t((vocab + kTileElems - 1) / kTileElems);
-    L.slot_bytes = round_up(size_t(batch) * row_tasks_per_seq * L.S * sizeof(uint64_t));
-    L.tile_bytes = L.H > 1 ? round_up(size_t(batch) * L.ntiles * sizeof(uint64_t)) : 0;
+    L.slot_bytes = round_up(size_t(batch) * row_tasks_per_seq * L.S * kPair);
+    L.tile_bytes = L.H > 1 ? round_up(size_t(batch) * L.ntiles * 2 * kPair) : 0;
+    L.part_bytes = L.H > 1 ? round_up(size_t(batch) * L.H * 2 * kPair) : 0;
     return L;
 }
 
@@ -103,9 +120,9 @@ Layout layout_for(int64_t batch, int64_t row_tasks_per_seq, int64_t vocab) {
 Layout fused_layout(int64_t batch, int64_t gamma, int64_t vocab, bool cache_words = false) {
     Layout L = layout_for(batch, 2 * gamma + 2, vocab);
     small_split(batch * (2 * gamma + 2), vocab, &L.S, &L.chunk);
-    const int64_t words = (2 * gamma + 2) * L.S + (cache_words ? 3 * (gamma + 1) : 0);
-    L.slot_bytes = round_up(size_t(batch) * words * sizeof(uint64_t));
-    L.key_bytes = L.S > 1 ? round_up(size_t(batch) * (gamma + 1) * L.S * kTopfKeyWords * sizeof(uint64_t)) : 0;
+    const int64_t pairs = (2 * gamma + 2) * L.S + (cache_words ? 3 * (gamma + 1) : 0);
+    L.slot_bytes = round_up(size_t(batch) * pairs * kPair);
+    L.key_bytes = L.S > 1 ? round_up(size_t(batch) * (gamma + 1) * L.S * kTopfKeyWords * kPair) : 0;
     return L;
 }
 
@@ -126,8 +143,11 @@ void set_bonus(ChainArgs& a, const Layout& L, int64_t row_words, void* workspace
     a.chunk = L.chunk;
     a.H = L.H;
     a.ntiles = L.ntiles;
-    a.slots = static_cast<uint64_t*>(workspace);
-    a.tiles = L.H > 1 ? reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.slot_bytes) : nullptr;
+    char* ws = static_cast<char*>(workspace);
+    a.slots = reinterpret_cast<uint64_t*>(ws);
+    a.tiles = L.H > 1 ? reinterpret_cast<uint64_t*>(ws + L.slot_bytes) : nullptr;
+    a.parts = L.H > 1 ? reinterpret_cast<uint64_t*>(ws + L.slot_bytes + L.tile_bytes) : nullptr;
+    a.epoch = next_epoch();
 }
 
 specv_status check_chain_sizes(int32_t batch, int32_t gamma, int32_t vocab) {
@@ -143,8 +163,8 @@ size_t verify_topk_bytes(int64_t batch, int64_t gamma, int64_t vocab) {
     return fused_layout(batch, gamma, vocab).total();
 }
 
-// Tree workspace: the row words, then per tree the walk words (the walkers'
-// pass totals, acknowledgements, the drawn token).
+// Tree workspace: the row pairs, then per tree the walk words (the walkers'
+// pass messages, acknowledgements, the drawn token).
 size_t tree_walk_offset(int64_t batch, int64_t nodes, int64_t vocab) {
     return layout_for(batch, 2 * nodes, vocab).slot_bytes;
 }
@@ -300,7 +320,9 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
     a.gamma = gamma;
     a.V = vocab;
     set_bonus(a, L, (2 * int64_t(gamma) + 2) * L.S, workspace, elem_size(target.dtype));
-    if (L.S > 1) a.topf_keys = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.slot_bytes + L.tile_bytes);
+    if (L.S > 1)
+        a.topf_keys = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.slot_bytes + L.tile_bytes +
+                                                  L.part_bytes);
     a.seed = seed;
     a.offset = offset;
     a.out_tokens = out_tokens;
@@ -367,7 +389,9 @@ specv_status specv_verify_cache(specv_logits target, specv_logits draft, const i
     a.gamma = gamma;
     a.V = vocab;
     set_bonus(a, L, (2 * int64_t(gamma) + 2) * L.S, workspace, elem_size(target.dtype));
-    if (L.S > 1) a.topf_keys = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.slot_bytes + L.tile_bytes);
+    if (L.S > 1)
+        a.topf_keys = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.slot_bytes + L.tile_bytes +
+                                                  L.part_bytes);
     a.seed = seed;
     a.offset = offset;
     a.out_tokens = out_tokens;
@@ -545,6 +569,7 @@ specv_status specv_tree_verify(specv_logits target, specv_logits draft, const in
     a.D = tree_fused(nodes) ? bonus_delay(batch, 2 * int64_t(nodes) * L.S) : 0;
     a.cache_nodes = cached_positions(batch, int64_t(vocab) * elem_size(target.dtype), nodes);
     a.walk = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + tree_walk_offset(batch, nodes, vocab));
+    a.epoch = next_epoch();
     const hipError_t e = launch_tree(a, target.dtype == SPECV_BF16 ? DT_BF16 : DT_F32,
                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_tree_verify launch failed: %s", hipGetErrorString(e));

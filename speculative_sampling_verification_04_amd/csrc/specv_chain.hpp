@@ -70,53 +70,77 @@ __device__ __forceinline__ SeqView dense_seq(const ChainArgs& a, int b) {
 }
 
 // LDS of one bonus workgroup. A kernel whose row workgroups need LDS of their
-// own may overlay the two (a workgroup is one or the other).
+// own may overlay the two (a workgroup is one or the other). The tile sums
+// live in the launch's dynamic LDS (TileLds), sized by the vocabulary.
 struct ResolveLds {
     RowStats st[2 * 64 + 1];
-    float tile_sum[kMaxTiles];
 };
 
-// Bonus workgroup h of a sequence. slots: the sequence's nslots words (row r
-// chunk j at r * S + j: target row r for r <= G, draft row r - G - 1 after
-// that; then, with a.cache_words, three cache words per draft row from word
-// 2G + 2). tiles: its ntiles tile words (used when H > 1). NoDraft: the draft
-// has no probabilities (q is the point mass at the drafted token). Cache: the
-// cache words exist (a.cache_words; specv_verify_cache only).
+// Per-tile sums of the bonus pass in dynamic LDS: w (fp64, the corrected
+// tile sums in the end) and q (the residual's second term, fp32: it only
+// carries the correction, ~1e-7 of a tile, so its own rounding is
+// immaterial).
+struct TileLds {
+    double* w;
+    float* q;
+};
+
+extern __shared__ __align__(16) char specv_dyn_lds[];
+
+// The dynamic LDS bytes a chain launch needs for `ntiles` tiles.
+inline size_t tile_lds_bytes(int64_t ntiles) { return size_t(ntiles) * (sizeof(double) + sizeof(float)) + 16; }
+
+__device__ __forceinline__ TileLds tile_lds(int ntiles) {
+    double* w = reinterpret_cast<double*>(specv_dyn_lds);
+    return TileLds{w, reinterpret_cast<float*>(w + ntiles)};
+}
+
+// Bonus workgroup h of a sequence. slots: the sequence's nslots pairs (row r
+// chunk j at pair r * S + j: target row r for r <= G, draft row r - G - 1
+// after that; then, with a.cache_words, three cache pairs per draft row from
+// pair (2G + 2) * S). tiles: its tile pairs (two per tile: the sums of w~ and
+// q~) and parts: its helpers' pairs (two per helper: sum p and sum p (2^h -
+// 1)), used when H > 1. NoDraft: the draft has no probabilities (q is the
+// point mass at the drafted token). Cache: the cache pairs exist
+// (a.cache_words; specv_verify_cache only).
 template <int DT, bool NoDraft = false, bool Cache = false>
 __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView& q, float T, uint64_t* slots,
-                                              int64_t nslots, uint64_t* tiles, int h, ResolveLds& lds) {
+                                              int64_t nslots, uint64_t* tiles, uint64_t* parts, int h,
+                                              ResolveLds& lds) {
     const int b = q.b;
     const int gamma = q.gamma;
     const int G = q.G;
-    const int R = NoDraft ? G + 1 : 2 * G + 1;   // row words to merge
+    const int R = NoDraft ? G + 1 : 2 * G + 1;   // rows to merge
     const bool greedy = !(T > 0.0f);
     const bool last = h == a.H - 1;
     const float c = greedy ? 0.0f : log2e_over(T);
-    const uint64_t* extra = slots + int64_t(2 * G + 2) * a.S;  // the cache words, when a.cache_words
+    const uint32_t ep = a.epoch;
+    const uint64_t* extra = slots + 2 * int64_t(2 * G + 2) * a.S;  // the cache pairs, when a.cache_words
 
     if (greedy && !last) return;  // the greedy bonus is an argmax: nothing to share
 
     RowStats* st = lds.st;
-    float* tile_sum = lds.tile_sum;
+    const int ntiles = int((int64_t(a.V) + kTileElems - 1) / kTileElems);
+    const TileLds tl = tile_lds(ntiles);
     __shared__ int32_t s_k;
     __shared__ int32_t s_bonus;
     __shared__ float s_mass;
     __shared__ uint64_t s_cache_word;
 
-    if (!wait_slots(slots, nslots, a.wait_ticks)) {  // never expected: see wait_slots
+    if (!wait_pairs(slots, nslots, ep, a.wait_ticks)) {  // never expected: see wait_pairs
         if (last) {
             if (threadIdx.x == 0) a.out_nacc[b] = -1;
-            zero_slots(slots, nslots);
+            zero_pairs(slots, nslots);
         }
         return;
     }
-    // One word per row: thread r reads row r's. Several: row r's S chunk
-    // words are merged by one wave, four rows per wave at a time, with all
+    // One value per row: thread r reads row r's. Several: row r's S chunk
+    // values are merged by one wave, four rows per wave at a time, with all
     // their loads in flight together.
     constexpr int kRowsPerStep = 4;
     if (a.S == 1) {
         for (int r = threadIdx.x; r < R; r += kThreads)
-            st[r] = (greedy && r > G) ? RowStats{-INFINITY, -INFINITY, -1, 0.0} : stats_of_word(peek(slots + r), greedy, c);
+            st[r] = (greedy && r > G) ? RowStats{-INFINITY, -INFINITY, -1, 0.0} : stats_of_word(read_pair(slots, r), greedy, c);
     }
     for (int r0 = wave_id(); a.S > 1 && r0 < R; r0 += kRowsPerStep * kWaves) {
         uint64_t wv[kRowsPerStep];
@@ -124,7 +148,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
         for (int j = 0; j < kRowsPerStep; ++j) {
             const int r = r0 + j * kWaves;
             const bool need = r < R && !(greedy && r > G) && lane_id() < a.S;
-            wv[j] = need ? peek(slots + int64_t(r) * a.S + lane_id()) : 0ull;
+            wv[j] = need ? read_pair(slots, int64_t(r) * a.S + lane_id()) : 0ull;
         }
 #pragma unroll
         for (int j = 0; j < kRowsPerStep; ++j) {
@@ -160,10 +184,10 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
                         RowStats qs = st[G + 1 + i];
                         double scale = 1.0;
                         if (Cache) {  // Saguaro sampling: q = sigma_{F_i,C}(draft_i / T)
-                            const uint64_t zw = peek(extra + 3 * i);
+                            const uint64_t zw = read_pair(extra, 3 * i);
                             if ((zw >> 32) == 1ull) {
                                 qs.Z = double(__uint_as_float(uint32_t(zw)));
-                                if (full_key(zd, x) + 1ull >= peek(extra + 3 * i + 1)) scale = double(a.C);
+                                if (full_key(zd, x) >= read_pair(extra, 3 * i + 1)) scale = double(a.C);
                             }
                         }
                         pd = scale * prob_of(zd, c, qs);
@@ -188,75 +212,112 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
     if (greedy) {
         if (threadIdx.x == 0) { s_bonus = st[k].idx; s_mass = 1.0f; }
     } else {
-        const int ntiles = int((int64_t(a.V) + kTileElems - 1) / kTileElems);
         const float v = stream_uniform(a.seed, a.offset, uint32_t(b), 0u, uint32_t(gamma));
-        const void* trow = q.target(k);
-        using Resid = typename std::conditional<NoDraft, ExcludeWeights<DT>, ResidualWeights<DT, Cache>>::type;
-        Resid res;
+        // The bonus weights: the residual of row k (corrected, see
+        // specv_sample.hpp), p_t of row k without the drafted token (no draft
+        // probabilities), or p_t of row gamma when every draft was accepted.
+        const bool resid = k < gamma && !NoDraft;
         TargetWeights<DT> tgt;
-        tgt.p.init(trow, c, st[k]);
-        tgt.V = a.V;
-        res.p = tgt.p;
-        res.V = a.V;
-        if constexpr (NoDraft) {
-            res.x = k < gamma ? q.tokens[k] : -1;
-        } else {
-            res.coef = 1.0f;
-            if (k < gamma) {
-                RowStats qs = st[G + 1 + k];
-                uint64_t top_word = 0ull;
+        tgt.init(q.target(k), c, st[k], a.V, (NoDraft && k < gamma) ? int64_t(q.tokens[k]) : int64_t(-1));
+        ResidualWeights<DT, Cache> res;
+        if (resid) {
+            if constexpr (!NoDraft) {
+                const RowStats& qs = st[G + 1 + k];
+                double Bq = log2_norm(qs);
+                uint64_t top_key = ~0ull;
                 if (Cache) {
-                    const uint64_t zw = peek(extra + 3 * k);
+                    const uint64_t zw = read_pair(extra, 3 * k);
                     if ((zw >> 32) == 1ull) {
-                        qs.Z = double(__uint_as_float(uint32_t(zw)));
-                        top_word = peek(extra + 3 * k + 1);
+                        Bq = double(qs.mc) + log2(double(__uint_as_float(uint32_t(zw))));
+                        top_key = read_pair(extra, 3 * k + 1);
                     }
                 }
-                res.q.init(q.draft(k), c, qs);
-                res.q.scale = a.C;
-                res.q.top_word = top_word;
+                res.init(q.target(k), q.draft(k), c, st[k], Bq, 1.0, a.V);
+                res.top_key = top_key;
+                res.log2C = log2(double(a.C));
             }
         }
 
-        // Tile sums of the bonus weights: residual of row k, or p_t of row gamma.
+        // Pass A: the tile sums (this workgroup's share when H > 1) and the
+        // correction sums.
+        double ps = 0.0, pgs = 0.0;
+        const int lo = a.H > 1 ? int(int64_t(ntiles) * h / a.H) : 0;
+        const int hi = a.H > 1 ? int(int64_t(ntiles) * (h + 1) / a.H) : ntiles;
         if (a.H > 1) {
-            const int lo = int(int64_t(ntiles) * h / a.H);
-            const int hi = int(int64_t(ntiles) * (h + 1) / a.H);
-            auto put = [&](int t, float ts) { publish(tiles + t, pack_tile(ts)); };
-            if (k < gamma) weight_tile_range<kBonusTiles>(res, lo, hi, put);
-            else weight_tile_range<kBonusTiles>(tgt, lo, hi, put);
-            // Each helper read the row words before publishing its tiles, so
-            // once every tile word is seen the row words may be zeroed.
+            auto put = [&](int t, double tw, double tq) {
+                publish_pair(tiles + 4 * t, pack_f64(tw), ep);
+                publish_pair(tiles + 4 * t + 2, pack_f64(tq), ep);
+            };
+            if (resid) weight_tile_range<kBonusTiles>(res, lo, hi, put, ps, pgs);
+            else weight_tile_range<kBonusTiles>(tgt, lo, hi, put, ps, pgs);
+        } else {
+            auto put = [&](int t, double tw, double tq) { tl.w[t] = tw; tl.q[t] = float(tq); };
+            if (resid) weight_tile_range<kBonusTiles>(res, lo, hi, put, ps, pgs);
+            else weight_tile_range<kBonusTiles>(tgt, lo, hi, put, ps, pgs);
+        }
+        if (resid) block_sum2(ps, pgs);
+        if (a.H > 1) {
+            if (resid && threadIdx.x == 0) {
+                publish_pair(parts + 4 * h, pack_f64(ps), ep);
+                publish_pair(parts + 4 * h + 2, pack_f64(pgs), ep);
+            }
+            // Each helper read the row values before publishing its tiles, so
+            // once every tile pair is seen the row pairs may be zeroed.
             if (!last) return;
-            if (!wait_slots(tiles, ntiles, a.wait_ticks)) {
+            const bool ok = wait_pairs(tiles, 2 * int64_t(ntiles), ep, a.wait_ticks) &&
+                            (!resid || wait_pairs(parts, 2 * int64_t(a.H), ep, a.wait_ticks));
+            if (!ok) {
                 if (threadIdx.x == 0) a.out_nacc[b] = -1;
-                zero_slots(tiles, ntiles);
-                zero_slots(slots, nslots);
+                zero_pairs(tiles, 2 * int64_t(ntiles));
+                zero_pairs(parts, 2 * int64_t(a.H));
+                zero_pairs(slots, nslots);
                 return;
             }
-            for (int t = threadIdx.x; t < ntiles; t += kThreads) tile_sum[t] = tile_of(peek(tiles + t));
-            zero_slots(tiles, ntiles);
+            if (resid) {  // the helpers' correction sums, in helper order
+                ps = 0.0;
+                pgs = 0.0;
+                for (int j = 0; j < a.H; ++j) {
+                    ps += unpack_f64(read_pair(parts, 2 * j));
+                    pgs += unpack_f64(read_pair(parts, 2 * j + 1));
+                }
+            }
+            const double ca = resid ? correction_a(correction_kappa(ps, pgs)) : 0.0;
+            for (int t = threadIdx.x; t < ntiles; t += kThreads)
+                tl.w[t] = unpack_f64(read_pair(tiles, 2 * t)) + ca * unpack_f64(read_pair(tiles, 2 * t + 1));
+            __syncthreads();
+            zero_pairs(tiles, 2 * int64_t(ntiles));
+            if (resid) zero_pairs(parts, 2 * int64_t(a.H));
+            res.a = float(ca);
         } else {
-            auto put = [&](int t, float ts) { tile_sum[t] = ts; };
-            if (k < gamma) weight_tile_range<kBonusTiles>(res, 0, ntiles, put);
-            else weight_tile_range<kBonusTiles>(tgt, 0, ntiles, put);
+            __syncthreads();
+            const double ca = resid ? correction_a(correction_kappa(ps, pgs)) : 0.0;
+            if (resid) {
+                for (int t = threadIdx.x; t < ntiles; t += kThreads) tl.w[t] += ca * double(tl.q[t]);
+            }
+            res.a = float(ca);
         }
-        const double total = tiles_total(tile_sum, ntiles);
+        const double total = tiles_total(tl.w, ntiles);
 
         int32_t bonus = -1;
         float mass = 0.0f;
         if (total > 0.0) {
-            bonus = k < gamma ? sample_from_tiles(res, a.V, v, tile_sum) : sample_from_tiles(tgt, a.V, v, tile_sum);
+            bonus = resid ? sample_from_tiles(res, a.V, v, tl.w, total) : sample_from_tiles(tgt, a.V, v, tl.w, total);
             mass = float(total);
-        } else {  // a residual of zero mass (rounding only): p_t of row k
-            weight_tiles<kBonusTiles>(tgt, a.V, tile_sum);
-            bonus = sample_from_tiles(tgt, a.V, v, tile_sum);
+        }
+        if (bonus < 0) {  // a residual of zero mass (rounding only): p_t of row k
+            TargetWeights<DT> pk;
+            pk.init(q.target(k), c, st[k], a.V);
+            double x0 = 0.0, x1 = 0.0;
+            weight_tile_range<kBonusTiles>(pk, 0, ntiles, [&](int t, double tw, double) { tl.w[t] = tw; }, x0, x1);
+            const double W = tiles_total(tl.w, ntiles);
+            bonus = sample_from_tiles(pk, a.V, v, tl.w, W);
+            mass = 0.0f;
         }
         if (threadIdx.x == 0) { s_bonus = bonus; s_mass = mass; }
     }
-    if (threadIdx.x == 0) s_cache_word = (Cache && a.out_hit) ? peek(extra + 3 * k + 2) : ~0ull;
+    if (threadIdx.x == 0) s_cache_word = (Cache && a.out_hit) ? read_pair(extra, 3 * k + 2) : ~0ull;
     __syncthreads();
-    zero_slots(slots, nslots);   // consumed: back to the resting state
+    zero_pairs(slots, nslots);   // consumed: back to the resting state
     __syncthreads();
 
     for (int j = threadIdx.x; j < q.out_len; j += kThreads) {
@@ -274,7 +335,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
             const int32_t xk = k < gamma ? q.tokens[k] : -1;
             bool hit = false;
             if (cw != ~0ull && bonus >= 0 && bonus < a.V && bonus != xk)
-                hit = full_key(load_elem<DT>(q.draft(k), bonus), bonus) + 1ull >= cw;
+                hit = full_key(load_elem<DT>(q.draft(k), bonus), bonus) >= cw;
             a.out_hit[b] = hit ? 1 : 0;
         }
     }

@@ -302,13 +302,10 @@ __device__ __forceinline__ float stream_uniform(uint64_t seed, uint64_t offset, 
 
 // ---------------------------------------------------------- reductions
 
-// A chunk's statistics are published as one 64-bit word, so that a single
-// agent-scope atomic store carries both the value and its readiness, and a
-// reader that sees the word sees all of it (no fence is needed; on gfx950 an
-// agent-scope release fence is an L2 write-back). The low half is never 0 for
-// a published word, so a zero-filled slot means "not published yet".
+// A chunk's statistics are one 64-bit value (published as a tagged pair,
+// below); the reader recomputes mc = fp32(m * c):
 //   softmax: hi = bits(max logit m), lo = ~bits(fp32 s), s = sum 2^(z*c - mc)
-//            relative to mc = fp32(m * c), which the reader recomputes;
+//            relative to mc;
 //   greedy:  hi = bits(best logit),  lo = ~uint32(index), index >= 0;
 //   skipped row (nothing read): hi = bits(-inf), lo = ~bits(0.0f).
 __device__ __forceinline__ uint64_t pack_slot(float hi, uint32_t lo) {
@@ -317,18 +314,42 @@ __device__ __forceinline__ uint64_t pack_slot(float hi, uint32_t lo) {
 __device__ __forceinline__ uint64_t pack_softmax(float m, double s) { return pack_slot(m, ~__float_as_uint(float(s))); }
 __device__ __forceinline__ uint64_t pack_argmax(float v, int32_t idx) { return pack_slot(v, ~uint32_t(idx)); }
 __device__ __forceinline__ uint64_t pack_skipped() { return pack_slot(-INFINITY, ~__float_as_uint(0.0f)); }
-// Any published word is nonzero as a whole (the row words even in their low
-// half); tile and cache words rely on the whole-word test.
-__device__ __forceinline__ bool slot_ready(uint64_t w) { return w != 0ull; }
 __device__ __forceinline__ float slot_hi(uint64_t w) { return __uint_as_float(uint32_t(w >> 32)); }
 __device__ __forceinline__ float slot_s(uint64_t w) { return __uint_as_float(~uint32_t(w)); }
 __device__ __forceinline__ int32_t slot_idx(uint64_t w) { return int32_t(~uint32_t(w)); }
+__device__ __forceinline__ uint64_t pack_f64(double x) { return uint64_t(__double_as_longlong(x)); }
+__device__ __forceinline__ double unpack_f64(uint64_t w) { return __longlong_as_double(int64_t(w)); }
 
-__device__ __forceinline__ void publish(uint64_t* slot, uint64_t w) {
-    __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// ------------------------------------------------------ published values
+//
+// Workgroups of one launch exchange 64-bit values through the workspace. A
+// value is published as a pair of 64-bit words, each holding a 32-bit tag in
+// its high half and one half of the value in its low half, written with
+// agent-scope relaxed atomic stores: each word is single-copy atomic, so a
+// reader that sees the tag in both words has the whole value, and no fence
+// is needed (on gfx950 an agent-scope release fence is an L2 write-back).
+// The tag is the call's epoch (nonzero, a new one for every call), or for the
+// tree walkers' pass totals the epoch and the pass number, so a zero word or
+// a word left by another call or pass never reads as published. Consumed
+// words are returned to zero (the workspace's resting state).
+__device__ __forceinline__ void publish_pair(uint64_t* p, uint64_t v, uint32_t tag) {
+    const uint64_t t = uint64_t(tag) << 32;
+    __hip_atomic_store(p, t | (v >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p + 1, t | (v & 0xffffffffull), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t peek(const uint64_t* slot) {
-    return __hip_atomic_load(const_cast<uint64_t*>(slot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t peek(const uint64_t* w) {
+    return __hip_atomic_load(const_cast<uint64_t*>(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void clear_word(uint64_t* w) {
+    __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool pair_ok(uint64_t hi, uint64_t lo, uint32_t tag) {
+    return uint32_t(hi >> 32) == tag && uint32_t(lo >> 32) == tag;
+}
+__device__ __forceinline__ uint64_t pair_value(uint64_t hi, uint64_t lo) { return (hi << 32) | (lo & 0xffffffffull); }
+// The value of pair i (both words loaded now; the caller knows it is there).
+__device__ __forceinline__ uint64_t read_pair(const uint64_t* p, int64_t i) {
+    return pair_value(peek(p + 2 * i), peek(p + 2 * i + 1));
 }
 
 // a += b for softmax partials (both relative to their own mc).

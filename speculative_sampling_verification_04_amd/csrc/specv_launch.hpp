@@ -22,8 +22,8 @@ struct RowView {
 // Chain verification. Per sequence there are R = 2*gamma + 1 row tasks
 // (target rows 0..gamma, then draft rows 0..gamma-1), each split into S
 // chunks of `chunk` elements, then H bonus workgroups; row chunk j of the
-// sequence in dispatch slot s publishes its statistics in slots[s * R * S + j]
-// (one 64-bit word).
+// sequence in dispatch slot s publishes its statistics as pair s * R * S + j
+// of `slots` (two 64-bit words per pair, tagged with the call's epoch).
 struct ChainArgs {
     RowView target, draft;
     const int32_t* tokens;
@@ -40,7 +40,8 @@ struct ChainArgs {
     // after its rows) share the tile sums of the weights; the last of them
     // resolves. With H > 1 they meet in `tiles` (ntiles words per sequence).
     int32_t H, ntiles;
-    uint64_t* tiles;
+    uint64_t* tiles;         // two pairs per tile per sequence slot (4 * ntiles words)
+    uint64_t* parts;         // two pairs per bonus workgroup per sequence slot (4 * H words)
     int32_t D;               // bonus workgroups trail their rows by D sequences (see decode_chain)
     int32_t cache_rows;      // rows 0 .. cache_rows-1 of T > 0 sequences: cacheable loads (cached_positions)
     // Fused top-F (verify_topf_kernel only): F_k candidates at position k
@@ -67,19 +68,20 @@ struct ChainArgs {
     const int32_t* offsets;
     int32_t num_draft;
     uint64_t wait_ticks;     // bound on every wait for another workgroup's word (WaitBound)
+    uint32_t epoch;          // this call's tag on every published pair (nonzero)
 };
 
 // Tree verification. Per tree there are 2N row tasks (target rows of every
-// node, then draft rows of every node), each split into S chunks, one slot
-// per chunk (slots[(b * 2N + task) * S + chunk]), and H walkers that meet in
-// `walk` (kWalkWords words per tree: the walkers' pass totals for two pass
-// parities, one acknowledgement per walker, the drawn token).
+// node, then draft rows of every node), each split into S chunks, one pair
+// per chunk (pair (b * 2N + task) * S + chunk of `slots`), and H walkers that
+// meet in `walk` (kWalkWords words per tree: the walkers' pass messages for
+// two pass parities, one acknowledgement per walker, the drawn token).
 constexpr int kMaxWalkers = 16;
 constexpr int kMaxTreeNodes = 4096;  // SPECV_MAX_TREE_NODES
 // Tiles of one walker's share: ceil(tiles / H) with H = tree_walkers(V) is at
 // most 32 while tiles <= 512, and at most kMaxTiles / kMaxWalkers beyond.
 constexpr int kMaxWalkTiles = kMaxTiles / kMaxWalkers;
-constexpr int kWalkWords = 3 * kMaxWalkers + 1;
+constexpr int kWalkWords = 2 * (2 * kMaxWalkers * 4 + kMaxWalkers + 1);
 
 struct TreeArgs {
     RowView target, draft;
@@ -103,6 +105,7 @@ struct TreeArgs {
     // tree b + D in dispatch order.
     int32_t D;
     uint64_t wait_ticks;     // bound on every wait for another workgroup's word (WaitBound)
+    uint32_t epoch;          // this call's tag on every published pair (nonzero, low 16 bits too)
 };
 
 // Trees of up to this many nodes are verified in one launch.

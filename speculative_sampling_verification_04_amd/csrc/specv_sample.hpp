@@ -6,10 +6,32 @@
 // 2.2 step 4 / Speculative Decoding (dl-note), sec. 2.3]: the sample is the
 // smallest index j with w_0 + ... + w_j >= v * W, W = sum of all weights.
 // Two passes over the row: (A) the waves sum 512-element tiles (64 lanes x 8
-// consecutive elements), several tiles in flight per wave, into LDS; (B) wave 0
-// scans the tile sums in fp64 to find the tile that holds v*W, recomputes that
-// tile's weights (bit-identical to pass A) and scans them for the index. Only
-// the one row (pair) that needs a sample is read a second time.
+// consecutive elements), several tiles in flight per wave, in fp64; (B) wave
+// 0 scans the tile sums in fp64 to find the tile that holds v*W, recomputes
+// that tile's weights (the same values as pass A) and scans them for the
+// index. Only the one row (pair) that needs a sample is read a second time.
+//
+// Accuracy. A draw agrees with the exact one unless v*W lies within the
+// weights' relative error of a bucket edge, so every weight is computed with
+// an error relative to itself of a few 1e-7, whatever the row:
+//  * p = 2^(z*c - B) with t = z*c - B formed in fp64 and split as n + f,
+//    |f| <= 1/2, so the fp32 exponential sees a small argument;
+//  * the residual max(p - q, 0) = p * max(0, 1 - 2^h), h = log2(q/p), is
+//    never formed as a difference of two probabilities: h is formed in fp64
+//    from the two logits, and 1 - 2^h by a series where |h| < 1;
+//  * the ratio of the two rows' normalisers, which enters every h, is known
+//    from the streaming pass only to ~1e-7 relative (fp32 terms), an error
+//    that would shift W by ~1e-7 absolute, far above 1e-7 * W when W is
+//    small. Pass A therefore also measures the correction: with the
+//    streaming normalisers, sum_x p(x) 2^h(x) = 2^kappa should be 1, and
+//    kappa = log2(1 + sum p (2^h - 1)) is accumulated from terms p * (2^h -
+//    1) whose errors are relative to |p - q|, hence bounded by ~1e-7 * W.
+//    The corrected weights are p * max(0, 1 - 2^(h - kappa)), i.e. for every
+//    element with h < 0: w~ + a * q~ with w~ = p (1 - 2^h), q~ = p 2^h and
+//    a = 1 - 2^-kappa (exact, not a linearisation), so the pass keeps the
+//    tile sums of w~ and q~ and applies a once kappa is known. Elements whose
+//    sign of h - kappa differs from that of h (|h| < |kappa| ~ 1e-7) are off
+//    by at most p * |kappa|.
 #pragma once
 
 #include "specv_device.hpp"
@@ -119,25 +141,25 @@ __device__ __forceinline__ Placement place(const float* temperature, int B, Deco
     return s_pl;
 }
 
-// Waits until the n slots are all published (wave 0 polls with agent-scope
-// atomic loads). Every slot's writer is a workgroup with a lower index, which
-// is dispatched before the caller and never waits itself, so the wait ends;
-// the spin is bounded anyway. Returns false if the bound was reached.
-__device__ bool wait_slots(const uint64_t* slots, int64_t n, uint64_t ticks) {
+// Waits until the n pairs at p (2n words) all carry `tag` (wave 0 polls with
+// agent-scope atomic loads, four loads per lane in flight). Every pair's
+// writer is a workgroup that started before the caller and never waits for
+// it, so the wait ends; it is bounded anyway. Returns false if the bound was
+// reached. Whole workgroup.
+__device__ bool wait_pairs(const uint64_t* p, int64_t n, uint32_t tag, uint64_t ticks) {
     __shared__ int s_ok;
     if (wave_id() == 0) {
         int ok = 0;
+        const int64_t nw = 2 * n;
         for (const WaitBound t(ticks); !t.expired();) {
-            // Four loads in flight per lane per step (no short-circuit, so
-            // that no load waits for another).
             bool mine = true;
-            int64_t i = lane_id();
-            for (; i + 3 * kWaveSize < n; i += 4 * kWaveSize) {
-                const uint64_t a0 = peek(slots + i), a1 = peek(slots + i + kWaveSize);
-                const uint64_t a2 = peek(slots + i + 2 * kWaveSize), a3 = peek(slots + i + 3 * kWaveSize);
-                mine &= slot_ready(a0) & slot_ready(a1) & slot_ready(a2) & slot_ready(a3);
+            int64_t i = 2 * lane_id();
+            for (; i + 2 * kWaveSize < nw; i += 4 * kWaveSize) {
+                const uint64_t a0 = peek(p + i), a1 = peek(p + i + 1);
+                const uint64_t a2 = peek(p + i + 2 * kWaveSize), a3 = peek(p + i + 2 * kWaveSize + 1);
+                mine &= pair_ok(a0, a1, tag) & pair_ok(a2, a3, tag);
             }
-            for (; i < n; i += kWaveSize) mine &= slot_ready(peek(slots + i));
+            for (; i < nw; i += 2 * kWaveSize) mine &= pair_ok(peek(p + i), peek(p + i + 1), tag);
             if (__all(mine)) { ok = 1; break; }
             __builtin_amdgcn_s_sleep(2);
         }
@@ -147,9 +169,9 @@ __device__ bool wait_slots(const uint64_t* slots, int64_t n, uint64_t ticks) {
     return s_ok != 0;
 }
 
-// Returns the n slots to zero (the workspace's resting state).
-__device__ __forceinline__ void zero_slots(uint64_t* slots, int64_t n) {
-    for (int64_t i = threadIdx.x; i < n; i += kThreads) publish(slots + i, 0ull);
+// Returns n pairs (2n words) to zero, the workspace's resting state.
+__device__ __forceinline__ void zero_pairs(uint64_t* p, int64_t n) {
+    for (int64_t i = threadIdx.x; i < 2 * n; i += kThreads) clear_word(p + i);
 }
 
 // Merged statistics of one row (all chunks).
@@ -160,8 +182,8 @@ struct RowStats {
     double Z;    // sum of 2^(z*c - mc)
 };
 
-// A row's statistics from its one word (S = 1): what merging that word alone
-// gives. Any thread.
+// A row's statistics from its one value (S = 1): what merging that value
+// alone gives. Any thread.
 __device__ __forceinline__ RowStats stats_of_word(uint64_t w, bool greedy, float c) {
     RowStats r{-INFINITY, -INFINITY, -1, 0.0};
     const float v = slot_hi(w);
@@ -176,14 +198,13 @@ __device__ __forceinline__ RowStats stats_of_word(uint64_t w, bool greedy, float
     return r;
 }
 
-// A row's statistics from its S <= 64 chunk words, chunk j's word in lane j
-// (the words of lanes >= S are ignored). Greedy: the largest (value, lowest
+// A row's statistics from its S <= 64 chunk values, chunk j's in lane j (the
+// values of lanes >= S are ignored). Greedy: the largest (value, lowest
 // index) over the chunks, an order-free maximum. Softmax: the largest chunk
 // maximum m, then the chunks' sums rescaled to it, 2^(m_j c - m c), and added
 // in the wave's fixed order, so that every workgroup that merges the same
-// words gets the same bits. Whole wave (every lane active); the result is
-// the same in every lane. The S loads are one round trip, issued by the
-// caller.
+// values gets the same bits. Whole wave (every lane active); the result is
+// the same in every lane.
 __device__ __forceinline__ RowStats merge_chunk_words(uint64_t w, int S, bool greedy, float c) {
     const bool mine = lane_id() < S;
     RowStats r;
@@ -213,6 +234,10 @@ __device__ __forceinline__ double prob_of(float z, float c, const RowStats& st) 
     return exp2(double(z) * double(c) - double(st.mc)) / st.Z;
 }
 
+// log2 of a row's normaliser in the streaming pass's reference: p(x) =
+// 2^(z*c - log2_norm).
+__device__ __forceinline__ double log2_norm(const RowStats& st) { return double(st.mc) + log2(st.Z); }
+
 // Raw bits of 8 consecutive elements [j0, j0+8): one or two 16-byte loads when
 // the row start is 16-byte aligned (`vec`) and the group is whole; element
 // loads otherwise, -inf past the end of the row.
@@ -237,91 +262,163 @@ __device__ __forceinline__ void load_group(const void* row, int64_t j0, int64_t 
     }
 }
 
-// Probabilities p = 2^(z*c - mc) / Z of one row (fp32). With a threshold key
-// (Saguaro sampling), the elements whose key reaches it (the row's top F) are
-// scaled by `scale` and Z is the correspondingly reduced normaliser.
-template <int DT, bool kScaled = false>
-struct ProbRow {
-    const void* row;
-    float c, nmc, invZ;
-    bool vec;
-    float scale;          // factor on the top-F elements (kScaled only)
-    uint64_t top_word;    // threshold key + 1 (0: no scaling; kScaled only)
-    __device__ void init(const void* r, float c_, const RowStats& st) {
-        row = r; c = c_; nmc = -st.mc; invZ = float(1.0 / st.Z);
-        vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0;
-        scale = 1.0f; top_word = 0ull;
-    }
-    // Elements j0 .. j0 + 7.
-    __device__ __forceinline__ void probs(const Raw8<DT>& raw, int64_t j0, float p[kLaneElems]) const {
-        float z[kLaneElems];
-        unpack8<DT>(raw, z);
-#pragma unroll
-        for (int e = 0; e < kLaneElems; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(z[e], c, nmc)) * invZ;
-        if (kScaled && top_word != 0ull) {
-#pragma unroll
-            for (int e = 0; e < kLaneElems; ++e)
-                if (full_key(z[e], j0 + e) + 1ull >= top_word) p[e] *= scale;
-        }
-    }
+// ------------------------------------------------------------ weights
+//
+// 2^t in fp32 for t <= ~1 with a relative error of about one fp32 rounding
+// whatever |t|: t = n + f, n = rint(t), |f| <= 1/2, 2^t = 2^f * 2^n. (Formed
+// as fp32 fma(z, c, -m c), t itself would carry an absolute rounding error
+// of up to |t| * 2^-24, i.e. a relative error of |t| * 4e-8 in 2^t.)
+__device__ __forceinline__ float exp2_reduced(double t) {
+    t = fmax(t, -300.0);                   // 2^-300 is 0 in fp32 (keeps -inf out of rint)
+    const double n = rint(t);
+    return ldexpf(__builtin_amdgcn_exp2f(float(t - n)), int(n));
+}
+
+// 2^h - 1 with an error relative to itself of a few fp32 roundings: for
+// |h| < 1 the series of e^x - 1 at x = h ln 2 (terms up to x^9 / 9!, a
+// truncation below 1e-8 relative for |x| < ln 2); beyond, 2^h - 1 directly
+// (|2^h - 1| >= 1/2 there). -inf gives -1.
+__device__ __forceinline__ float exp2m1(float h) {
+    const float x = h * 0.69314718055994531f;
+    float s = 1.0f / 362880.0f;                 // 1/9!
+    s = fmaf(s, x, 1.0f / 40320.0f);
+    s = fmaf(s, x, 1.0f / 5040.0f);
+    s = fmaf(s, x, 1.0f / 720.0f);
+    s = fmaf(s, x, 1.0f / 120.0f);
+    s = fmaf(s, x, 1.0f / 24.0f);
+    s = fmaf(s, x, 1.0f / 6.0f);
+    s = fmaf(s, x, 0.5f);
+    s = fmaf(s, x, 1.0f);
+    const float big = __builtin_amdgcn_exp2f(h) - 1.0f;
+    return fabsf(h) < 1.0f ? x * s : big;
+}
+
+// Weights of one 8-element group as pass A needs them: w (the weights), q
+// (the residual's second term, 0 unless a correction is pending), and the
+// lane's contributions to the correction sums (psum, pgsum).
+struct GroupW {
+    float w[kLaneElems];
+    float q[kLaneElems];
+    float psum, pgsum;
 };
 
-// Weights p of one row (the bonus after every draft was accepted, a leaf).
+// Weights p of one row (the bonus after every draft was accepted, a leaf):
+// p(x) = 2^(z*c - B), B = log2 of the row's normaliser. With `excl` >= 0 that
+// token's weight is 0: the residual when the draft has no probabilities and q
+// is the point mass at the drafted token [Speculative Decoding (dl-note),
+// Appendix "Implementation Details"].
 template <int DT>
 struct TargetWeights {
+    static constexpr bool kCorrected = false;
     struct Raw { Raw8<DT> p; };
-    ProbRow<DT> p;
+    const void* row;
+    double c, B;
     int64_t V;
-    __device__ __forceinline__ void load(int64_t j0, Raw& r) const { load_group<DT>(p.row, j0, V, p.vec, r.p); }
-    __device__ __forceinline__ void weights(const Raw& r, int64_t j0, float w[kLaneElems]) const { p.probs(r.p, j0, w); }
-};
-
-// Weights of p with one token removed: max(p - onehot(x), 0), the residual
-// when the draft has no probabilities and q is the point mass at the drafted
-// token x [Speculative Decoding (dl-note), Appendix "Implementation Details"].
-template <int DT>
-struct ExcludeWeights {
-    struct Raw { Raw8<DT> p; };
-    ProbRow<DT> p;
-    int64_t V;
-    int64_t x;
-    __device__ __forceinline__ void load(int64_t j0, Raw& r) const { load_group<DT>(p.row, j0, V, p.vec, r.p); }
-    __device__ __forceinline__ void weights(const Raw& r, int64_t j0, float w[kLaneElems]) const {
-        p.probs(r.p, j0, w);
+    int64_t excl;
+    bool vec;
+    __device__ void init(const void* r, float c_, const RowStats& st, int64_t V_, int64_t excl_ = -1) {
+        row = r; c = double(c_); B = log2_norm(st); V = V_; excl = excl_;
+        vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0;
+    }
+    __device__ __forceinline__ void load(int64_t j0, Raw& r) const { load_group<DT>(row, j0, V, vec, r.p); }
+    __device__ __forceinline__ void group(const Raw& r, int64_t j0, GroupW& g) const {
+        float z[kLaneElems];
+        unpack8<DT>(r.p, z);
 #pragma unroll
-        for (int e = 0; e < kLaneElems; ++e)
-            if (j0 + e == x) w[e] = 0.0f;
+        for (int e = 0; e < kLaneElems; ++e) {
+            const float p = exp2_reduced(fma(double(z[e]), c, -B));   // 0 for z = -inf
+            g.w[e] = (j0 + e == excl) ? 0.0f : p;
+            g.q[e] = 0.0f;
+        }
+        g.psum = 0.0f;
+        g.pgsum = 0.0f;
+    }
+    // The weights a pass B tile scan uses: the same as pass A's.
+    __device__ __forceinline__ void weights(const Raw& r, int64_t j0, float w[kLaneElems]) const {
+        GroupW g;
+        group(r, j0, g);
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) w[e] = g.w[e];
     }
 };
 
-// Weights max(p - coef * q, 0): the chain residual (coef = 1) and the MSS
-// residual after rejections (coef = c_j of the tree kernel's recurrence).
-template <int DT, bool kScaledQ = false>
+// Residual weights max(0, p - coef * q) = p * max(0, 1 - 2^h) with
+// h = log2(coef * q / p) = (zq - zp) c + [top] log2 C - Hk: the chain residual
+// (coef = 1) and the multi-step residual after rejections (coef = c_j of the
+// tree walk's recurrence), q optionally Saguaro's sigma_{F,C} (its top-F
+// elements, key >= top_key, carry C). Hk = B_q - B_p - log2(coef) (+ kappa,
+// once known), B = log2 of each row's normaliser. With a pending correction
+// (kCorrected use: a != 0 after kappa is known) the weight of an element with
+// h < 0 is w~ + a q~ (see the file comment); pass A returns w~ and q~.
+template <int DT, bool kTop = false>
 struct ResidualWeights {
+    static constexpr bool kCorrected = true;
     struct Raw { Raw8<DT> p, q; };
-    ProbRow<DT> p;
-    ProbRow<DT, kScaledQ> q;
-    float coef;
+    const void* prow;
+    const void* qrow;
+    double c, Bp, Hk, log2C;
+    uint64_t top_key;      // elements of q whose full key is >= this carry C (~0: none)
     int64_t V;
-    __device__ __forceinline__ void load(int64_t j0, Raw& r) const {
-        load_group<DT>(p.row, j0, V, p.vec, r.p);
-        load_group<DT>(q.row, j0, V, q.vec, r.q);
+    bool pvec, qvec;
+    float a;               // 1 - 2^-kappa: the correction applied to the weights (0: none)
+    __device__ void init(const void* pr, const void* qr, float c_, const RowStats& sp, double Bq, double coef,
+                         int64_t V_) {
+        prow = pr; qrow = qr; c = double(c_); Bp = log2_norm(sp);
+        Hk = Bq - Bp - log2(coef);
+        log2C = 0.0; top_key = ~0ull; V = V_; a = 0.0f;
+        pvec = (reinterpret_cast<uintptr_t>(pr) & 15u) == 0;
+        qvec = (reinterpret_cast<uintptr_t>(qr) & 15u) == 0;
     }
-    __device__ __forceinline__ void weights(const Raw& r, int64_t j0, float w[kLaneElems]) const {
-        float a[kLaneElems], b[kLaneElems];
-        p.probs(r.p, j0, a);
-        q.probs(r.q, j0, b);
+    __device__ __forceinline__ void load(int64_t j0, Raw& r) const {
+        load_group<DT>(prow, j0, V, pvec, r.p);
+        load_group<DT>(qrow, j0, V, qvec, r.q);
+    }
+    __device__ __forceinline__ void group(const Raw& r, int64_t j0, GroupW& g) const {
+        float zp[kLaneElems], zq[kLaneElems];
+        unpack8<DT>(r.p, zp);
+        unpack8<DT>(r.q, zq);
+        const double nq = -(Hk + Bp);                                // log2 q~ = zq c [+ log2 C] + nq
+        float ps = 0.0f, pgs = 0.0f;
 #pragma unroll
-        for (int e = 0; e < kLaneElems; ++e) w[e] = fmaxf(fmaf(-coef, b[e], a[e]), 0.0f);
+        for (int e = 0; e < kLaneElems; ++e) {
+            const bool top = kTop && full_key(zq[e], j0 + e) >= top_key;
+            const float p = exp2_reduced(fma(double(zp[e]), c, -Bp));  // 0 for zp = -inf
+            double h = fma(double(zq[e]) - double(zp[e]), c, -Hk);     // log2(coef q / p)
+            double tq = fma(double(zq[e]), c, nq);                      // log2 of coef q~
+            if (top) { h += log2C; tq += log2C; }
+            const float em1 = exp2m1(float(h));                         // 2^h - 1
+            const bool live = p > 0.0f;
+            const bool neg = live && h < 0.0;
+            const float wt = neg ? p * -em1 : 0.0f;
+            g.w[e] = wt;
+            g.q[e] = neg ? p - wt : 0.0f;
+            ps += p;
+            // p (2^h - 1), i.e. coef q~ - p: from the series where |h| < 1;
+            // else q~ - p with q~ = 2^tq formed directly, which stays in range
+            // when p is tiny and 2^h is not, and counts q's mass where p = 0.
+            pgs += (live && h < 1.0) ? p * em1 : exp2_reduced(tq) - p;
+        }
+        g.psum = ps;
+        g.pgsum = pgs;
+    }
+    // The weights of a pass B tile scan: w~ + a q~ on the elements with h < 0.
+    __device__ __forceinline__ void weights(const Raw& r, int64_t j0, float w[kLaneElems]) const {
+        GroupW g;
+        group(r, j0, g);
+#pragma unroll
+        for (int e = 0; e < kLaneElems; ++e) w[e] = fmaxf(fmaf(a, g.q[e], g.w[e]), 0.0f);
     }
 };
 
-// Pass A over tiles [t_lo, t_hi): per-tile sums of the weights (fp32), handed
-// to sink(t, sum) by lane 0 of the wave that summed the tile. Every wave keeps
-// TIF tiles' loads in flight (more is faster for a lone workgroup; fewer keeps
+// Pass A over tiles [t_lo, t_hi): per tile the fp64 sums of w~ and q~,
+// handed to sink(t, w_sum, q_sum) by lane 0 of the wave that summed the tile;
+// the lane's contributions to sum p and sum p (2^h - 1) are added to psum and
+// pgsum (fp64, per thread; corrected weights only). Every wave keeps TIF
+// tiles' loads in flight (more is faster for a lone workgroup; fewer keeps
 // the registers of a kernel that also streams rows low).
 template <int TIF = kTilesInFlight, class WFn, class Sink>
-__device__ __forceinline__ void weight_tile_range(const WFn& f, int t_lo, int t_hi, Sink sink) {
+__device__ __forceinline__ void weight_tile_range(const WFn& f, int t_lo, int t_hi, Sink sink, double& psum,
+                                                  double& pgsum) {
     for (int t0 = t_lo + wave_id() * TIF; t0 < t_hi; t0 += kWaves * TIF) {
         typename WFn::Raw raw[TIF];
 #pragma unroll
@@ -330,17 +427,47 @@ __device__ __forceinline__ void weight_tile_range(const WFn& f, int t_lo, int t_
 #pragma unroll
         for (int u = 0; u < TIF; ++u) {
             if (t0 + u >= t_hi) break;
-            float w[kLaneElems];
-            f.weights(raw[u], int64_t(t0 + u) * kTileElems + lane_id() * kLaneElems, w);
-            const float ls = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
-            const float ts = wave_sum(ls);
-            if (lane_id() == 0) sink(t0 + u, ts);
+            GroupW g;
+            f.group(raw[u], int64_t(t0 + u) * kTileElems + lane_id() * kLaneElems, g);
+            const float lw = ((g.w[0] + g.w[1]) + (g.w[2] + g.w[3])) + ((g.w[4] + g.w[5]) + (g.w[6] + g.w[7]));
+            const double tw = wave_sum(double(lw));
+            double tq = 0.0;
+            if (WFn::kCorrected) {
+                const float lq = ((g.q[0] + g.q[1]) + (g.q[2] + g.q[3])) + ((g.q[4] + g.q[5]) + (g.q[6] + g.q[7]));
+                tq = wave_sum(double(lq));
+                psum += double(g.psum);
+                pgsum += double(g.pgsum);
+            }
+            if (lane_id() == 0) sink(t0 + u, tw, tq);
         }
     }
 }
 
+// Workgroup totals (in a fixed order: wave sums, then the waves in order) of
+// two per-thread fp64 values. Whole workgroup.
+__device__ __forceinline__ void block_sum2(double& x, double& y) {
+    __shared__ double sx[kWaves], sy[kWaves];
+    x = wave_sum(x);
+    y = wave_sum(y);
+    if (lane_id() == 0) { sx[wave_id()] = x; sy[wave_id()] = y; }
+    __syncthreads();
+    x = sx[0];
+    y = sy[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) { x += sx[w]; y += sy[w]; }
+    __syncthreads();
+}
+
+// The correction of the file comment from the totals of sum p and
+// sum p (2^h - 1): a = 1 - 2^-kappa, kappa = log2(1 + pg / p).
+__device__ __forceinline__ double correction_kappa(double psum, double pgsum) {
+    const double r = psum > 0.0 ? 1.0 + pgsum / psum : 0.0;
+    return r > 0.0 ? log2(r) : 0.0;
+}
+__device__ __forceinline__ double correction_a(double kappa) { return 1.0 - exp2(-kappa); }
+
 // Total of the tile sums in fp64 (whole workgroup; tile_sum in LDS).
-__device__ __forceinline__ double tiles_total(const float* tile_sum, int ntiles) {
+__device__ __forceinline__ double tiles_total(const double* tile_sum, int ntiles) {
     __shared__ double s_total;
     __syncthreads();
     if (wave_id() == 0) {
@@ -352,20 +479,6 @@ __device__ __forceinline__ double tiles_total(const float* tile_sum, int ntiles)
     __syncthreads();
     return s_total;
 }
-
-// Pass A over the whole row by one workgroup: tile sums into LDS, and their
-// total.
-template <int TIF = kTilesInFlight, class WFn>
-__device__ __forceinline__ double weight_tiles(const WFn& f, int64_t V, float* tile_sum) {
-    const int ntiles = int((V + kTileElems - 1) / kTileElems);
-    weight_tile_range<TIF>(f, 0, ntiles, [&](int t, float ts) { tile_sum[t] = ts; });
-    return tiles_total(tile_sum, ntiles);
-}
-
-// A tile sum published to another workgroup: one 64-bit word, hi = 1 so that
-// a published word is never 0 (0 = not yet written), lo = the fp32 bits.
-__device__ __forceinline__ uint64_t pack_tile(float ts) { return (1ull << 32) | uint64_t(__float_as_uint(ts)); }
-__device__ __forceinline__ float tile_of(uint64_t w) { return __uint_as_float(uint32_t(w)); }
 
 // The element of tile `tile` at which the running sum of f's weights over the
 // tile first reaches tin; rounding past the tile's scanned total takes its
@@ -399,8 +512,12 @@ __device__ __forceinline__ int32_t sample_in_tile(const WFn& f, int tile, double
             idx = tile * kTileElems + L * kLaneElems + __shfl(fe, L);
         } else {  // rounding: v*W fell past the tile's scanned total; take its last positive element
             const uint64_t m2 = __ballot(le >= 0);
-            const int L = 63 - __builtin_clzll(m2);
-            idx = tile * kTileElems + L * kLaneElems + __shfl(le, L);
+            if (m2 != 0) {
+                const int L = 63 - __builtin_clzll(m2);
+                idx = tile * kTileElems + L * kLaneElems + __shfl(le, L);
+            } else {
+                idx = -1;
+            }
         }
         if (lane == 0) s_idx = idx;
     }
@@ -408,12 +525,12 @@ __device__ __forceinline__ int32_t sample_in_tile(const WFn& f, int tile, double
     return s_idx;
 }
 
-// The tile of tile_sum[0..n) (fp32 sums of consecutive tiles) at which a
+// The tile of tile_sum[0..n) (fp64 sums of consecutive tiles) at which a
 // running fp64 sum that starts at `base` first reaches `target`, counting
 // positive tiles only, and the remainder of the target inside it (*tin).
 // Rounding that leaves the target past the last tile takes the last positive
 // tile. -1 when no tile is positive. Wave 0 computes; whole workgroup.
-__device__ __forceinline__ int find_tile(const float* tile_sum, int n, double base, double target, double* tin) {
+__device__ __forceinline__ int find_tile(const double* tile_sum, int n, double base, double target, double* tin) {
     __shared__ int32_t s_tile;
     __shared__ double s_tin;
     const int lane = lane_id();
@@ -423,7 +540,7 @@ __device__ __forceinline__ int find_tile(const float* tile_sum, int n, double ba
         const int t1 = min(n, t0 + seg);
         double ps = 0.0;
         bool pos = false;
-        for (int t = t0; t < t1; ++t) { ps += tile_sum[t]; pos = pos || tile_sum[t] > 0.0f; }
+        for (int t = t0; t < t1; ++t) { ps += tile_sum[t]; pos = pos || tile_sum[t] > 0.0; }
         const double incl = base + wave_inclusive_scan(ps);
         double excl = __shfl_up(incl, 1);
         if (lane == 0) excl = base;
@@ -436,14 +553,14 @@ __device__ __forceinline__ int find_tile(const float* tile_sum, int n, double ba
             if (lane == L) {
                 double acc = excl;
                 for (int t = t0; t < t1; ++t) {
-                    const float ts = tile_sum[t];
-                    const double nx = acc + double(ts);
-                    if (ts > 0.0f && nx >= target) { tile = t; rem = target - acc; break; }
+                    const double ts = tile_sum[t];
+                    const double nx = acc + ts;
+                    if (ts > 0.0 && nx >= target) { tile = t; rem = target - acc; break; }
                     acc = nx;
                 }
                 if (tile < 0) {  // rounding left the target past this segment: its last positive tile
                     for (int t = t1 - 1; t >= t0; --t)
-                        if (tile_sum[t] > 0.0f) { tile = t; rem = double(tile_sum[t]); break; }
+                        if (tile_sum[t] > 0.0) { tile = t; rem = tile_sum[t]; break; }
                 }
             }
             tile = __shfl(tile, L);
@@ -456,51 +573,16 @@ __device__ __forceinline__ int find_tile(const float* tile_sum, int n, double ba
     return s_tile;
 }
 
-// Pass B: given the tile sums of pass A, the smallest j with S_j >= v * W.
-// Returns -1 when the total is 0.
+// Pass B: given the tile sums of pass A (total W), the smallest j with
+// S_j >= v * W. Returns -1 when W is not positive.
 template <class WFn>
-__device__ __forceinline__ int32_t sample_from_tiles(const WFn& f, int64_t V, float v, const float* tile_sum) {
+__device__ __forceinline__ int32_t sample_from_tiles(const WFn& f, int64_t V, float v, const double* tile_sum,
+                                                     double W) {
+    if (!(W > 0.0)) return -1;
     const int ntiles = int((V + kTileElems - 1) / kTileElems);
-    const int lane = lane_id();
-    __shared__ int32_t s_tile;
-    __shared__ double s_tin;
-    if (wave_id() == 0) {
-        const int seg = (ntiles + kWaveSize - 1) / kWaveSize;
-        const int t0 = lane * seg;
-        const int t1 = min(ntiles, t0 + seg);
-        double ps = 0.0;
-        for (int t = t0; t < t1; ++t) ps += tile_sum[t];
-        const double incl = wave_inclusive_scan(ps);
-        const double W = __shfl(incl, kWaveSize - 1);
-        double excl = __shfl_up(incl, 1);
-        if (lane == 0) excl = 0.0;
-        const double target = double(v) * W;
-        const uint64_t m = __ballot(W > 0.0 && incl >= target);
-        int tile = -1;
-        double tin = 0.0;
-        if (m != 0) {
-            const int L = __builtin_ctzll(m);
-            if (lane == L) {
-                double acc = excl;
-                for (int t = t0; t < t1; ++t) {
-                    const float ts = tile_sum[t];
-                    const double nx = acc + double(ts);
-                    if (ts > 0.0f && nx >= target) { tile = t; tin = target - acc; break; }
-                    acc = nx;
-                }
-                if (tile < 0) {  // rounding left v*W past this segment: take its last positive tile
-                    for (int t = t1 - 1; t >= t0; --t)
-                        if (tile_sum[t] > 0.0f) { tile = t; tin = double(tile_sum[t]); break; }
-                }
-            }
-            tile = __shfl(tile, L);
-            tin = __shfl(tin, L);
-        }
-        if (lane == 0) { s_tile = tile; s_tin = tin; }
-    }
-    __syncthreads();
-    const int tile = s_tile;
-    return tile >= 0 ? sample_in_tile(f, tile, s_tin) : -1;
+    double tin = 0.0;
+    const int tile = find_tile(tile_sum, ntiles, 0.0, double(v) * W, &tin);
+    return tile >= 0 ? sample_in_tile(f, tile, tin) : -1;
 }
 
 }  // namespace specv

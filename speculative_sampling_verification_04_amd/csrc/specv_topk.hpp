@@ -189,25 +189,18 @@ __device__ __forceinline__ void topf_write(const uint64_t* pick, int need, int F
     }
 }
 
-// Ends a row's selection (whole workgroup, after streaming; keys: LDS of
-// topf_keys<K>() words): every wave compacts its candidates to at most K
-// groups, the keys that reach the largest wave threshold are gathered, wave 0
-// pops the F + 1 largest, and thread 0 writes the first F ids (and logits)
-// that are not `excl`, then -1 up to Fmax entries. Returns the F + 1 largest
-// keys of the row in LDS (0 = none), before the exclusion; they stay valid
-// until the caller's next barrier.
 // The F1 largest keys of a row searched in chunks, from the chunks' published
-// lists (n words at kw: each chunk's F1 largest keys + 1, 1 for none, 0 =
-// not yet written): waits for the n words, loads them into mk (LDS, n words)
-// and pops the F1 largest, which are the row's own (each of them is among
-// its chunk's F1 largest). Returns them in LDS, largest first (0 = none; all
-// 0 if the wait ran out). Whole workgroup.
+// lists (n pairs at kw: each chunk's F1 largest keys, 0 for none): waits for
+// the n pairs, loads them into mk (LDS, n words) and pops the F1 largest,
+// which are the row's own (each of them is among its chunk's F1 largest).
+// Returns them in LDS, largest first (0 = none; all 0 if the wait ran out).
+// Whole workgroup.
 template <int kMaxKeys>
 __device__ __forceinline__ const uint64_t* topf_merge_chunks(const uint64_t* kw, int n, int F1, uint64_t* mk,
-                                                             uint64_t ticks) {
+                                                             uint32_t tag, uint64_t ticks) {
     __shared__ uint64_t s_pick[kMaxKeys];
-    const bool ok = wait_slots(kw, n, ticks);
-    for (int i = threadIdx.x; i < n; i += kThreads) mk[i] = ok ? peek(kw + i) - 1ull : 0ull;
+    const bool ok = wait_pairs(kw, n, tag, ticks);
+    for (int i = threadIdx.x; i < n; i += kThreads) mk[i] = ok ? read_pair(kw, i) : 0ull;
     __syncthreads();
     if (wave_id() == 0) {
         for (int r = 0; r < F1; ++r) {
@@ -223,6 +216,13 @@ __device__ __forceinline__ const uint64_t* topf_merge_chunks(const uint64_t* kw,
     return s_pick;
 }
 
+// Ends a row's selection (whole workgroup, after streaming; keys: LDS of
+// topf_keys<K>() words): every wave compacts its candidates to at most K
+// groups, the keys that reach the largest wave threshold are gathered, wave 0
+// pops the F + 1 largest, and thread 0 writes the first F ids (and logits)
+// that are not `excl`, then -1 up to Fmax entries. Returns the F + 1 largest
+// keys of the row in LDS (0 = none), before the exclusion; they stay valid
+// until the caller's next barrier.
 template <int DT, int K>
 __device__ __forceinline__ const uint64_t* topf_finish(TopKAcc<DT, K>& acc, const void* rp, int64_t V, int F,
                                                        int Fmax, int32_t excl, int32_t* out_ids, float* out_logits,
@@ -233,13 +233,15 @@ __device__ __forceinline__ const uint64_t* topf_finish(TopKAcc<DT, K>& acc, cons
     return pick;
 }
 
-// The F-th largest key of the row (no exclusion), or 0 when F = 0: a key is
-// among the row's top F iff it is >= this.
-__device__ __forceinline__ uint64_t topf_sigma_key(const uint64_t* pick, int F) { return F > 0 ? pick[F - 1] : 0ull; }
+// The F-th largest key of the row (no exclusion), or ~0 (reached by no key)
+// when F = 0: a key is among the row's top F iff it is >= this.
+__device__ __forceinline__ uint64_t topf_sigma_key(const uint64_t* pick, int F) { return F > 0 ? pick[F - 1] : ~0ull; }
 
-// The F-th largest key once `excl` is dropped, or 0 when F = 0: a key other
-// than excl's is a cache candidate iff it is >= this.
+// The F-th largest key once `excl` is dropped, or ~0 when F = 0: a key other
+// than excl's is a cache candidate iff it is >= this (0 when the row has
+// fewer than F other elements: then every one is).
 __device__ __forceinline__ uint64_t topf_cache_key(const uint64_t* pick, int F, int32_t excl) {
+    if (F == 0) return ~0ull;
     int n = 0;
     for (int r = 0; r <= F && n < F; ++r) {
         const uint64_t key = pick[r];

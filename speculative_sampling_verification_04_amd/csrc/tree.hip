@@ -10,16 +10,16 @@
 // 1. Rows (tree_row): the row-statistics stream of the chain kernel over
 //    every node's target row and over the draft rows of nodes that have
 //    children (the distribution their children were drawn from); every
-//    workgroup publishes one 64-bit word.
+//    workgroup publishes one tagged pair.
 //
 // 2. Walkers (tree_walk): H workgroups per tree (launch_tree_dt says why
 //    they are all resident together). Every walker of a tree runs
 //    the same walk on the same data and takes the same decisions; each full pass
 //    over a node's rows that the walk needs is split between them: walker h
 //    sums the weights over its share of the 512-element tiles, keeps its tile
-//    sums in LDS and publishes its share's total as one word tagged with the
-//    pass number, and every walker then adds the H totals in walker order. A
-//    pass therefore costs one exchange of H words, with no command round trip;
+//    sums in LDS and publishes its share's totals tagged with the pass
+//    number, and every walker then adds the H totals in walker order. A
+//    pass therefore costs one exchange of H messages, with no command round trip;
 //    the accept tests of a node's children are prepared in parallel when the
 //    walk reaches the node. The final draw is made by the walker whose share
 //    holds the inverse-CDF point.
@@ -32,7 +32,15 @@
 // (p - (c_j + M_j) q) / M_j). So every rejection costs one pass over the
 // node's target and draft rows, whose tile sums also serve the final
 // inverse-CDF draw if every child is rejected. The accept test for a child
-// with token t uses the gathered logits in fp64: u <= r_j(t) / q(t).
+// with token t uses the gathered logits in fp64: u <= r_j(t) / q(t), with
+// r_j(t) / q(t) = max(0, p(t)/q(t) - c_j) / M_j and p(t)/q(t) formed from the
+// two logits (never as a difference of probabilities).
+//
+// Accuracy (see specv_sample.hpp): the node's first residual pass measures
+// the correction kappa of the two rows' normaliser ratio and sum p~ = A; its
+// tile sums are corrected once kappa is known, later passes at the node fold
+// kappa into their exponent, and masses are taken in probability units
+// (sums / A), so c_j and M_j carry only the weights' own rounding.
 #include "specv_launch.hpp"
 #include "specv_sample.hpp"
 
@@ -91,7 +99,7 @@ __device__ __forceinline__ void tree_row(const TreeArgs& a, int b, int64_t w) {
             word = pack_softmax(acc.m, acc.s);
         }
     }
-    if (threadIdx.x == 0) publish(a.slots + int64_t(b) * 2 * N * a.S + w, word);
+    if (threadIdx.x == 0) publish_pair(a.slots + 2 * (int64_t(b) * 2 * N * a.S + w), word, a.epoch);
 }
 
 template <int DT>
@@ -102,43 +110,37 @@ __global__ __launch_bounds__(kThreads) void tree_stats_kernel(TreeArgs a) {
 
 // ------------------------------------------------------------------ walk
 
-// Walk words of one tree (a.walk + b * kWalkWords, zero at rest): the walkers'
-// pass totals, double-buffered by pass parity (tag = pass number in the high
-// half, fp32 total in the low half), one acknowledgement per walker, and the
-// bonus word of the final draw (1 << 32 | bonus).
+// Walk words of one tree (a.walk + b * kWalkWords, zero at rest), all as
+// tagged pairs: the walkers' pass messages, double-buffered by pass parity
+// (four fp64 values per walker: the sums of w~ and q~ over its share, and of
+// p and p (2^h - 1) when the pass measures the correction; tag = epoch and
+// pass number), one acknowledgement per walker and the drawn token (tag =
+// the epoch).
+constexpr int kPassValues = 4;
 struct WalkWords {
-    uint64_t* part;   // [2][kMaxWalkers]
-    uint64_t* ack;    // [kMaxWalkers]
-    uint64_t* bonus;  // [1]
+    uint64_t* part;   // [2][kMaxWalkers][kPassValues] pairs
+    uint64_t* ack;    // [kMaxWalkers] pairs
+    uint64_t* bonus;  // [1] pair
 };
+static_assert(kWalkWords == 2 * (2 * kMaxWalkers * kPassValues + kMaxWalkers + 1), "walk words of one tree");
 
 __device__ __forceinline__ WalkWords walk_of(const TreeArgs& a, int b) {
     uint64_t* w = a.walk + int64_t(b) * kWalkWords;
-    return WalkWords{w, w + 2 * kMaxWalkers, w + 3 * kMaxWalkers};
+    uint64_t* ack = w + 2 * (2 * kMaxWalkers * kPassValues);
+    return WalkWords{w, ack, ack + 2 * kMaxWalkers};
 }
 
-// Waits until each of the n words carries tag `p` in its high half (wave 0
-// polls; bounded like wait_slots). Whole workgroup.
-__device__ bool wait_tagged(const uint64_t* w, int n, uint32_t p, uint64_t ticks) {
-    __shared__ int s_ok;
-    if (wave_id() == 0) {
-        int ok = 0;
-        for (const WaitBound t(ticks); !t.expired();) {
-            bool mine = true;
-            for (int i = lane_id(); i < n; i += kWaveSize) mine &= uint32_t(peek(w + i) >> 32) == p;
-            if (__all(mine)) { ok = 1; break; }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        if (lane_id() == 0) s_ok = ok;
-    }
-    __syncthreads();
-    return s_ok != 0;
+// Tag of the pass messages: the epoch's low 16 bits (never 0) and the pass
+// number (1 .. < 2^16), so neither a zero word, a message of the pass before
+// last in the same buffer nor one of another call reads as this pass's.
+__device__ __forceinline__ uint32_t pass_tag(uint32_t epoch, uint32_t pass) {
+    return ((epoch & 0xffffu) << 16) | (pass & 0xffffu);
 }
 
 // Waits until the words of node `node`'s target row (and, with `draft`, its
 // draft row) are published (wave 0 polls). Whole workgroup; false if the
 // bound was reached.
-__device__ bool wait_node(const uint64_t* slots, int N, int S, int node, bool draft, uint64_t ticks) {
+__device__ bool wait_node(const uint64_t* slots, int N, int S, int node, bool draft, uint32_t ep, uint64_t ticks) {
     __shared__ int s_ok;
     if (wave_id() == 0) {
         int ok = 0;
@@ -147,7 +149,7 @@ __device__ bool wait_node(const uint64_t* slots, int N, int S, int node, bool dr
             bool mine = true;
             for (int i = lane_id(); i < n; i += kWaveSize) {
                 const int64_t k = i < S ? int64_t(node) * S + i : int64_t(N + node) * S + (i - S);
-                mine &= slot_ready(peek(slots + k));
+                mine &= pair_ok(peek(slots + 2 * k), peek(slots + 2 * k + 1), ep);
             }
             if (__all(mine)) { ok = 1; break; }
             __builtin_amdgcn_s_sleep(2);
@@ -164,15 +166,20 @@ template <int NM>
 struct WalkLds {
     RowStats sp, sq;              // statistics of the current node's target and draft rows
     int32_t kid[kThreads];        // a batch of the current node's children, ascending
-    double pc[kThreads], qc[kThreads];  // p(t), q(t) of each child's token t
+    double pc[kThreads], qc[kThreads];  // p(t), q(t) of each child's token t (streaming statistics)
+    float zp[kThreads], zq[kThreads];   // the two logits at each child's token
     float u[kThreads];            // each child's uniform
-    float part[kMaxWalkers];      // the walkers' totals of the last pass
-    float tile[kMaxWalkTiles];    // this walker's tile sums of the last pass
+    double part[kMaxWalkers];     // the walkers' totals of the last pass (corrected)
+    double tile[kMaxWalkTiles];   // this walker's tile sums of the last pass (corrected)
+    float tile_q[kMaxWalkTiles];  // their q~ sums (a pass that measures the correction)
     int32_t par[NM];              // the tree's parents and tokens
     int32_t tok[NM];
     int nk, from;                 // batch size; next position of the child scan
     int ok;
 };
+
+// The weights of one pass over the current node's rows.
+enum PassKind { kPassTarget = 0, kPassFirst = 1, kPassResid = 2 };
 
 // TIF: tiles in flight per wave in a pass. kStreaming: the tree's rows may
 // still be streaming, so a node's words are awaited before they are read.
@@ -186,45 +193,95 @@ struct Walker {
     const void* prow;
     const void* qrow;
     uint32_t pass = 0;
+    // The node's correction (measured by its first residual pass): kappa,
+    // and the sum of p~ over the row (masses in probability units = sums of
+    // weights / A).
+    double kappa = 0.0, A = 1.0;
 
-    // One shared pass over the current node's weights (target: p; else
-    // max(0, p - coef q)). Returns the fp64 sum of the H walker totals, or -1
-    // if a wait ran out.
-    __device__ __forceinline__ double run_pass(bool target, float coef) {
+    // One shared pass over the current node's weights: p (kPassTarget); the
+    // first residual max(0, p - q), which also measures the node's
+    // correction (kPassFirst); or max(0, p - coef q) with the correction
+    // known (kPassResid). Sets *total to the fp64 sum of the H walker
+    // totals (corrected; every walker computes the same totals in the same
+    // order); false if a wait ran out.
+    __device__ __forceinline__ bool run_pass(PassKind kind, double coef, double* total) {
         ++pass;
-        auto put = [&](int t, float ts) { s.tile[t - lo] = ts; };
-        if (target) {
+        double ps = 0.0, pgs = 0.0;
+        auto put = [&](int t, double tw, double tq) { s.tile[t - lo] = tw; s.tile_q[t - lo] = float(tq); };
+        if (kind == kPassTarget) {
             TargetWeights<DT> f;
-            f.p.init(prow, c, s.sp);
-            f.V = a.V;
-            weight_tile_range<TIF>(f, lo, hi, put);
+            f.init(prow, c, s.sp, a.V);
+            weight_tile_range<TIF>(f, lo, hi, put, ps, pgs);
         } else {
             ResidualWeights<DT> f;
-            f.p.init(prow, c, s.sp);
-            f.q.init(qrow, c, s.sq);
-            f.coef = coef;
-            f.V = a.V;
-            weight_tile_range<TIF>(f, lo, hi, put);
+            f.init(prow, qrow, c, s.sp, log2_norm(s.sq), coef, a.V);
+            if (kind == kPassResid) f.Hk += kappa;
+            weight_tile_range<TIF>(f, lo, hi, put, ps, pgs);
         }
-        const double mine = tiles_total(s.tile, hi - lo);
-        uint64_t* part = w.part + (pass & 1u) * kMaxWalkers;
-        if (threadIdx.x == 0) publish(part + h, (uint64_t(pass) << 32) | __float_as_uint(float(mine)));
-        if (!wait_tagged(part, a.H, pass, a.wait_ticks)) return -1.0;
-        if (threadIdx.x < a.H) s.part[threadIdx.x] = __uint_as_float(uint32_t(peek(part + threadIdx.x)));
+        const int nt = hi - lo;
+        double mw = 0.0, mq = 0.0;
+        __shared__ double s_mw, s_mq;
         __syncthreads();
-        double total = 0.0;
-        for (int k = 0; k < a.H; ++k) total += double(s.part[k]);
-        return total;
+        if (wave_id() == 0) {
+            double x = 0.0, y = 0.0;
+            for (int t = lane_id(); t < nt; t += kWaveSize) { x += s.tile[t]; y += double(s.tile_q[t]); }
+            x = wave_sum(x);
+            y = wave_sum(y);
+            if (lane_id() == 0) { s_mw = x; s_mq = y; }
+        }
+        if (kind == kPassFirst) block_sum2(ps, pgs);
+        __syncthreads();
+        mw = s_mw;
+        mq = s_mq;
+        const uint32_t tag = pass_tag(a.epoch, pass);
+        uint64_t* part = w.part + 2 * (int64_t(pass & 1u) * kMaxWalkers * kPassValues);
+        if (threadIdx.x == 0) {
+            uint64_t* mine = part + 2 * kPassValues * h;
+            publish_pair(mine + 0, pack_f64(mw), tag);
+            publish_pair(mine + 2, pack_f64(mq), tag);
+            publish_pair(mine + 4, pack_f64(ps), tag);
+            publish_pair(mine + 6, pack_f64(pgs), tag);
+        }
+        if (!wait_pairs(part, int64_t(a.H) * kPassValues, tag, a.wait_ticks)) return false;
+        __shared__ double s_kappa, s_A;
+        if (threadIdx.x == 0) {
+            double P = 0.0, PG = 0.0;
+            if (kind == kPassFirst) {
+                for (int k = 0; k < a.H; ++k) {
+                    P += unpack_f64(read_pair(part, kPassValues * k + 2));
+                    PG += unpack_f64(read_pair(part, kPassValues * k + 3));
+                }
+            }
+            const double kap = kind == kPassFirst ? correction_kappa(P, PG) : kappa;
+            const double ca = kind == kPassFirst ? correction_a(kap) : 0.0;
+            for (int k = 0; k < a.H; ++k)
+                s.part[k] = unpack_f64(read_pair(part, kPassValues * k)) +
+                            ca * unpack_f64(read_pair(part, kPassValues * k + 1));
+            s_kappa = kap;
+            s_A = kind == kPassFirst ? P : A;
+        }
+        __syncthreads();
+        if (kind == kPassFirst) {
+            kappa = s_kappa;
+            A = s_A > 0.0 ? s_A : 1.0;
+            const double ca = correction_a(kappa);
+            for (int t = threadIdx.x; t < nt; t += kThreads) s.tile[t] += ca * double(s.tile_q[t]);
+            __syncthreads();
+        }
+        double t = 0.0;
+        for (int k = 0; k < a.H; ++k) t += s.part[k];
+        *total = t;
+        return true;
     }
 
     // The next batch of the node's children (ascending ids; the first batch
     // of a node starts after the node and also brings the node's statistics)
-    // and their accept-test inputs. The statistics words and the children's
+    // and their accept-test inputs. The statistics pairs and the children's
     // logits are read in one round trip. Whole workgroup; false if a wait for
     // the node's words ran out.
     __device__ __forceinline__ bool next_batch(int node, bool first) {
-        const uint64_t* slots = a.slots + int64_t(b) * 2 * N * a.S;
-        if (kStreaming && first && !wait_node(slots, N, a.S, node, true, a.wait_ticks)) return false;
+        const uint64_t* slots = a.slots + 2 * int64_t(b) * 2 * N * a.S;
+        if (kStreaming && first && !wait_node(slots, N, a.S, node, true, a.epoch, a.wait_ticks)) return false;
         if (wave_id() == 0) {
             int n = 0, base = first ? node + 1 : s.from;
             for (; base < N && n <= kThreads - kWaveSize; base += kWaveSize) {
@@ -238,8 +295,8 @@ struct Walker {
         }
         if (first && wave_id() == 1) {  // the node's statistics, beside wave 0's scan
             const bool lane_ok = lane_id() < a.S;
-            const uint64_t wp = lane_ok ? peek(slots + int64_t(node) * a.S + lane_id()) : 0ull;
-            const uint64_t wq = lane_ok ? peek(slots + int64_t(N + node) * a.S + lane_id()) : 0ull;
+            const uint64_t wp = lane_ok ? read_pair(slots, int64_t(node) * a.S + lane_id()) : 0ull;
+            const uint64_t wq = lane_ok ? read_pair(slots, int64_t(N + node) * a.S + lane_id()) : 0ull;
             const RowStats sp = merge_chunk_words(wp, a.S, false, c);
             const RowStats sq = merge_chunk_words(wq, a.S, false, c);
             if (lane_id() == 0) { s.sp = sp; s.sq = sq; }
@@ -255,22 +312,32 @@ struct Walker {
         if (mine) {
             s.pc[threadIdx.x] = in_range ? prob_of(zp, c, s.sp) : 0.0;
             s.qc[threadIdx.x] = in_range ? prob_of(zq, c, s.sq) : 0.0;
+            s.zp[threadIdx.x] = zp;
+            s.zq[threadIdx.x] = zq;
             s.u[threadIdx.x] = stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(ch));
         }
         __syncthreads();
         return true;
     }
 
-    // Final draw from the weights of the last pass (their fp32 walker totals
-    // in s.part, total W): the walker whose share holds v * W finds the tile
-    // and the token and publishes it. Returns whether a draw was made.
-    __device__ __forceinline__ bool draw(bool target, float coef, double W) {
+    // p(t) / q(t) at child k of the batch once the node's correction is
+    // known: 2^(kappa - h), h = (zq - zp) c - (B_q - B_p), in fp64 (no
+    // difference of probabilities).
+    __device__ __forceinline__ double p_over_q(int k) const {
+        const double hk = fma(double(s.zq[k]) - double(s.zp[k]), double(c), -(log2_norm(s.sq) - log2_norm(s.sp)));
+        return exp2(kappa - hk);
+    }
+
+    // Final draw from the weights of the last pass (the walkers' totals in
+    // s.part, total W): the walker whose share holds v * W finds the tile and
+    // the token and publishes it. Returns whether a draw was made.
+    __device__ __forceinline__ bool draw(PassKind kind, double coef, double W) {
         if (!(W > 0.0)) return false;
         const double want = double(v) * W;
         int owner = -1;
         double base = 0.0, acc = 0.0;
         for (int k = 0; k < a.H; ++k) {  // same in every thread of every walker
-            const double P = double(s.part[k]);
+            const double P = s.part[k];
             if (P > 0.0) {
                 owner = k;
                 base = acc;
@@ -283,21 +350,19 @@ struct Walker {
             const int t = find_tile(s.tile, hi - lo, base, want, &tin);
             int32_t bonus = -1;
             if (t >= 0) {
-                if (target) {
+                if (kind == kPassTarget) {
                     TargetWeights<DT> f;
-                    f.p.init(prow, c, s.sp);
-                    f.V = a.V;
+                    f.init(prow, c, s.sp, a.V);
                     bonus = sample_in_tile(f, lo + t, tin);
                 } else {
                     ResidualWeights<DT> f;
-                    f.p.init(prow, c, s.sp);
-                    f.q.init(qrow, c, s.sq);
-                    f.coef = coef;
-                    f.V = a.V;
+                    f.init(prow, qrow, c, s.sp, log2_norm(s.sq), coef, a.V);
+                    if (kind == kPassResid) f.Hk += kappa;
+                    else f.a = float(correction_a(kappa));
                     bonus = sample_in_tile(f, lo + t, tin);
                 }
             }
-            if (threadIdx.x == 0) publish(w.bonus, (1ull << 32) | uint32_t(bonus));
+            if (threadIdx.x == 0) publish_pair(w.bonus, uint64_t(uint32_t(bonus)), a.epoch);
         }
         return owner >= 0;
     }
@@ -318,10 +383,10 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
     const WalkWords w = walk_of(a, b);
-    uint64_t* slots = a.slots + int64_t(b) * 2 * N * a.S;
+    uint64_t* slots = a.slots + 2 * int64_t(b) * 2 * N * a.S;
 
     if (greedy && h != 0) {  // VerifyGreedy is one walker's argmax walk
-        if (threadIdx.x == 0) publish(w.ack + h, 1ull);
+        if (threadIdx.x == 0) publish_pair(w.ack + 2 * h, 1ull, a.epoch);
         return;
     }
     if (threadIdx.x == 0) { s_nacc = 0; s_fail = 0; }
@@ -336,12 +401,12 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     if (greedy) {  // VerifyGreedy
         int node = 0;
         while (true) {
-            if (kStreaming && !wait_node(slots, N, a.S, node, false, a.wait_ticks)) {
+            if (kStreaming && !wait_node(slots, N, a.S, node, false, a.epoch, a.wait_ticks)) {
                 if (threadIdx.x == 0) s_fail = 1;
                 break;
             }
             if (wave_id() == 0) {
-                const uint64_t wg = lane_id() < a.S ? peek(slots + int64_t(node) * a.S + lane_id()) : 0ull;
+                const uint64_t wg = lane_id() < a.S ? read_pair(slots, int64_t(node) * a.S + lane_id()) : 0ull;
                 const RowStats sg = merge_chunk_words(wg, a.S, true, 0.0f);
                 if (lane_id() == 0) s.sp = sg;
             }
@@ -374,8 +439,12 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
             wk.prow = row_ptr(a.target, esz, b, node);
             wk.qrow = row_ptr(a.draft, esz, b, node);
             if (!wk.next_batch(node, true)) { failed = true; break; }
-            double cj = 0.0, Mj = 1.0;   // r = max(0, p - cj q) / Mj; identical everywhere
+            // r = max(0, p - cj q) / Mj (probability units); identical in every
+            // walker. The node's first rejection measures its correction.
+            double cj = 0.0, Mj = 1.0;
+            bool measured = false;
             bool tiles_valid = false;    // the last pass's tiles hold the weights of the current r
+            PassKind last_kind = kPassTarget;
             bool any_child = false, accepted = false;
             int k = 0;
             while (true) {
@@ -387,9 +456,14 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
                     continue;
                 }
                 any_child = true;
-                const double pt = s.pc[k], qt = s.qc[k];
-                const double rt = fmax(pt - cj * qt, 0.0) / Mj;
-                if (qt > 0.0 && double(s.u[k]) <= rt / qt) {
+                double ratio;        // r(t) / q(t)
+                if (!measured) {     // r = p: the streaming statistics suffice
+                    const double pt = s.pc[k], qt = s.qc[k];
+                    ratio = qt > 0.0 ? pt / qt : -1.0;
+                } else {
+                    ratio = s.qc[k] > 0.0 ? fmax(wk.p_over_q(k) - cj, 0.0) / Mj : -1.0;
+                }
+                if (ratio >= 0.0 && double(s.u[k]) <= ratio) {
                     const int ch = s.kid[k];
                     if (threadIdx.x == 0) {
                         if (h == 0) a.out_path[int64_t(b) * N + s_nacc] = ch;
@@ -400,9 +474,13 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
                     break;
                 }
                 // Rejected: r <- norm(max(0, r - q)).
-                const double M = wk.run_pass(false, float(cj + Mj));
-                if (M < 0.0) { failed = true; break; }
-                if (M > 0.0) { cj = cj + Mj; Mj = M; tiles_valid = true; }
+                const PassKind kind = measured ? kPassResid : kPassFirst;
+                const double coef = cj + Mj;
+                double Wsum = 0.0;
+                if (!wk.run_pass(kind, coef, &Wsum)) { failed = true; break; }
+                measured = true;
+                const double M = Wsum / wk.A;
+                if (M > 0.0) { cj = coef; Mj = M; tiles_valid = true; last_kind = kind; }
                 else tiles_valid = false;
                 ++k;
             }
@@ -412,11 +490,13 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
             // Every child rejected (or a leaf): draw the bonus from the last
             // residual, or from p when no residual of positive mass was formed.
             const bool from_p = !any_child || cj == 0.0;
-            double W = Mj;
-            if (from_p) W = wk.run_pass(true, 0.0f);
-            else if (!tiles_valid) W = wk.run_pass(false, float(cj));
-            if (W < 0.0) { failed = true; break; }
-            drew = wk.draw(from_p, float(cj), W);
+            double W = Mj * wk.A;
+            PassKind kind = last_kind;
+            bool ok = true;
+            if (from_p) { kind = kPassTarget; ok = wk.run_pass(kPassTarget, 0.0, &W); }
+            else if (!tiles_valid) { kind = kPassResid; ok = wk.run_pass(kPassResid, cj, &W); }
+            if (!ok) { failed = true; break; }
+            drew = wk.draw(kind, kind == kPassTarget ? 0.0 : cj, W);
             break;
         }
         if (failed && threadIdx.x == 0) s_fail = 1;
@@ -424,7 +504,7 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     __syncthreads();
 
     if (h != 0) {  // done with every word of the tree: acknowledge and leave
-        if (threadIdx.x == 0) publish(w.ack + h, 1ull);
+        if (threadIdx.x == 0) publish_pair(w.ack + 2 * h, 1ull, a.epoch);
         return;
     }
     // Walker 0: wait for the other walkers (and the drawn token), write the
@@ -433,22 +513,23 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     if (wave_id() == 0) {
         int ok = 0;
         for (const WaitBound t(a.wait_ticks); !t.expired();) {
-            bool mine = lane_id() == 0 || lane_id() >= a.H || peek(w.ack + lane_id()) != 0ull;
-            if (lane_id() == 0 && drew) mine = peek(w.bonus) != 0ull;
+            bool mine = lane_id() == 0 || lane_id() >= a.H ||
+                        pair_ok(peek(w.ack + 2 * lane_id()), peek(w.ack + 2 * lane_id() + 1), a.epoch);
+            if (lane_id() == 0 && drew) mine = pair_ok(peek(w.bonus), peek(w.bonus + 1), a.epoch);
             if (__all(mine)) { ok = 1; break; }
             __builtin_amdgcn_s_sleep(2);
         }
         if (lane_id() == 0) s_done = ok;
     }
     __syncthreads();
-    if (drew && threadIdx.x == 0) bonus = s_done ? int32_t(uint32_t(peek(w.bonus))) : -1;
+    if (drew && threadIdx.x == 0) bonus = s_done ? int32_t(uint32_t(read_pair(w.bonus, 0))) : -1;
     // No row of the tree may publish after its words are returned to zero.
-    const bool rows_done = !kStreaming || wait_slots(slots, int64_t(2) * N * a.S, a.wait_ticks);
+    const bool rows_done = !kStreaming || wait_pairs(slots, int64_t(2) * N * a.S, a.epoch, a.wait_ticks);
     const bool fail = s_fail || !s_done || !rows_done;
     const int nacc = s_nacc;
     for (int j = nacc + threadIdx.x; j < N; j += kThreads) a.out_path[int64_t(b) * N + j] = -1;
-    zero_slots(slots, int64_t(2) * N * a.S);
-    zero_slots(w.part, kWalkWords);
+    zero_pairs(slots, int64_t(2) * N * a.S);
+    for (int i = threadIdx.x; i < kWalkWords; i += kThreads) clear_word(w.part + i);
     if (threadIdx.x == 0) {
         a.out_nacc[b] = fail ? -1 : nacc;
         a.out_bonus[b] = fail ? -1 : bonus;

@@ -6,13 +6,14 @@
 // sequence, row workgroups stream one chunk of one row each: target rows
 // 0..gamma and (for T > 0) draft rows 0..gamma-1, each read once from HBM
 // with 16-byte loads, and publish the chunk's statistics (online max and sum
-// of 2^(z*c - mc), or the greedy argmax) as one 64-bit atomic word. Then the
-// sequence's H bonus workgroups wait for those words (their writers were
+// of 2^(z*c - mc), or the greedy argmax) as one tagged pair of words. Then
+// the sequence's H bonus workgroups wait for those pairs (their writers were
 // dispatched before them) and resolve the sequence (chain_resolve):
 //   accept tests u_i <= p_t(x_i)/p_d(x_i) in fp64 (one lane per position),
 //   k = first rejection by wave ballot,
 //   bonus by inverse CDF over max(p_t - p_d, 0) of row k, or p_t of row gamma,
 // then the last one writes the outcome and zeroes the words for the next call.
+// The bonus pass's tile sums live in dynamic LDS (tile_lds_bytes).
 #include "specv_chain.hpp"
 
 namespace specv {
@@ -35,11 +36,11 @@ __global__ __launch_bounds__(kThreads) void chain_verify_kernel(ChainArgs a) {
     const int b = pl.b;
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
-    uint64_t* slots = a.slots + int64_t(sidx) * RS;
+    uint64_t* slots = a.slots + 2 * int64_t(sidx) * RS;
     if (w >= RS) {  // bonus workgroup: dispatched after every row of the sequence
         __shared__ ResolveLds lds;
-        chain_resolve<DT>(a, dense_seq<DT>(a, b), T, slots, RS, a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr,
-                          int(w - RS), lds);
+        chain_resolve<DT>(a, dense_seq<DT>(a, b), T, slots, RS, a.tiles ? a.tiles + 4 * int64_t(sidx) * a.ntiles : nullptr,
+                          a.parts ? a.parts + 4 * int64_t(sidx) * a.H : nullptr, int(w - RS), lds);
         return;
     }
     const int chunk = int(w % a.S);
@@ -64,17 +65,18 @@ __global__ __launch_bounds__(kThreads) void chain_verify_kernel(ChainArgs a) {
             word = pack_softmax(acc.m, acc.s);
         }
     }
-    if (threadIdx.x == 0) publish(slots + w, word);
+    if (threadIdx.x == 0) publish_pair(slots + 2 * w, word, a.epoch);
 }
 
 }  // namespace
 
 hipError_t launch_chain(const ChainArgs& a, int dtype, hipStream_t stream) {
     const int64_t grid = int64_t(a.B) * ((2 * a.gamma + 1) * int64_t(a.S) + a.H);
+    const size_t lds = tile_lds_bytes(a.ntiles);
     if (dtype == DT_BF16)
-        hipLaunchKernelGGL(chain_verify_kernel<DT_BF16>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(chain_verify_kernel<DT_BF16>, dim3(unsigned(grid)), dim3(kThreads), lds, stream, a);
     else
-        hipLaunchKernelGGL(chain_verify_kernel<DT_F32>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(chain_verify_kernel<DT_F32>, dim3(unsigned(grid)), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 

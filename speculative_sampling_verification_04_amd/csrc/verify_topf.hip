@@ -60,7 +60,7 @@ union FusedLds {
     } rows;
 };
 
-// The sigma_{F,C} normaliser word of a draft row: its softmax sum Z (relative
+// The sigma_{F,C} normaliser value of a draft row: its softmax sum Z (relative
 // to the reference m*c) loses (1 - C) of its F largest terms; 2 << 32 (no
 // scaling) if nothing would be left.
 __device__ __forceinline__ uint64_t sigma_word(const uint64_t* pick, int F, float c, float mc, double Z, float C) {
@@ -86,8 +86,8 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     const int b = pl.b;
     const float T = a.temperature[b];
     const bool greedy = !(T > 0.0f);
-    const int64_t words = int64_t(R1) * S + (Cache ? 3 * (a.gamma + 1) : 0);  // per sequence
-    uint64_t* slots = a.slots + int64_t(sidx) * words;
+    const int64_t words = int64_t(R1) * S + (Cache ? 3 * (a.gamma + 1) : 0);  // pairs per sequence
+    uint64_t* slots = a.slots + 2 * int64_t(sidx) * words;
     if (slot >= 2 * half) {  // bonus workgroup: dispatched after every row of the sequence
         const int h = slot - 2 * half;
         if (S > 1) {
@@ -99,8 +99,9 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
             for (int row = h; row <= a.gamma; row += a.H) {
                 const int Fk = a.Fk[row];
                 const int F1 = Fk + 1;
-                uint64_t* kw = a.topf_keys + (int64_t(b) * (a.gamma + 1) + row) * S * kTopfKeyWords;
-                const uint64_t* pick = topf_merge_chunks<kTopfKeyWords>(kw, S * F1, F1, lds.merge, a.wait_ticks);
+                uint64_t* kw = a.topf_keys + 2 * (int64_t(b) * (a.gamma + 1) + row) * S * kTopfKeyWords;
+                const uint64_t* pick = topf_merge_chunks<kTopfKeyWords>(kw, S * F1, F1, lds.merge, a.epoch,
+                                                                        a.wait_ticks);
                 const int32_t excl = row < a.gamma ? a.tokens[int64_t(b) * a.gamma + row] : -1;
                 if (threadIdx.x == 0) {
                     const int64_t out = (int64_t(b) * (a.gamma + 1) + row) * a.F;
@@ -109,28 +110,29 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
                 }
                 if (Cache) {
                     const bool scaled = !greedy && row < a.gamma && a.C < 1.0f && Fk > 0;
-                    const uint64_t* rw = slots + int64_t(a.gamma + 1 + row) * S;   // the row's chunk words
+                    const uint64_t* rw = slots + 2 * int64_t(a.gamma + 1 + row) * S;   // the row's chunk pairs
                     __shared__ uint64_t s_zword;
                     if (threadIdx.x == 0) s_zword = 2ull << 32;
-                    if (scaled && wait_slots(rw, S, a.wait_ticks) && wave_id() == 0) {
-                        const RowStats st = merge_chunk_words(lane_id() < S ? peek(rw + lane_id()) : 0ull, S, false,
-                                                              log2e_over(T));
+                    if (scaled && wait_pairs(rw, S, a.epoch, a.wait_ticks) && wave_id() == 0) {
+                        const RowStats st = merge_chunk_words(lane_id() < S ? read_pair(rw, lane_id()) : 0ull, S,
+                                                              false, log2e_over(T));
                         if (lane_id() == 0) s_zword = sigma_word(pick, Fk, log2e_over(T), st.mc, st.Z, a.C);
                     }
                     __syncthreads();
                     if (threadIdx.x == 0) {
-                        uint64_t* extra = slots + int64_t(R1) * S + 3 * row;
-                        publish(extra + 0, s_zword);
-                        publish(extra + 1, Fk > 0 ? topf_sigma_key(pick, Fk) + 1ull : ~0ull);
-                        publish(extra + 2, Fk > 0 ? topf_cache_key(pick, Fk, excl) + 1ull : ~0ull);
+                        uint64_t* extra = slots + 2 * (int64_t(R1) * S + 3 * row);
+                        publish_pair(extra + 0, s_zword, a.epoch);
+                        publish_pair(extra + 2, topf_sigma_key(pick, Fk), a.epoch);
+                        publish_pair(extra + 4, topf_cache_key(pick, Fk, excl), a.epoch);
                     }
                 }
-                zero_slots(kw, S * F1);
+                zero_pairs(kw, S * F1);
                 __syncthreads();
             }
         }
         chain_resolve<DT, false, Cache>(a, dense_seq<DT>(a, b), T, slots, words,
-                                        a.tiles ? a.tiles + int64_t(sidx) * a.ntiles : nullptr, h, lds.resolve);
+                                        a.tiles ? a.tiles + 4 * int64_t(sidx) * a.ntiles : nullptr,
+                                        a.parts ? a.parts + 4 * int64_t(sidx) * a.H : nullptr, h, lds.resolve);
         return;
     }
     const int task = slot / S;               // row slot: target rows 0..gamma, then draft rows
@@ -183,17 +185,17 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
                          : topf_finish<DT, K>(acc, rp, V, Fk, a.F, excl, ids, vals, lds.rows.keys);
         }
         if (S > 1 && threadIdx.x <= Fk) {  // this chunk's Fk + 1 largest keys, for the merge
-            uint64_t* kw = a.topf_keys + (int64_t(b) * (a.gamma + 1) + row) * S * kTopfKeyWords + chunk * (Fk + 1);
-            publish(kw + threadIdx.x, pick[threadIdx.x] + 1ull);
+            uint64_t* kw = a.topf_keys + 2 * ((int64_t(b) * (a.gamma + 1) + row) * S * kTopfKeyWords + chunk * (Fk + 1));
+            publish_pair(kw + 2 * threadIdx.x, pick[threadIdx.x], a.epoch);
         }
         if (Cache && S == 1 && threadIdx.x == 0) {
-            uint64_t* extra = slots + R1 + 3 * row;
-            publish(extra + 0, zword);
-            publish(extra + 1, Fk > 0 ? topf_sigma_key(pick, Fk) + 1ull : ~0ull);
-            publish(extra + 2, Fk > 0 ? topf_cache_key(pick, Fk, excl) + 1ull : ~0ull);
+            uint64_t* extra = slots + 2 * (R1 + 3 * row);
+            publish_pair(extra + 0, zword, a.epoch);
+            publish_pair(extra + 2, topf_sigma_key(pick, Fk), a.epoch);
+            publish_pair(extra + 4, topf_cache_key(pick, Fk, excl), a.epoch);
         }
     }
-    if (threadIdx.x == 0) publish(slots + slot, word);
+    if (threadIdx.x == 0) publish_pair(slots + 2 * slot, word, a.epoch);
 }
 
 template <int DT, bool Cache>
@@ -202,11 +204,12 @@ hipError_t launch_dt(const ChainArgs& a, hipStream_t stream) {
         return hipErrorInvalidValue;   // the merge's LDS and key area
     const dim3 grid(unsigned(int64_t(a.B) * ((2 * a.gamma + 2) * int64_t(a.S) + a.H)));
     const int K = a.F + 1;
-    if (K <= 2) hipLaunchKernelGGL((verify_topf_kernel<DT, 2, Cache>), grid, dim3(kThreads), 0, stream, a);
-    else if (K <= 4) hipLaunchKernelGGL((verify_topf_kernel<DT, 4, Cache>), grid, dim3(kThreads), 0, stream, a);
-    else if (K <= 8) hipLaunchKernelGGL((verify_topf_kernel<DT, 8, Cache>), grid, dim3(kThreads), 0, stream, a);
-    else if (K <= 16) hipLaunchKernelGGL((verify_topf_kernel<DT, 16, Cache>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((verify_topf_kernel<DT, 32, Cache>), grid, dim3(kThreads), 0, stream, a);
+    const size_t lds = tile_lds_bytes(a.ntiles);
+    if (K <= 2) hipLaunchKernelGGL((verify_topf_kernel<DT, 2, Cache>), grid, dim3(kThreads), lds, stream, a);
+    else if (K <= 4) hipLaunchKernelGGL((verify_topf_kernel<DT, 4, Cache>), grid, dim3(kThreads), lds, stream, a);
+    else if (K <= 8) hipLaunchKernelGGL((verify_topf_kernel<DT, 8, Cache>), grid, dim3(kThreads), lds, stream, a);
+    else if (K <= 16) hipLaunchKernelGGL((verify_topf_kernel<DT, 16, Cache>), grid, dim3(kThreads), lds, stream, a);
+    else hipLaunchKernelGGL((verify_topf_kernel<DT, 32, Cache>), grid, dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 

@@ -5,10 +5,8 @@ Parity bar:
 * accept lengths, bonus tokens, tree paths and top-F ids: bit-exact. The one
   allowance is a sequence where the oracle reports a near tie (a threshold
   comparison within 1e-6 of equality: |u - ratio| <= 1e-6, or v*W within
-  1e-6*W of a bucket edge) or an ill-conditioned residual (mass below 1e-3,
-  where fp32 rounding of p_t - p_d is large relative to the mass): such a
-  sequence is still compared, and only if its outcome differs is it counted
-  as excused; excused sequences must stay rare;
+  1e-6*W of a bucket edge): such a sequence is still compared, and only if
+  its outcome differs is it counted (and printed) as excused;
 * p_t(x), p_d(x) and the bonus mass: within 1e-5 absolute.
 """
 import numpy as np
@@ -18,7 +16,6 @@ import oracle
 from speculative_sampling_verification_04_amd import binding
 
 PROB_TOL = 1e-5
-ILL_MASS = 1e-3
 
 
 def log(msg):
@@ -69,21 +66,21 @@ def chain_outcome_equal(gpu, ref, b, n):
 
 
 def excused_bound(n):
-    """Near ties whose outcome may differ: at most a tenth of the batch (one
-    at small batches)."""
+    """A sanity bound on near ties whose outcome differs (each is allowed by
+    the parity bar; many would point at a precision problem): at most a tenth
+    of the batch, one at small batches."""
     return max(1, n // 10)
 
 
 def compare_chain(gpu, ref, seqs, gamma, name):
     """Asserts the parity bar; returns (matched, excused): excused sequences
-    are near ties (or ill-conditioned residuals) whose outcome differs."""
+    are oracle-flagged near ties whose outcome differs."""
     excused, near_equal = [], 0
     for n, b in enumerate(seqs):
         k = ref["num_accepted"][n]
-        ill = k < gamma and ref["bonus_mass"][n] < ILL_MASS
         np.testing.assert_allclose(gpu["probs"][b], ref["probs"][n], atol=PROB_TOL,
                                    err_msg=f"{name}: probs of sequence {b}")
-        if ref["near_tie"][n] or ill:
+        if ref["near_tie"][n]:
             if chain_outcome_equal(gpu, ref, b, n):
                 near_equal += 1
             else:

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_common import ILL_MASS, PROB_TOL, chain_to_dev, log, to_dev
+from gpu_common import PROB_TOL, chain_to_dev, log, to_dev
 from speculative_sampling_verification_04_amd import binding
 
 pytestmark = pytest.mark.gpu
@@ -56,8 +56,8 @@ def run(r, with_draft):
 
 
 def compare(gpu, ref, r, name):
-    """Parity bar of the chain tests: every sequence compared; a near tie (or an
-    ill-conditioned residual) whose outcome differs is excused, and counted."""
+    """Parity bar of the chain tests: every sequence compared; an oracle-flagged
+    near tie whose outcome differs is excused, and counted."""
     excused, near_equal = [], 0
     for b in range(r["B"]):
         o0, o1 = r["offsets"][b], r["offsets"][b + 1]
@@ -65,7 +65,7 @@ def compare(gpu, ref, r, name):
                                    err_msg=f"{name}: probs of sequence {b}")
         k = ref["num_accepted"][b]
         same = gpu["num_accepted"][b] == k and np.array_equal(gpu["tokens"][b], ref["tokens"][b])
-        if ref["near_tie"][b] or (k < o1 - o0 and ref["bonus_mass"][b] < ILL_MASS):
+        if ref["near_tie"][b]:
             if same:
                 near_equal += 1
             else:
