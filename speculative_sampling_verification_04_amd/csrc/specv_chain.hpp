@@ -114,6 +114,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
     const bool greedy = !(T > 0.0f);
     const bool last = h == a.H - 1;
     const float c = greedy ? 0.0f : log2e_over(T);
+    const double c64 = greedy ? 0.0 : 1.4426950408889634 / double(T);   // the bonus weights' exponent scale
     const uint32_t ep = a.epoch;
     const uint64_t* extra = slots + 2 * int64_t(2 * G + 2) * a.S;  // the cache pairs, when a.cache_words
 
@@ -218,7 +219,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
         // probabilities), or p_t of row gamma when every draft was accepted.
         const bool resid = k < gamma && !NoDraft;
         TargetWeights<DT> tgt;
-        tgt.init(q.target(k), c, st[k], a.V, (NoDraft && k < gamma) ? int64_t(q.tokens[k]) : int64_t(-1));
+        tgt.init(q.target(k), c64, st[k], a.V, (NoDraft && k < gamma) ? int64_t(q.tokens[k]) : int64_t(-1));
         ResidualWeights<DT, Cache> res;
         if (resid) {
             if constexpr (!NoDraft) {
@@ -232,7 +233,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
                         top_key = read_pair(extra, 3 * k + 1);
                     }
                 }
-                res.init(q.target(k), q.draft(k), c, st[k], Bq, 1.0, a.V);
+                res.init(q.target(k), q.draft(k), c64, st[k], Bq, 1.0, a.V);
                 res.top_key = top_key;
                 res.log2C = log2(double(a.C));
             }
@@ -306,7 +307,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
         }
         if (bonus < 0) {  // a residual of zero mass (rounding only): p_t of row k
             TargetWeights<DT> pk;
-            pk.init(q.target(k), c, st[k], a.V);
+            pk.init(q.target(k), c64, st[k], a.V);
             double x0 = 0.0, x1 = 0.0;
             weight_tile_range<kBonusTiles>(pk, 0, ntiles, [&](int t, double tw, double) { tl.w[t] = tw; }, x0, x1);
             const double W = tiles_total(tl.w, ntiles);

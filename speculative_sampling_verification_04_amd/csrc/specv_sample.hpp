@@ -293,13 +293,11 @@ __device__ __forceinline__ float exp2m1(float h) {
     return fabsf(h) < 1.0f ? x * s : big;
 }
 
-// Weights of one 8-element group as pass A needs them: w (the weights), q
-// (the residual's second term, 0 unless a correction is pending), and the
-// lane's contributions to the correction sums (psum, pgsum).
-struct GroupW {
-    float w[kLaneElems];
-    float q[kLaneElems];
-    float psum, pgsum;
+// Lane sums of one 8-element group as pass A needs them: of the weights w,
+// of q (the residual's second term, 0 unless a correction is pending), and
+// the lane's contributions to the correction sums p and pg.
+struct GroupSums {
+    float w = 0.0f, q = 0.0f, p = 0.0f, pg = 0.0f;
 };
 
 // Weights p of one row (the bonus after every draft was accepted, a leaf):
@@ -316,29 +314,24 @@ struct TargetWeights {
     int64_t V;
     int64_t excl;
     bool vec;
-    __device__ void init(const void* r, float c_, const RowStats& st, int64_t V_, int64_t excl_ = -1) {
-        row = r; c = double(c_); B = log2_norm(st); V = V_; excl = excl_;
+    __device__ void init(const void* r, double c64, const RowStats& st, int64_t V_, int64_t excl_ = -1) {
+        row = r; c = c64; B = log2_norm(st); V = V_; excl = excl_;
         vec = (reinterpret_cast<uintptr_t>(r) & 15u) == 0;
     }
     __device__ __forceinline__ void load(int64_t j0, Raw& r) const { load_group<DT>(row, j0, V, vec, r.p); }
-    __device__ __forceinline__ void group(const Raw& r, int64_t j0, GroupW& g) const {
+    __device__ __forceinline__ void weights(const Raw& r, int64_t j0, float w[kLaneElems]) const {
         float z[kLaneElems];
         unpack8<DT>(r.p, z);
 #pragma unroll
         for (int e = 0; e < kLaneElems; ++e) {
             const float p = exp2_reduced(fma(double(z[e]), c, -B));   // 0 for z = -inf
-            g.w[e] = (j0 + e == excl) ? 0.0f : p;
-            g.q[e] = 0.0f;
+            w[e] = (j0 + e == excl) ? 0.0f : p;
         }
-        g.psum = 0.0f;
-        g.pgsum = 0.0f;
     }
-    // The weights a pass B tile scan uses: the same as pass A's.
-    __device__ __forceinline__ void weights(const Raw& r, int64_t j0, float w[kLaneElems]) const {
-        GroupW g;
-        group(r, j0, g);
-#pragma unroll
-        for (int e = 0; e < kLaneElems; ++e) w[e] = g.w[e];
+    __device__ __forceinline__ void sums(const Raw& r, int64_t j0, GroupSums& g) const {
+        float w[kLaneElems];
+        weights(r, j0, w);
+        g.w = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
     }
 };
 
@@ -361,9 +354,9 @@ struct ResidualWeights {
     int64_t V;
     bool pvec, qvec;
     float a;               // 1 - 2^-kappa: the correction applied to the weights (0: none)
-    __device__ void init(const void* pr, const void* qr, float c_, const RowStats& sp, double Bq, double coef,
+    __device__ void init(const void* pr, const void* qr, double c64, const RowStats& sp, double Bq, double coef,
                          int64_t V_) {
-        prow = pr; qrow = qr; c = double(c_); Bp = log2_norm(sp);
+        prow = pr; qrow = qr; c = c64; Bp = log2_norm(sp);
         Hk = Bq - Bp - log2(coef);
         log2C = 0.0; top_key = ~0ull; V = V_; a = 0.0f;
         pvec = (reinterpret_cast<uintptr_t>(pr) & 15u) == 0;
@@ -373,40 +366,57 @@ struct ResidualWeights {
         load_group<DT>(prow, j0, V, pvec, r.p);
         load_group<DT>(qrow, j0, V, qvec, r.q);
     }
-    __device__ __forceinline__ void group(const Raw& r, int64_t j0, GroupW& g) const {
+    // Element e of a group: w~ and q~ (0 unless h < 0), and its terms of the
+    // correction sums, p and p (2^h - 1).
+    __device__ __forceinline__ void element(float zp, float zq, int64_t j, double nq, float& wt, float& qt, float& p,
+                                            float& pg) const {
+        const bool top = kTop && full_key(zq, j) >= top_key;
+        const double tp = fma(double(zp), c, -Bp);                   // log2 p~
+        p = exp2_reduced(tp);                                         // 0 for zp = -inf
+        double h = fma(double(zq) - double(zp), c, -Hk);             // log2(coef q / p)
+        if (top) h += log2C;
+        const float em1 = exp2m1(float(h));                          // 2^h - 1 (relative accuracy)
+        wt = fmaxf(p * -em1, 0.0f);                                   // p (1 - 2^h) where h < 0
+        qt = wt > 0.0f ? p - wt : 0.0f;
+        pg = p * em1;                                                 // p (2^h - 1) = coef q~ - p
+        // Where p is 0 (a -inf target logit, or below fp32's range) or 2^h
+        // leaves fp32's range, p (2^h - 1) is coef q~ - p with q~ = 2^tq
+        // formed directly (q's mass where p vanishes). Rare: a wave takes
+        // this branch only if one of its lanes needs it.
+        if (!(p > 0.0f && h < 120.0)) {
+            double tq = fma(double(zq), c, nq);                       // log2 of coef q~
+            if (top) tq += log2C;
+            pg = exp2_reduced(tq) - p;
+            if (!(p > 0.0f)) wt = qt = 0.0f;
+        }
+    }
+    __device__ __forceinline__ void sums(const Raw& r, int64_t j0, GroupSums& g) const {
         float zp[kLaneElems], zq[kLaneElems];
         unpack8<DT>(r.p, zp);
         unpack8<DT>(r.q, zq);
         const double nq = -(Hk + Bp);                                // log2 q~ = zq c [+ log2 C] + nq
-        float ps = 0.0f, pgs = 0.0f;
 #pragma unroll
         for (int e = 0; e < kLaneElems; ++e) {
-            const bool top = kTop && full_key(zq[e], j0 + e) >= top_key;
-            const float p = exp2_reduced(fma(double(zp[e]), c, -Bp));  // 0 for zp = -inf
-            double h = fma(double(zq[e]) - double(zp[e]), c, -Hk);     // log2(coef q / p)
-            double tq = fma(double(zq[e]), c, nq);                      // log2 of coef q~
-            if (top) { h += log2C; tq += log2C; }
-            const float em1 = exp2m1(float(h));                         // 2^h - 1
-            const bool live = p > 0.0f;
-            const bool neg = live && h < 0.0;
-            const float wt = neg ? p * -em1 : 0.0f;
-            g.w[e] = wt;
-            g.q[e] = neg ? p - wt : 0.0f;
-            ps += p;
-            // p (2^h - 1), i.e. coef q~ - p: from the series where |h| < 1;
-            // else q~ - p with q~ = 2^tq formed directly, which stays in range
-            // when p is tiny and 2^h is not, and counts q's mass where p = 0.
-            pgs += (live && h < 1.0) ? p * em1 : exp2_reduced(tq) - p;
+            float wt, qt, p, pg;
+            element(zp[e], zq[e], j0 + e, nq, wt, qt, p, pg);
+            g.w += wt;
+            g.q += qt;
+            g.p += p;
+            g.pg += pg;
         }
-        g.psum = ps;
-        g.pgsum = pgs;
     }
     // The weights of a pass B tile scan: w~ + a q~ on the elements with h < 0.
     __device__ __forceinline__ void weights(const Raw& r, int64_t j0, float w[kLaneElems]) const {
-        GroupW g;
-        group(r, j0, g);
+        float zp[kLaneElems], zq[kLaneElems];
+        unpack8<DT>(r.p, zp);
+        unpack8<DT>(r.q, zq);
+        const double nq = -(Hk + Bp);
 #pragma unroll
-        for (int e = 0; e < kLaneElems; ++e) w[e] = fmaxf(fmaf(a, g.q[e], g.w[e]), 0.0f);
+        for (int e = 0; e < kLaneElems; ++e) {
+            float wt, qt, p, pg;
+            element(zp[e], zq[e], j0 + e, nq, wt, qt, p, pg);
+            w[e] = fmaxf(fmaf(a, qt, wt), 0.0f);
+        }
     }
 };
 
@@ -427,16 +437,14 @@ __device__ __forceinline__ void weight_tile_range(const WFn& f, int t_lo, int t_
 #pragma unroll
         for (int u = 0; u < TIF; ++u) {
             if (t0 + u >= t_hi) break;
-            GroupW g;
-            f.group(raw[u], int64_t(t0 + u) * kTileElems + lane_id() * kLaneElems, g);
-            const float lw = ((g.w[0] + g.w[1]) + (g.w[2] + g.w[3])) + ((g.w[4] + g.w[5]) + (g.w[6] + g.w[7]));
-            const double tw = wave_sum(double(lw));
+            GroupSums g;
+            f.sums(raw[u], int64_t(t0 + u) * kTileElems + lane_id() * kLaneElems, g);
+            const double tw = wave_sum(double(g.w));
             double tq = 0.0;
             if (WFn::kCorrected) {
-                const float lq = ((g.q[0] + g.q[1]) + (g.q[2] + g.q[3])) + ((g.q[4] + g.q[5]) + (g.q[6] + g.q[7]));
-                tq = wave_sum(double(lq));
-                psum += double(g.psum);
-                pgsum += double(g.pgsum);
+                tq = wave_sum(double(g.q));
+                psum += double(g.p);
+                pgsum += double(g.pg);
             }
             if (lane_id() == 0) sink(t0 + u, tw, tq);
         }

@@ -51,7 +51,7 @@ namespace {
 constexpr int kU = 4;          // 16-byte steps per lane per iteration
 constexpr int kD = 0;          // prefetch form (see stream_chunk)
 constexpr int kWalkTiles = 8;       // tiles in flight per wave in a walk pass (walk launch)
-constexpr int kFusedWalkTiles = 4;  // the same in the one-launch form
+constexpr int kFusedWalkTiles = 1;  // the same in the one-launch form (its registers set the rows' occupancy)
 
 __device__ __forceinline__ const void* row_ptr(const RowView& v, int esz, int64_t b, int64_t r) {
     return static_cast<const char*>(v.data) + (b * v.stride_seq + r * v.stride_row) * esz;
@@ -188,6 +188,7 @@ struct Walker {
     const TreeArgs& a;
     int b, h, N, lo, hi;
     float c, v;
+    double c64;                   // exponent scale of the pass weights and p/q ratios (fp64 log2(e)/T)
     WalkWords w;
     WalkLds<NM>& s;
     const void* prow;
@@ -210,11 +211,11 @@ struct Walker {
         auto put = [&](int t, double tw, double tq) { s.tile[t - lo] = tw; s.tile_q[t - lo] = float(tq); };
         if (kind == kPassTarget) {
             TargetWeights<DT> f;
-            f.init(prow, c, s.sp, a.V);
+            f.init(prow, c64, s.sp, a.V);
             weight_tile_range<TIF>(f, lo, hi, put, ps, pgs);
         } else {
             ResidualWeights<DT> f;
-            f.init(prow, qrow, c, s.sp, log2_norm(s.sq), coef, a.V);
+            f.init(prow, qrow, c64, s.sp, log2_norm(s.sq), coef, a.V);
             if (kind == kPassResid) f.Hk += kappa;
             weight_tile_range<TIF>(f, lo, hi, put, ps, pgs);
         }
@@ -324,7 +325,7 @@ struct Walker {
     // known: 2^(kappa - h), h = (zq - zp) c - (B_q - B_p), in fp64 (no
     // difference of probabilities).
     __device__ __forceinline__ double p_over_q(int k) const {
-        const double hk = fma(double(s.zq[k]) - double(s.zp[k]), double(c), -(log2_norm(s.sq) - log2_norm(s.sp)));
+        const double hk = fma(double(s.zq[k]) - double(s.zp[k]), c64, -(log2_norm(s.sq) - log2_norm(s.sp)));
         return exp2(kappa - hk);
     }
 
@@ -352,11 +353,11 @@ struct Walker {
             if (t >= 0) {
                 if (kind == kPassTarget) {
                     TargetWeights<DT> f;
-                    f.init(prow, c, s.sp, a.V);
+                    f.init(prow, c64, s.sp, a.V);
                     bonus = sample_in_tile(f, lo + t, tin);
                 } else {
                     ResidualWeights<DT> f;
-                    f.init(prow, qrow, c, s.sp, log2_norm(s.sq), coef, a.V);
+                    f.init(prow, qrow, c64, s.sp, log2_norm(s.sq), coef, a.V);
                     if (kind == kPassResid) f.Hk += kappa;
                     else f.a = float(correction_a(kappa));
                     bonus = sample_in_tile(f, lo + t, tin);
@@ -431,8 +432,8 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
         }
     } else {  // MSS
         Walker<DT, NM, TIF, kStreaming> wk{a, b, h, N, int(int64_t(a.ntiles) * h / a.H), int(int64_t(a.ntiles) * (h + 1) / a.H),
-                      log2e_over(T), stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(N)), w, s,
-                      nullptr, nullptr};
+                      log2e_over(T), stream_uniform(a.seed, a.offset, uint32_t(b), 1u, uint32_t(N)),
+                      1.4426950408889634 / double(T), w, s, nullptr, nullptr};
         int node = 0;
         bool failed = false;
         while (!failed) {
@@ -547,8 +548,10 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeArgs a) {
 // trees instead of waiting for the end of the whole stream. The walker's LDS
 // is sized for the small trees and its passes keep fewer tiles in flight, so
 // that the row workgroups keep their residency.
+// The walker's registers (about 165) set the whole launch's allocation; the
+// bound keeps it at three workgroups per CU for the row workgroups.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void tree_fused_kernel(TreeArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void tree_fused_kernel(TreeArgs a) {
     const int64_t RS = int64_t(2) * a.N * a.S;
     int b;
     int64_t w;
