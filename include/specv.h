@@ -113,14 +113,22 @@ specv_status specv_verify_workspace_size(int32_t batch, int32_t gamma,
  *                   zero-residual fallback).
  * workspace: device memory of at least specv_verify_workspace_size() bytes,
  *            256-byte aligned. It must be zero-filled before its first use;
- *            every call leaves it zero-filled again, so one workspace can be
- *            reused by calls that are ordered on one stream. Calls that may
- *            run concurrently need separate workspaces. (Workgroups of one
- *            call exchange statistics through it and wait only for
- *            workgroups dispatched before them; the waits are bounded, and a
- *            sequence whose wait ran out reports out_num_accepted = -1, after
- *            which the caller must zero the workspace again. This is not
- *            expected to happen.)
+ *            every call leaves it zero-filled again (but for word 1 of its
+ *            256-byte header, below), so one workspace can be reused by calls
+ *            that are ordered on one stream. Calls that may run concurrently
+ *            need separate workspaces. Workgroups of one call exchange
+ *            statistics through it, every word tagged with the call's own
+ *            epoch (so a word another call left never counts). Enqueues two
+ *            kernels: the verification, and a finisher. A bonus workgroup
+ *            waits for the row workgroups of its sequence, which the map of
+ *            workgroups puts before it, for at most about 1.3 ms; if that
+ *            runs out it marks the sequence deferred and the finisher, which
+ *            starts once every workgroup of the first kernel has finished,
+ *            completes it with the same arithmetic (the outcome is the same).
+ *            So the call drains whatever the order in which the GPU starts
+ *            workgroups and whatever else runs on it. Header word 1 (uint64)
+ *            counts the sequences completed by finishers: a statistic, never
+ *            read by the library, that only grows (0 in normal operation).
  */
 specv_status specv_verify(specv_logits target, specv_logits draft,
                           const int32_t* draft_tokens, const float* temperature,
@@ -300,10 +308,13 @@ specv_status specv_tree_verify_workspace_size(int32_t batch, int32_t nodes,
  * each tree's walk, which follows its tree's rows node by node) and two
  * beyond (the row statistics, then the walks). A walk's passes over a node's
  * rows are shared by up to 16 workgroups per tree that wait for each other
- * and for the tree's rows (each XCD starts workgroups in index order and
- * those they wait for come earlier or beside them, so every tree gets all of
- * its workgroups resident). A wait that times out (about a second) makes that
- * tree report -1.
+ * and for the tree's rows. Each workgroup takes its task number from a
+ * ticket counter in the workspace header (word 0, zero at rest) when it
+ * starts, so tasks are numbered in the order workgroups actually start; a
+ * task waits only for tasks with smaller numbers or for the other walkers of
+ * its tree, whose numbers are consecutive, so every wait is on a task a
+ * running workgroup holds or the next one to start will take. A wait that
+ * still times out (about 1.3 s; not expected) makes that tree report -1.
  */
 specv_status specv_tree_verify(specv_logits target, specv_logits draft,
                                const int32_t* parent, const int32_t* tokens,
@@ -324,14 +335,16 @@ specv_status specv_uniforms(uint64_t seed, uint64_t offset, int32_t tag,
 const char* specv_last_error(void);
 
 /*
- * For tests of the failure path. The kernels' workgroups wait for each
+ * For tests of the bounded waits. The kernels' workgroups wait for each
  * other's published words (row statistics, tile sums, top-F keys, a tree's
- * pass totals); every wait is bounded, by default by 2^27 ticks of the
- * GPU's 100 MHz constant clock (about 1.3 s), and a wait that runs out makes
- * its sequence or tree report -1 instead of hanging. This sets the bound for
- * later calls from any thread (0 restores the default) and returns the
- * previous one. A call whose waits ran out may leave words in its
- * workspace: zero it before the next call. Not for production use.
+ * pass totals); every wait is bounded in ticks of the GPU's 100 MHz constant
+ * clock: a chain call's (specv_verify, specv_verify_topk, specv_verify_cache,
+ * specv_verify_ragged) by min(bound, 2^17), after which the sequence is left
+ * to the call's finisher (same outcome), a tree call's by the bound itself,
+ * by default 2^27 (about 1.3 s), after which the tree reports -1. This sets
+ * the bound for later calls from any thread (0 restores the default) and
+ * returns the previous one. Every call leaves its workspace zero-filled
+ * whether or not its waits ran out. Not for production use.
  */
 uint64_t specv_debug_set_wait_bound(uint64_t ticks);
 

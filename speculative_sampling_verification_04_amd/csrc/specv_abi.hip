@@ -35,9 +35,15 @@ specv_status ok() {
 }
 
 // Bound on the kernels' waits for each other's words (WaitBound ticks); only
-// tests change it (specv_debug_set_wait_bound).
+// tests change it (specv_debug_set_wait_bound). A chain bonus task waits at
+// most kRescueTicks before it defers its sequence to the finisher launch; a
+// tree task's wait that reaches the bound makes its tree report -1.
 std::atomic<uint64_t> g_wait_ticks{kMaxWaitTicks};
 uint64_t wait_ticks() { return g_wait_ticks.load(std::memory_order_relaxed); }
+uint64_t chain_wait_ticks() {
+    const uint64_t t = wait_ticks();
+    return t < kRescueTicks ? t : kRescueTicks;
+}
 
 // Every call tags the values its workgroups publish with a new epoch, so a
 // word left in a workspace by an earlier call (a writer that published after
@@ -53,6 +59,7 @@ uint32_t next_epoch() {
 }
 
 int elem_size(int32_t dtype) { return dtype == SPECV_BF16 ? 2 : 4; }
+
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -86,11 +93,16 @@ specv_status check_workspace(void* ws, size_t have, size_t need) {
 
 RowView view(const specv_logits& l) { return RowView{l.data, l.stride_seq, l.stride_row}; }
 
-// Workspace (every value a tagged pair of 64-bit words, kPair bytes): one
-// pair per row chunk (its statistics); then, when the bonus draw is shared by
-// H > 1 workgroups, two pairs per residual tile of every sequence (the tile's
-// sums of w~ and q~) and two per bonus workgroup (its correction sums).
+// Workspace: a 256-byte header (word 0: a tree launch's ticket counter,
+// TaskQueue, zero at rest; word 1: the number of sequences that chain
+// launches left to their finisher, a statistic that only grows), then every value a tagged pair of 64-bit words (kPair
+// bytes): one pair per row chunk (its statistics); then, when the bonus draw
+// is shared by H > 1 workgroups, two pairs per residual tile of every
+// sequence (the tile's sums of w~ and q~) and two per bonus workgroup (its
+// correction sums); the fused kernel's top-F chunk keys; last, two deferral
+// pairs per sequence (chain launches; the finisher's).
 constexpr size_t kPair = 2 * sizeof(uint64_t);
+constexpr size_t kHeader = 256;
 struct Layout {
     int32_t S;
     int64_t chunk;
@@ -100,7 +112,9 @@ struct Layout {
     size_t tile_bytes;
     size_t part_bytes;
     size_t key_bytes = 0;    // fused kernel with S > 1: the draft-row chunks' top-F keys
-    size_t total() const { return slot_bytes + tile_bytes + part_bytes + key_bytes; }
+    size_t mark_bytes;       // chain launches: two deferral pairs per sequence (the finisher's)
+    size_t mark_offset() const { return kHeader + slot_bytes + tile_bytes + part_bytes + key_bytes; }
+    size_t total() const { return mark_offset() + mark_bytes; }
 };
 
 Layout layout_for(int64_t batch, int64_t row_tasks_per_seq, int64_t vocab) {
@@ -111,6 +125,7 @@ Layout layout_for(int64_t batch, int64_t row_tasks_per_seq, int64_t vocab) {
     L.slot_bytes = round_up(size_t(batch) * row_tasks_per_seq * L.S * kPair);
     L.tile_bytes = L.H > 1 ? round_up(size_t(batch) * L.ntiles * 2 * kPair) : 0;
     L.part_bytes = L.H > 1 ? round_up(size_t(batch) * L.H * 2 * kPair) : 0;
+    L.mark_bytes = round_up(size_t(batch) * 2 * kPair);
     return L;
 }
 
@@ -143,7 +158,9 @@ void set_bonus(ChainArgs& a, const Layout& L, int64_t row_words, void* workspace
     a.chunk = L.chunk;
     a.H = L.H;
     a.ntiles = L.ntiles;
-    char* ws = static_cast<char*>(workspace);
+    a.marks = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.mark_offset());
+    a.deferred = static_cast<uint64_t*>(workspace) + 1;
+    char* ws = static_cast<char*>(workspace) + kHeader;
     a.slots = reinterpret_cast<uint64_t*>(ws);
     a.tiles = L.H > 1 ? reinterpret_cast<uint64_t*>(ws + L.slot_bytes) : nullptr;
     a.parts = L.H > 1 ? reinterpret_cast<uint64_t*>(ws + L.slot_bytes + L.tile_bytes) : nullptr;
@@ -163,10 +180,11 @@ size_t verify_topk_bytes(int64_t batch, int64_t gamma, int64_t vocab) {
     return fused_layout(batch, gamma, vocab).total();
 }
 
-// Tree workspace: the row pairs, then per tree the walk words (the walkers'
-// pass messages, acknowledgements, the drawn token).
+// Tree workspace: the header (ticket counter), the row pairs, then per tree
+// the walk words (the walkers' pass messages, acknowledgements, the drawn
+// token).
 size_t tree_walk_offset(int64_t batch, int64_t nodes, int64_t vocab) {
-    return layout_for(batch, 2 * nodes, vocab).slot_bytes;
+    return kHeader + layout_for(batch, 2 * nodes, vocab).slot_bytes;
 }
 size_t tree_bytes(int64_t batch, int64_t nodes, int64_t vocab) {
     return tree_walk_offset(batch, nodes, vocab) + round_up(size_t(batch) * kWalkWords * sizeof(uint64_t));
@@ -265,7 +283,7 @@ specv_status specv_verify(specv_logits target, specv_logits draft, const int32_t
     if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
 
     ChainArgs a{};
-    a.wait_ticks = wait_ticks();
+    a.wait_ticks = chain_wait_ticks();
     a.target = view(target);
     a.draft = view(draft);
     a.tokens = draft_tokens;
@@ -311,7 +329,7 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
         return st;
 
     ChainArgs a{};
-    a.wait_ticks = wait_ticks();
+    a.wait_ticks = chain_wait_ticks();
     a.target = view(target);
     a.draft = view(draft);
     a.tokens = draft_tokens;
@@ -321,8 +339,8 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
     a.V = vocab;
     set_bonus(a, L, (2 * int64_t(gamma) + 2) * L.S, workspace, elem_size(target.dtype));
     if (L.S > 1)
-        a.topf_keys = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.slot_bytes + L.tile_bytes +
-                                                  L.part_bytes);
+        a.topf_keys = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kHeader + L.slot_bytes +
+                                                  L.tile_bytes + L.part_bytes);
     a.seed = seed;
     a.offset = offset;
     a.out_tokens = out_tokens;
@@ -380,7 +398,7 @@ specv_status specv_verify_cache(specv_logits target, specv_logits draft, const i
     if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
 
     ChainArgs a{};
-    a.wait_ticks = wait_ticks();
+    a.wait_ticks = chain_wait_ticks();
     a.target = view(target);
     a.draft = view(draft);
     a.tokens = draft_tokens;
@@ -390,8 +408,8 @@ specv_status specv_verify_cache(specv_logits target, specv_logits draft, const i
     a.V = vocab;
     set_bonus(a, L, (2 * int64_t(gamma) + 2) * L.S, workspace, elem_size(target.dtype));
     if (L.S > 1)
-        a.topf_keys = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.slot_bytes + L.tile_bytes +
-                                                  L.part_bytes);
+        a.topf_keys = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kHeader + L.slot_bytes +
+                                                  L.tile_bytes + L.part_bytes);
     a.seed = seed;
     a.offset = offset;
     a.out_tokens = out_tokens;
@@ -445,7 +463,7 @@ specv_status specv_verify_ragged(specv_logits target, specv_logits draft, const 
     if ((st = check_workspace(workspace, workspace_bytes, L.total())) != SPECV_OK) return st;
 
     ChainArgs a{};
-    a.wait_ticks = wait_ticks();
+    a.wait_ticks = chain_wait_ticks();
     a.target = view(target);
     a.draft = view(draft);
     a.tokens = draft_tokens;
@@ -563,7 +581,8 @@ specv_status specv_tree_verify(specv_logits target, specv_logits draft, const in
     a.out_path = out_path;
     a.out_nacc = out_num_accepted;
     a.out_bonus = out_bonus;
-    a.slots = static_cast<uint64_t*>(workspace);
+    a.queue = static_cast<uint64_t*>(workspace);
+    a.slots = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kHeader);
     a.H = H;
     a.ntiles = int32_t((int64_t(vocab) + kTileElems - 1) / kTileElems);
     a.D = tree_fused(nodes) ? bonus_delay(batch, 2 * int64_t(nodes) * L.S) : 0;

@@ -12,6 +12,14 @@
 // tile sum as a self-validating word, so the pass runs H-wide instead of on
 // one workgroup. The last one (h = H-1) collects the tile sums, draws the
 // bonus, writes the outcome and returns the words it consumed to zero.
+//
+// Every wait is bounded. In the main launch a wait that runs out makes the
+// last bonus workgroup mark the sequence deferred (its other workgroups just
+// stop), and the finisher launch, which runs after every workgroup of the
+// main launch has finished, resolves it with the same code (Finish = true):
+// one workgroup that computes every helper's tiles itself, with the same
+// arithmetic, so the outcome is the one the main launch would have given.
+
 #pragma once
 
 #include <type_traits>
@@ -100,13 +108,15 @@ __device__ __forceinline__ TileLds tile_lds(int ntiles) {
 // after that; then, with a.cache_words, three cache pairs per draft row from
 // pair (2G + 2) * S). tiles: its tile pairs (two per tile: the sums of w~ and
 // q~) and parts: its helpers' pairs (two per helper: sum p and sum p (2^h -
-// 1)), used when H > 1. NoDraft: the draft has no probabilities (q is the
-// point mass at the drafted token). Cache: the cache pairs exist
-// (a.cache_words; specv_verify_cache only).
-template <int DT, bool NoDraft = false, bool Cache = false>
+// 1)), used when H > 1. mark: the sequence's deferral pair. NoDraft: the
+// draft has no probabilities (q is the point mass at the drafted token).
+// Cache: the cache pairs exist (a.cache_words; specv_verify_cache only).
+// Finish: the finisher's resolve of a deferred sequence (h = H - 1; every
+// word it reads is already published).
+template <int DT, bool NoDraft = false, bool Cache = false, bool Finish = false>
 __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView& q, float T, uint64_t* slots,
-                                              int64_t nslots, uint64_t* tiles, uint64_t* parts, int h,
-                                              ResolveLds& lds) {
+                                              int64_t nslots, uint64_t* tiles, uint64_t* parts, uint64_t* mark,
+                                              int h, ResolveLds& lds) {
     const int b = q.b;
     const int gamma = q.gamma;
     const int G = q.G;
@@ -128,11 +138,23 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
     __shared__ float s_mass;
     __shared__ uint64_t s_cache_word;
 
-    if (!wait_pairs(slots, nslots, ep, a.wait_ticks)) {  // never expected: see wait_pairs
-        if (last) {
+    const uint64_t ticks = Finish ? kMaxWaitTicks : a.wait_ticks;
+    // A wait that ran out: the main launch defers the sequence; the
+    // finisher, for which every word is already published, reports -1 (not
+    // expected) and returns the words to zero.
+    auto give_up = [&]() {
+        if (!last) return;
+        if (Finish) {
             if (threadIdx.x == 0) a.out_nacc[b] = -1;
             zero_pairs(slots, nslots);
+            if (tiles) zero_pairs(tiles, 2 * int64_t(ntiles));
+            if (parts) zero_pairs(parts, 2 * int64_t(a.H));
+        } else if (threadIdx.x == 0) {
+            publish_pair(mark, 1ull, ep);
         }
+    };
+    if (!wait_pairs(slots, nslots, ep, ticks)) {
+        give_up();
         return;
     }
     // One value per row: thread r reads row r's. Several: row r's S chunk
@@ -242,41 +264,41 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
         // Pass A: the tile sums (this workgroup's share when H > 1) and the
         // correction sums.
         double ps = 0.0, pgs = 0.0;
-        const int lo = a.H > 1 ? int(int64_t(ntiles) * h / a.H) : 0;
-        const int hi = a.H > 1 ? int(int64_t(ntiles) * (h + 1) / a.H) : ntiles;
         if (a.H > 1) {
-            auto put = [&](int t, double tw, double tq) {
-                publish_pair(tiles + 4 * t, pack_f64(tw), ep);
-                publish_pair(tiles + 4 * t + 2, pack_f64(tq), ep);
+            // Helper j's share: its tiles' pairs and its correction sums.
+            auto helper = [&](int j) {
+                const int lo = int(int64_t(ntiles) * j / a.H);
+                const int hi = int(int64_t(ntiles) * (j + 1) / a.H);
+                double s0 = 0.0, s1 = 0.0;
+                auto put = [&](int t, double tw, double tq) {
+                    publish_pair(tiles + 4 * t, pack_f64(tw), ep);
+                    publish_pair(tiles + 4 * t + 2, pack_f64(tq), ep);
+                };
+                if (resid) weight_tile_range<kBonusTiles>(res, lo, hi, put, s0, s1);
+                else weight_tile_range<kBonusTiles>(tgt, lo, hi, put, s0, s1);
+                if (resid) {
+                    block_sum2(s0, s1);
+                    if (threadIdx.x == 0) {
+                        publish_pair(parts + 4 * j, pack_f64(s0), ep);
+                        publish_pair(parts + 4 * j + 2, pack_f64(s1), ep);
+                    }
+                }
             };
-            if (resid) weight_tile_range<kBonusTiles>(res, lo, hi, put, ps, pgs);
-            else weight_tile_range<kBonusTiles>(tgt, lo, hi, put, ps, pgs);
-        } else {
-            auto put = [&](int t, double tw, double tq) { tl.w[t] = tw; tl.q[t] = float(tq); };
-            if (resid) weight_tile_range<kBonusTiles>(res, lo, hi, put, ps, pgs);
-            else weight_tile_range<kBonusTiles>(tgt, lo, hi, put, ps, pgs);
-        }
-        if (resid) block_sum2(ps, pgs);
-        if (a.H > 1) {
-            if (resid && threadIdx.x == 0) {
-                publish_pair(parts + 4 * h, pack_f64(ps), ep);
-                publish_pair(parts + 4 * h + 2, pack_f64(pgs), ep);
+            if (Finish) {
+                for (int j = 0; j < a.H; ++j) helper(j);
+            } else {
+                helper(h);
             }
             // Each helper read the row values before publishing its tiles, so
             // once every tile pair is seen the row pairs may be zeroed.
             if (!last) return;
-            const bool ok = wait_pairs(tiles, 2 * int64_t(ntiles), ep, a.wait_ticks) &&
-                            (!resid || wait_pairs(parts, 2 * int64_t(a.H), ep, a.wait_ticks));
+            const bool ok = wait_pairs(tiles, 2 * int64_t(ntiles), ep, ticks) &&
+                            (!resid || wait_pairs(parts, 2 * int64_t(a.H), ep, ticks));
             if (!ok) {
-                if (threadIdx.x == 0) a.out_nacc[b] = -1;
-                zero_pairs(tiles, 2 * int64_t(ntiles));
-                zero_pairs(parts, 2 * int64_t(a.H));
-                zero_pairs(slots, nslots);
+                give_up();
                 return;
             }
             if (resid) {  // the helpers' correction sums, in helper order
-                ps = 0.0;
-                pgs = 0.0;
                 for (int j = 0; j < a.H; ++j) {
                     ps += unpack_f64(read_pair(parts, 2 * j));
                     pgs += unpack_f64(read_pair(parts, 2 * j + 1));
@@ -290,6 +312,10 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
             if (resid) zero_pairs(parts, 2 * int64_t(a.H));
             res.a = float(ca);
         } else {
+            auto put = [&](int t, double tw, double tq) { tl.w[t] = tw; tl.q[t] = float(tq); };
+            if (resid) weight_tile_range<kBonusTiles>(res, 0, ntiles, put, ps, pgs);
+            else weight_tile_range<kBonusTiles>(tgt, 0, ntiles, put, ps, pgs);
+            if (resid) block_sum2(ps, pgs);
             __syncthreads();
             const double ca = resid ? correction_a(correction_kappa(ps, pgs)) : 0.0;
             if (resid) {

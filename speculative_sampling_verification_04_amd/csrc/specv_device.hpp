@@ -25,6 +25,10 @@ constexpr int kLaneElems = 8;               // elements per lane per step
 constexpr int kTileElems = kWaveSize * kLaneElems;  // residual tile: 512
 constexpr int kMaxTiles = 2048;             // vocab <= 2048 * 512
 constexpr uint64_t kMaxWaitTicks = uint64_t(1) << 27;   // default wait bound: ~1.3 s at 100 MHz (WaitBound)
+// Bound on a chain task's wait for another task's words before it defers
+// its sequence to the finisher (~1.3 ms of the 100 MHz clock: far beyond a
+// row's streaming time under full load).
+constexpr uint64_t kRescueTicks = uint64_t(1) << 17;
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
 

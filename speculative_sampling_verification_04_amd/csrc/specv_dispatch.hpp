@@ -3,17 +3,16 @@
 // each workgroup index stands for). Plain integer arithmetic with no GPU
 // types, so that the host (and a CPU test) can check it.
 //
-// Every launch relies on two properties of these maps:
+// The chain launches rely on two properties of these maps:
 //   * each map is a bijection from [0, B * (RS + H)) onto the tasks;
 //   * every bonus workgroup of a sequence comes after all of its rows, and its
 //     H bonus workgroups come in order h = 0 .. H-1 (the last one collects
 //     what the others publish).
-// So a workgroup waits only for workgroups of lower index. Workgroups are
-// dealt to the XCDs in turn and each XCD starts its own in index order, and a
-// waiting workgroup holds its slot. Then the unfinished workgroup of lowest
-// index waits for nothing unfinished, and every workgroup already started on
-// its XCD has a lower index and has finished, so it starts and finishes: the
-// launch always drains.
+// So a bonus workgroup waits only for workgroups of lower index, which the
+// hardware normally starts first: its waits are short. Correctness and
+// termination do not depend on that order: every wait is bounded, and a
+// sequence whose bonus workgroup gives up is completed by the finisher
+// launch, after the whole launch has drained.
 #pragma once
 
 #include <stdint.h>

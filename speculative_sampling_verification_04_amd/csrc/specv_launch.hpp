@@ -67,8 +67,13 @@ struct ChainArgs {
     // tokens[offsets[b] .. offsets[b+1]); gamma is the largest allowed count.
     const int32_t* offsets;
     int32_t num_draft;
-    uint64_t wait_ticks;     // bound on every wait for another workgroup's word (WaitBound)
+    uint64_t wait_ticks;     // bound on a bonus task's wait for other tasks' words; past it the sequence is deferred
     uint32_t epoch;          // this call's tag on every published pair (nonzero)
+    // Deferral marks, two pairs per sequence slot (zero at rest): the
+    // resolve, and (fused kernel) a draft row's top-F merge, left to the
+    // finisher launch.
+    uint64_t* marks;
+    uint64_t* deferred;      // count of the sequences the finisher completed (a statistic; only grows)
 };
 
 // Tree verification. Per tree there are 2N row tasks (target rows of every
@@ -106,6 +111,7 @@ struct TreeArgs {
     int32_t D;
     uint64_t wait_ticks;     // bound on every wait for another workgroup's word (WaitBound)
     uint32_t epoch;          // this call's tag on every published pair (nonzero, low 16 bits too)
+    uint64_t* queue;         // the launch's ticket counter (TaskQueue; zero at rest)
 };
 
 // Trees of up to this many nodes are verified in one launch.

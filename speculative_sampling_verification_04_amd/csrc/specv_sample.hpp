@@ -81,71 +81,144 @@ __device__ __forceinline__ void block_merge_argmax(float& v, int32_t& i) {
 
 constexpr int kMaxOrderedBatch = 4096;
 
-// Where a workgroup of a chain launch sits: its sequence slot, its index in
-// that slot's tasks, and the sequence in the slot.
+// ------------------------------------------------------------ scheduling
+//
+// Two launch disciplines, neither of which depends on the order in which the
+// hardware starts workgroups or on what else runs on the GPU.
+//
+// Chain launches (verify, fused top-F, ragged): workgroup g runs task g of a
+// fixed map (decode_chain, decode_fused) that puts a sequence's bonus tasks
+// after the row tasks whose words they read, so in practice their waits are
+// short. Every wait is bounded (kRescueTicks); a bonus task whose wait runs
+// out gives up and marks its sequence deferred, and a second launch on the
+// same stream (the finisher) resolves the deferred sequences. By then every
+// workgroup of the first launch has finished, so the finisher never waits.
+// No workgroup ever needs another one to start: the first launch drains in
+// bounded time, the finisher has nothing to wait for, and the outcome is the
+// same as without the deferral. The launch needs no shared counter, which
+// would be one atomic per workgroup on one address, all of them at once
+// when the launch starts.
+//
+// Tree launches: the walkers of a tree exchange totals on every pass and
+// cannot stand in for one another, so they need each other running. Each
+// workgroup takes its task number from a ticket counter in the workspace
+// when it starts (TaskQueue), so tasks are numbered in the order in which
+// workgroups actually start. A task waits only for tasks with smaller
+// numbers, which a running workgroup has claimed, or for the other walkers
+// of its tree, whose numbers are consecutive: by induction from the
+// smallest unfinished task, the launch drains whatever the start order.
+
+struct TaskQueue {
+    uint64_t* ticket;
+    int64_t n;          // tasks (n >= 1)
+    // Claim by thread 0 (the caller broadcasts it). The wrapping increment
+    // hands out old and stores (old >= n - 1 ? 0 : old + 1): the claim of
+    // n - 1 leaves the counter at zero for the next launch, with no store
+    // that could race a claim. A counter found at n or above (a workspace
+    // that was not zeroed) is wrapped to zero by that same claim, which then
+    // claims again; from then on every stored value is below n, so the
+    // second claim is in range. The result is clamped all the same: a task
+    // number is always in [0, n).
+    __device__ __forceinline__ int64_t claim() const {
+        const uint64_t last = uint64_t(n - 1);
+        uint64_t t = __builtin_amdgcn_atomic_inc64(ticket, last, __ATOMIC_RELAXED, "agent");
+        if (t > last) t = __builtin_amdgcn_atomic_inc64(ticket, last, __ATOMIC_RELAXED, "agent");
+        return int64_t(t < last ? t : last);
+    }
+};
+
+// One task per workgroup of a tree launch, its number taken from the ticket
+// counter when the workgroup starts: the launch has exactly n workgroups, so
+// its claims are 0 .. n - 1 and leave the counter at zero.
+__device__ __forceinline__ int64_t claim_one(uint64_t* ticket, int64_t n) {
+    __shared__ int64_t s_task;
+    if (threadIdx.x == 0) s_task = TaskQueue{ticket, n}.claim();
+    __syncthreads();
+    return uniform_i64(s_task);
+}
+
+// Dispatch order of the sequences of a chain launch: T > 0 first, then the
+// greedy ones, each group by increasing index (identity when B >
+// kMaxOrderedBatch): only T > 0 sequences re-read a row to draw the bonus, so
+// their bonus tasks come early and overlap the greedy sequences' rows. A
+// workgroup builds the order once (one ballot per 64 temperatures) and maps
+// each task's sequence slot to its sequence.
+struct SeqOrder {
+    uint64_t masks[kMaxOrderedBatch / kWaveSize];   // bit b: sequence b has T > 0
+    int nS;                                          // T > 0 sequences (B when not ordered)
+    int B;
+    bool ordered;
+    // Whole workgroup (wave 0 reads the temperatures).
+    __device__ __forceinline__ void init(const float* temperature, int B_) {
+        if (wave_id() == 0) {
+            const int lane = lane_id();
+            const bool ord = B_ <= kMaxOrderedBatch;
+            int nseq = B_;
+            if (ord) {
+                nseq = 0;
+                const int nm = (B_ + kWaveSize - 1) / kWaveSize;
+                for (int c = 0; c < nm; ++c) {
+                    const int i = c * kWaveSize + lane;
+                    const uint64_t m = __ballot(i < B_ && temperature[i] > 0.0f);
+                    if (lane == 0) masks[c] = m;
+                    nseq += __popcll(m);
+                }
+            }
+            if (lane == 0) { nS = nseq; B = B_; ordered = ord; }
+        }
+        __syncthreads();
+    }
+    // The sequence in slot sidx. Whole wave (the same in every lane).
+    __device__ __forceinline__ int seq_wave(int sidx) const {
+        if (!ordered) return sidx;
+        const bool sampled = sidx < nS;
+        int k = sampled ? sidx : sidx - nS;
+        const int nm = (B + kWaveSize - 1) / kWaveSize;
+        for (int c = 0; c < nm; ++c) {
+            uint64_t m = sampled ? masks[c] : ~masks[c];
+            const int valid = min(kWaveSize, B - c * kWaveSize);
+            if (valid < kWaveSize) m &= (1ull << valid) - 1ull;
+            const int cnt = __popcll(m);
+            if (k < cnt) {   // the k-th set bit of m
+                const bool bit = (m >> lane_id()) & 1ull;
+                const uint64_t hit = __ballot(bit && lanes_below(m) == k);
+                return c * kWaveSize + __builtin_ctzll(hit);
+            }
+            k -= cnt;
+        }
+        return sidx;
+    }
+};
+
+// Where a task of a chain launch sits: its sequence slot, its index in that
+// slot's tasks, and the sequence in the slot.
 struct Placement {
     int sidx;
     int64_t w;
     int b;
 };
 
-// Placement of workgroup g. Sequences are dispatched T > 0 first, then the
-// greedy ones, each group by increasing index (identity when B >
-// kMaxOrderedBatch): only T > 0 sequences re-read a row to draw the bonus, so
-// their bonus workgroups start early and overlap the greedy sequences' rows.
-// decode(nS, sidx, w) maps g to its slot given the number nS of T > 0
-// sequences. Wave 0 computes everything (one round trip for the
-// temperatures, ballots, no serial search); whole workgroup, one barrier.
+// Placement of task t given decode(nS, sidx, w); wave 0 computes, the
+// workgroup gets it through LDS (one barrier), as wave-uniform values (so
+// that what is derived from them stays in scalar registers).
 template <class Decode>
-__device__ __forceinline__ Placement place(const float* temperature, int B, Decode decode) {
-    __shared__ uint64_t masks[kMaxOrderedBatch / kWaveSize];
+__device__ __forceinline__ Placement place_task(const SeqOrder& ord, Decode decode) {
     __shared__ Placement s_pl;
     if (wave_id() == 0) {
-        const int lane = lane_id();
-        const int nm = (B + kWaveSize - 1) / kWaveSize;
-        const bool ordered = B <= kMaxOrderedBatch;
-        int nS = B;
-        if (ordered) {
-            nS = 0;
-            for (int c = 0; c < nm; ++c) {
-                const int i = c * kWaveSize + lane;
-                const uint64_t m = __ballot(i < B && temperature[i] > 0.0f);
-                if (lane == 0) masks[c] = m;
-                nS += __popcll(m);
-            }
-        }
         int sidx;
         int64_t w;
-        decode(nS, sidx, w);
-        int b = sidx;
-        if (ordered) {
-            const bool sampled = sidx < nS;
-            int k = sampled ? sidx : sidx - nS;
-            for (int c = 0; c < nm; ++c) {
-                uint64_t m = sampled ? masks[c] : ~masks[c];
-                const int valid = min(kWaveSize, B - c * kWaveSize);
-                if (valid < kWaveSize) m &= (1ull << valid) - 1ull;
-                const int cnt = __popcll(m);
-                if (k < cnt) {   // the k-th set bit of m
-                    const bool bit = (m >> lane) & 1ull;
-                    const uint64_t hit = __ballot(bit && lanes_below(m) == k);
-                    b = c * kWaveSize + __builtin_ctzll(hit);
-                    break;
-                }
-                k -= cnt;
-            }
-        }
-        if (lane == 0) s_pl = Placement{sidx, w, b};
+        decode(ord.nS, sidx, w);
+        const int b = ord.seq_wave(sidx);
+        if (lane_id() == 0) s_pl = Placement{sidx, w, b};
     }
     __syncthreads();
-    return s_pl;
+    return Placement{__builtin_amdgcn_readfirstlane(s_pl.sidx), uniform_i64(s_pl.w),
+                     __builtin_amdgcn_readfirstlane(s_pl.b)};
 }
 
 // Waits until the n pairs at p (2n words) all carry `tag` (wave 0 polls with
-// agent-scope atomic loads, four loads per lane in flight). Every pair's
-// writer is a workgroup that started before the caller and never waits for
-// it, so the wait ends; it is bounded anyway. Returns false if the bound was
-// reached. Whole workgroup.
+// agent-scope atomic loads, four loads per lane in flight), for at most
+// `ticks`. Returns false if the bound was reached. Whole workgroup.
 __device__ bool wait_pairs(const uint64_t* p, int64_t n, uint32_t tag, uint64_t ticks) {
     __shared__ int s_ok;
     if (wave_id() == 0) {

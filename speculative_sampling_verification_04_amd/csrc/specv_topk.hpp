@@ -190,16 +190,15 @@ __device__ __forceinline__ void topf_write(const uint64_t* pick, int need, int F
 }
 
 // The F1 largest keys of a row searched in chunks, from the chunks' published
-// lists (n pairs at kw: each chunk's F1 largest keys, 0 for none): waits for
-// the n pairs, loads them into mk (LDS, n words) and pops the F1 largest,
-// which are the row's own (each of them is among its chunk's F1 largest).
-// Returns them in LDS, largest first (0 = none; all 0 if the wait ran out).
-// Whole workgroup.
+// lists (n pairs at kw: each chunk's F1 largest keys, 0 for none), which the
+// caller has seen published (ok; if not, nothing is read): loads them into mk
+// (LDS, n words) and pops the F1 largest, which are the row's own (each of
+// them is among its chunk's F1 largest). Returns them in LDS, largest first
+// (0 = none; all 0 without ok). Whole workgroup.
 template <int kMaxKeys>
 __device__ __forceinline__ const uint64_t* topf_merge_chunks(const uint64_t* kw, int n, int F1, uint64_t* mk,
-                                                             uint32_t tag, uint64_t ticks) {
+                                                             bool ok) {
     __shared__ uint64_t s_pick[kMaxKeys];
-    const bool ok = wait_pairs(kw, n, tag, ticks);
     for (int i = threadIdx.x; i < n; i += kThreads) mk[i] = ok ? read_pair(kw, i) : 0ull;
     __syncthreads();
     if (wave_id() == 0) {

@@ -105,7 +105,7 @@ __device__ __forceinline__ void tree_row(const TreeArgs& a, int b, int64_t w) {
 template <int DT>
 __global__ __launch_bounds__(kThreads) void tree_stats_kernel(TreeArgs a) {
     const int64_t RS = int64_t(2) * a.N * a.S;
-    tree_row<DT>(a, int(blockIdx.x / RS), blockIdx.x % RS);
+    tree_row<DT>(a, int(blockIdx.x / RS), blockIdx.x % RS);   // rows never wait: hardware order is fine
 }
 
 // ------------------------------------------------------------------ walk
@@ -537,9 +537,13 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     }
 }
 
+// Walkers of a tree wait for each other: each workgroup takes its walker's
+// number from the ticket counter (claim_one), so a tree's walkers are always
+// claimed by running workgroups or by the next ones to start.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeArgs a) {
-    tree_walk<DT, kMaxTreeNodes, kWalkTiles, false>(a, int(blockIdx.x / a.H), int(blockIdx.x % a.H));
+    const int64_t g = claim_one(a.queue, int64_t(a.B) * a.H);
+    tree_walk<DT, kMaxTreeNodes, kWalkTiles, false>(a, int(g / a.H), int(g % a.H));
 }
 
 // Trees of up to kFusedTreeNodes nodes: rows and walkers in one launch, in the
@@ -553,9 +557,10 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeArgs a) {
 template <int DT>
 __global__ __launch_bounds__(kThreads, 3) void tree_fused_kernel(TreeArgs a) {
     const int64_t RS = int64_t(2) * a.N * a.S;
+    const int64_t g = claim_one(a.queue, int64_t(a.B) * (RS + a.H));   // the one-launch grid (tree_grid)
     int b;
     int64_t w;
-    decode_chain(blockIdx.x, a.B, RS, a.H, a.D, b, w);
+    decode_chain(g, a.B, RS, a.H, a.D, b, w);
     if (w >= RS) tree_walk<DT, kFusedTreeNodes, kFusedWalkTiles, true>(a, b, int(w - RS));
     else tree_row<DT>(a, b, w);
 }
@@ -563,13 +568,12 @@ __global__ __launch_bounds__(kThreads, 3) void tree_fused_kernel(TreeArgs a) {
 template <int DT>
 hipError_t launch_tree_dt(const TreeArgs& a, hipStream_t stream) {
     if (tree_fused(a.N)) {
-        // One launch. Rows never wait; a walker waits for its tree's rows
-        // (lower indices) and for its tree's other walkers (its neighbours in
-        // index order). Each XCD starts its workgroups in index order, so
-        // when the unfinished workgroup of lowest index is a walker, the
-        // workgroups started on any XCD before one of its tree's walkers are
-        // finished ones or that tree's walkers (fewer than an XCD's slots):
-        // all of its tree's walkers get started, and the walk ends.
+        // One launch, one task per workgroup in ticket order (claim_one).
+        // Rows never wait; a walker waits for its tree's rows (smaller
+        // numbers) and for its tree's other walkers (neighbouring numbers).
+        // Every task a waiter depends on is claimed by a running workgroup or
+        // by the next workgroup to start, and rows always finish, so the
+        // launch drains whatever order the hardware starts workgroups in.
         hipLaunchKernelGGL(tree_fused_kernel<DT>, dim3(unsigned(tree_grid(a.B, a.N, a.S, a.H))), dim3(kThreads), 0,
                            stream, a);
         return hipGetLastError();
@@ -578,11 +582,8 @@ hipError_t launch_tree_dt(const TreeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(tree_stats_kernel<DT>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // An ordinary launch: the walkers of a tree wait only for each other, and
-    // each XCD starts its workgroups in index order, so the lowest tree still
-    // walking finds every workgroup started before its walkers finished, or
-    // one of its own walkers; all of its H <= 16 walkers get started, without
-    // the cost of a cooperative launch (~10-20 us here).
+    // The walkers of a tree wait only for each other (tickets, claim_one); a
+    // cooperative launch is not needed (it cost ~10-20 us here).
     hipLaunchKernelGGL(tree_walk_kernel<DT>, dim3(unsigned(int64_t(a.B) * a.H)), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

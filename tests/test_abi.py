@@ -71,14 +71,15 @@ def test_workspace_sizes(lib):
     # every value a 16-byte tagged pair: one per row (256 sequences x 17 rows
     # x 1 chunk), then two per 512-element residual tile of every sequence
     # (251 tiles at V = 128256, shared by ceil(251 / 32) = 8 bonus workgroups)
-    # and two per bonus workgroup
-    assert a == 256 * 17 * 16 + 256 * 251 * 32 + 256 * 8 * 32
+    # and two per bonus workgroup, then two deferral pairs per sequence (after
+    # a 256-byte header holding a tree launch's ticket counter)
+    assert a == 256 + 256 * 17 * 16 + 256 * 251 * 32 + 256 * 8 * 32 + 256 * 32
     st, b = ws_size(lib, "specv_verify_workspace_size", 8, 4, 32000)
     assert st == 0 and b >= 8 * 9 * 16 and b % 256 == 0      # rows split into chunks
     st, t = ws_size(lib, "specv_tree_verify_workspace_size", 32, 64, 152064)
     # row pairs, then 290 walk words per tree (pairs: 2 x 16 pass messages of
     # 4 values, 16 acknowledgements, the drawn token)
-    assert st == 0 and t == 32 * 128 * 16 + 32 * 290 * 8
+    assert st == 0 and t == 256 + 32 * 128 * 16 + 32 * 290 * 8
     st, c = ws_size(lib, "specv_verify_workspace_size", 4, 2, 16000)   # 32 tiles, 2 bonus workgroups at B = 4
     assert st == 0 and c % 256 == 0 and c < 4 * 5 * 64 * 16
     assert ws_size(lib, "specv_verify_workspace_size", 0, 8, 10)[0] == INVALID
@@ -122,17 +123,18 @@ def test_verify_validation(lib):
 
 def test_verify_topk_validation(lib):
     st, n = ws_size(lib, "specv_verify_topk_workspace_size", 256, 8, 128256)
-    # fused: 2*gamma + 2 row pairs per sequence, two pairs per tile, two per bonus workgroup
-    assert st == 0 and n == 256 * 18 * 16 + 256 * 251 * 32 + 256 * 8 * 32
+    # fused: 2*gamma + 2 row pairs per sequence, two pairs per tile, two per
+    # bonus workgroup, two deferral pairs per sequence
+    assert st == 0 and n == 256 + 256 * 18 * 16 + 256 * 251 * 32 + 256 * 8 * 32 + 256 * 32
     # 8 sequences, one chunk per row: 10 row pairs each, then the tiles of the 4
     # bonus workgroups (16 tiles each up to 64 sequences: 63 tiles at V = 32000)
     st, m = ws_size(lib, "specv_verify_topk_workspace_size", 8, 4, 32000)
-    assert st == 0 and m == 8 * 10 * 16 + 8 * 63 * 32 + 8 * 4 * 32
+    assert st == 0 and m == 256 + 8 * 10 * 16 + 8 * 63 * 32 + 8 * 4 * 32 + 8 * 32
     # 2 sequences, rows in 6 chunks: row pairs, tile pairs (196 tiles), the 13
     # bonus workgroups' pairs (rounded up to 256 bytes), then 32 top-F key
-    # pairs per draft-row chunk
+    # pairs per draft-row chunk, then the deferral pairs (rounded up)
     st, m = ws_size(lib, "specv_verify_topk_workspace_size", 2, 3, 100000)
-    assert st == 0 and m == 2 * 8 * 6 * 16 + 2 * 196 * 32 + 1024 + 2 * 4 * 6 * 32 * 16
+    assert st == 0 and m == 256 + 2 * 8 * 6 * 16 + 2 * 196 * 32 + 1024 + 2 * 4 * 6 * 32 * 16 + 256
 
     def call(F=2, B=2, topk=FAKE, tokens=FAKE, ws_bytes=1 << 20, ws=FAKE):
         return lib.specv_verify_topk(L(), L(), tokens, FAKE, B, 3, 10, F, 1, 0, FAKE, FAKE, None, None,
@@ -171,7 +173,7 @@ def test_tree_validation(lib):
 def test_verify_cache_validation(lib):
     st, n = ws_size(lib, "specv_verify_cache_workspace_size", 256, 8, 128256)
     # row pairs + 3 cache pairs per draft row, then the tile and bonus-workgroup pairs
-    assert st == 0 and n == 256 * (18 + 27) * 16 + 256 * 251 * 32 + 256 * 8 * 32
+    assert st == 0 and n == 256 + 256 * (18 + 27) * 16 + 256 * 251 * 32 + 256 * 8 * 32 + 256 * 32
 
     def call(fan=(2, 2, 1, 3), C=0.5, l=1.0, B=2, topk=FAKE, ws_bytes=1 << 20, V=10):
         arr = (ctypes.c_int32 * len(fan))(*fan)

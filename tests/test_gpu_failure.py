@@ -1,20 +1,23 @@
-"""The failure path of the kernels' bounded waits, forced from the host.
+"""The kernels' bounded waits, run out on purpose from the host.
 
 Workgroups wait for each other's published words (row statistics, tile sums,
-top-F keys, a tree's pass totals); every wait is bounded and a wait that runs
-out makes its sequence or tree report -1. Here the bound is set to one tick of
-the 100 MHz clock for one call: the call must still return, and every
-sequence or tree must either report -1 or give the oracle's outcome. The
-bound is then restored and the same call, on the same workspace (which the
-failed call may have left with words written after their readers gave up:
-every call tags its words with its own epoch, so those never count), must
-match the oracle again and leave the workspace zero."""
+top-F keys, a tree's pass totals), and every wait is bounded. Here the bound
+is set to one tick of the 100 MHz clock for one call, so that waits run out.
+A chain launch (verify, verify_topk) then leaves the sequences whose bonus
+workgroups gave up to its finisher launch, which completes them: every
+sequence must still give the oracle's outcome, and the workspace header's
+count of sequences completed that way must have grown. A tree launch has no
+finisher (its walkers need each other): a tree whose wait ran out reports -1,
+the others give the oracle's outcome. The bound is then restored and the
+same call on the same workspace must match the oracle again and leave the
+workspace zero (but for that count)."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
-from gpu_common import (chain_to_dev, compare_chain, compare_tree, log, run_chain_oracle, run_tree_oracle,
+from gpu_common import (chain_to_dev, compare_chain, compare_tree, log, run_chain_oracle, run_tree_oracle, to_dev,
                         tree_to_dev)
 from speculative_sampling_verification_04_amd import binding
 
@@ -40,19 +43,13 @@ def with_short_waits(call):
     return {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
 
 
-def check_chain_or_failed(gpu, ref, seqs, name):
-    failed = [b for b in seqs if gpu["num_accepted"][b] == -1]
-    for n, b in enumerate(seqs):
-        if b in failed or ref["near_tie"][n]:
-            continue
-        assert gpu["num_accepted"][b] == ref["num_accepted"][n], f"{name}: sequence {b}"
-        np.testing.assert_array_equal(gpu["tokens"][b], ref["tokens"][n], err_msg=f"{name}: sequence {b}")
-    log(f"{name}: {len(failed)} of {len(seqs)} sequences reported a wait that ran out")
-    assert failed, f"{name}: no wait ran out: the failure path was not exercised"
+def deferred_count(ws):
+    return int(ws[8:16].view(torch.int64).item())
 
 
-@pytest.mark.parametrize("B,gamma,V,entry", [(64, 4, 20000, "verify"), (3, 4, 40000, "verify_topk")])
-def test_chain_waits_that_run_out_report_minus_one(B, gamma, V, entry):
+@pytest.mark.parametrize("B,gamma,V,entry", [(64, 4, 20000, "verify"), (3, 4, 40000, "verify_topk"),
+                                             (48, 5, 30000, "verify_topk")])
+def test_chain_waits_that_run_out_are_finished(B, gamma, V, entry):
     w = workloads.make_chain(B, gamma, V, dtype="bf16", sigma=3.0, noise=1.0, temps="half0_half1",
                              gen_seed=71 + B, philox_seed=71)
     d = chain_to_dev(w)
@@ -65,11 +62,19 @@ def test_chain_waits_that_run_out_report_minus_one(B, gamma, V, entry):
                                            workspace=ws)
     log(f"short waits: {entry} B={B} gamma={gamma} V={V}")
     ref, seqs = run_chain_oracle(w)
-    check_chain_or_failed(with_short_waits(call), ref, seqs, f"{entry} short waits")
+    gpu = with_short_waits(call)
+    n = deferred_count(ws)
+    log(f"{entry} short waits: the finisher completed {n} of {B} sequences")
+    assert n > 0, f"{entry}: no wait ran out: the deferral path was not exercised"
+    compare_chain(gpu, ref, seqs, gamma, f"{entry} short waits")
+    ws[8:16].zero_()
     out = call()
     torch.cuda.synchronize()
-    gpu = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
-    compare_chain(gpu, ref, seqs, gamma, f"{entry} after short waits")
+    again = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
+    compare_chain(again, ref, seqs, gamma, f"{entry} after short waits")
+    for k in ("tokens", "num_accepted", "probs", "bonus_mass", "topk", "topk_logits"):
+        if k in gpu:   # the finisher's outcome is the main launch's, bit for bit
+            np.testing.assert_array_equal(gpu[k], again[k], err_msg=f"{entry}: {k}")
     assert int(ws.count_nonzero().item()) == 0
 
 
@@ -99,16 +104,51 @@ def test_tree_waits_that_run_out_report_minus_one():
 def test_default_workspace_after_waits_ran_out():
     # The binding's own workspace (one per device and stream): a call whose
     # waits ran out, then ordinary calls on the same default workspace, which
-    # must match the oracle (no zeroing by the caller).
+    # must all match the oracle (no zeroing by the caller).
     w = workloads.make_chain(48, 5, 30000, dtype="bf16", sigma=3.0, noise=1.0, temps="half0_half1",
                              gen_seed=75, philox_seed=75)
     d = chain_to_dev(w)
     call = lambda: binding.verify_topk(d["target"], d["draft"], d["tokens"], d["temperature"], 3, w.seed, 0)
     log("short waits on the default workspace, then ordinary calls")
     ref, seqs = run_chain_oracle(w)
-    check_chain_or_failed(with_short_waits(call), ref, seqs, "default workspace short waits")
+    compare_chain(with_short_waits(call), ref, seqs, w.gamma, "default workspace short waits")
     for rep in range(2):
         out = call()
         torch.cuda.synchronize()
         gpu = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
         compare_chain(gpu, ref, seqs, w.gamma, f"default workspace after short waits ({rep})")
+
+
+@pytest.mark.parametrize("with_draft", [True, False])
+def test_ragged_waits_that_run_out_are_finished(with_draft):
+    # Ragged batches, sequence 5 with offsets that break the contract (its
+    # rows publish skipped values and its finisher work only zeroes them).
+    from test_gpu_ragged import compare, make_ragged
+    r = make_ragged(40, 5, 20000, "bf16", "mixed", 77)
+    offsets = r["offsets"].copy()
+    d = {k: (to_dev(r[k], "bf16", "cuda") if k in ("target", "draft") else torch.from_numpy(r[k]).to("cuda"))
+         for k in ("target", "draft", "tokens", "temperature")}
+    bad = offsets.copy()
+    bad[6] = bad[5] - 1                       # sequence 5: decreasing offsets
+    ws = torch.zeros(binding.verify_ragged_workspace_bytes(40, 5, 20000, with_draft), dtype=torch.uint8, device="cuda")
+    draft = d["draft"] if with_draft else None
+
+    def call(offs):
+        return binding.verify_ragged(d["target"], draft, torch.from_numpy(offs).to("cuda"), d["tokens"],
+                                     d["temperature"], r["G"], r["seed"], 0, workspace=ws)
+
+    log(f"short waits: ragged B=40 G=5 V=20000 with_draft={with_draft}")
+    gpu = with_short_waits(lambda: call(offsets))
+    assert deferred_count(ws) > 0, "ragged: no wait ran out: the deferral path was not exercised"
+    ref = oracle.ragged.verify_ragged_batch(r["target"], r["draft"] if with_draft else None, offsets, r["tokens"],
+                                            r["temperature"], r["seed"], 0, r["G"])
+    compare(gpu, ref, r, "ragged short waits")
+    bad_out = with_short_waits(lambda: call(bad))
+    assert bad_out["num_accepted"][5] == -2
+    ws[8:16].zero_()
+    out = call(offsets)
+    torch.cuda.synchronize()
+    again = {k: v.cpu().numpy() for k, v in out.items() if v is not None}
+    for k in again:
+        np.testing.assert_array_equal(gpu[k], again[k], err_msg=f"ragged: {k}")
+    assert int(ws.count_nonzero().item()) == 0
