@@ -181,6 +181,28 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft,
                                int32_t* out_topk, float* out_topk_logits,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * specv_verify_topk for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument; the workspace is a static array of
+ * 4 MiB in the library, one per GPU, held until the process ends. Shapes whose
+ * specv_verify_topk_workspace_size exceeds 4 MiB are refused with
+ * SPECV_ERR_WORKSPACE (B = 256, gamma = 8, vocab = 128256 needs about 2.1
+ * MiB). Allocates nothing: the first call on a device looks up the array's
+ * address and enqueues a clear of it on `stream`; every call leaves it
+ * zero-filled (but for the statistic word of specv_verify's workspace
+ * header). All calls on one GPU share the array: calls that overlap in time
+ * on one GPU (different streams, or threads) race and must not be made.
+ * Everything else as for specv_verify_topk, outputs identical.
+ */
+specv_status specv_verify_topk_noalloc(specv_logits target, specv_logits draft,
+                                       const int32_t* draft_tokens, const float* temperature,
+                                       int32_t batch, int32_t gamma, int32_t vocab, int32_t F,
+                                       uint64_t seed, uint64_t offset,
+                                       int32_t* out_tokens, int32_t* out_num_accepted,
+                                       float* out_probs, float* out_bonus_mass,
+                                       int32_t* out_topk, float* out_topk_logits, void* stream);
+
 /* Bytes of workspace specv_verify_cache needs for (batch, gamma, vocab). */
 specv_status specv_verify_cache_workspace_size(int32_t batch, int32_t gamma,
                                                int32_t vocab, size_t* bytes);

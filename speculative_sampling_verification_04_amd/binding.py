@@ -19,7 +19,7 @@ STATUS_NAMES = {0: "SPECV_OK", 1: "SPECV_ERR_INVALID_ARG", 2: "SPECV_ERR_WORKSPA
                 3: "SPECV_ERR_UNSUPPORTED", 4: "SPECV_ERR_HIP"}
 
 EXPORTED = ("specv_verify_workspace_size", "specv_verify", "specv_bonus_topk",
-            "specv_verify_topk_workspace_size", "specv_verify_topk",
+            "specv_verify_topk_workspace_size", "specv_verify_topk", "specv_verify_topk_noalloc",
             "specv_tree_verify_workspace_size", "specv_tree_verify",
             "specv_verify_cache_workspace_size", "specv_verify_cache", "specv_geometric_fanout",
             "specv_verify_ragged_workspace_size", "specv_verify_ragged",
@@ -60,6 +60,8 @@ def load_library(path=LIB_PATH):
             "specv_verify_topk_workspace_size": [I32, I32, I32, SZP],
             "specv_verify_topk": [Logits, Logits, P, P, I32, I32, I32, I32, U64, U64,
                                   P, P, P, P, P, P, P, SZ, P],
+            "specv_verify_topk_noalloc": [Logits, Logits, P, P, I32, I32, I32, I32, U64, U64,
+                                          P, P, P, P, P, P, P],
             "specv_tree_verify_workspace_size": [I32, I32, I32, SZP],
             "specv_verify": [Logits, Logits, P, P, I32, I32, I32, U64, U64,
                              P, P, P, P, P, SZ, P],
@@ -241,6 +243,35 @@ def verify_topk(target, draft, draft_tokens, temperature, F, seed, offset=0, *,
                                  _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out["probs"]),
                                  _ptr(out["bonus_mass"]), _ptr(out["topk"]), _ptr(out["topk_logits"]),
                                  _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def verify_topk_noalloc(target, draft, draft_tokens, temperature, F, seed, offset=0, *,
+                        with_probs=True, with_mass=True, with_logits=True, out=None):
+    """verify_topk through specv_verify_topk_noalloc: no workspace (the
+    library's static one; refused beyond 4 MiB). Same outputs."""
+    lib = load_library()
+    B, rows, V = target.shape
+    gamma = rows - 1
+    dev = target.device
+    _int32(draft_tokens, (B, gamma), "draft_tokens")
+    if temperature.dtype != torch.float32 or temperature.shape != (B,) or not temperature.is_contiguous():
+        raise ValueError("temperature must be a contiguous float32 tensor of shape (B,)")
+    if tuple(draft.shape) != (B, rows, V):
+        raise ValueError("draft must be [B, gamma+1, V]")
+    if out is None:
+        out = dict(
+            tokens=torch.empty((B, gamma + 1), dtype=torch.int32, device=dev),
+            num_accepted=torch.empty((B,), dtype=torch.int32, device=dev),
+            probs=torch.empty((B, gamma, 2), dtype=torch.float32, device=dev) if with_probs else None,
+            bonus_mass=torch.empty((B,), dtype=torch.float32, device=dev) if with_mass else None,
+            topk=torch.empty((B, rows, F), dtype=torch.int32, device=dev),
+            topk_logits=torch.empty((B, rows, F), dtype=torch.float32, device=dev) if with_logits else None)
+    _check(lib.specv_verify_topk_noalloc(logits_view(target), logits_view(draft), _ptr(draft_tokens),
+                                         _ptr(temperature), B, gamma, V, F, seed, offset,
+                                         _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out["probs"]),
+                                         _ptr(out["bonus_mass"]), _ptr(out["topk"]), _ptr(out["topk_logits"]),
+                                         _stream(dev)))
     return out
 
 

@@ -7,6 +7,7 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <mutex>
 #include <string>
 
 #include "specv.h"
@@ -227,6 +228,50 @@ hipError_t launch_uniforms(uint64_t seed, uint64_t offset, int32_t tag, int32_t 
     return hipGetLastError();
 }
 
+// The workspace of specv_verify_topk_noalloc: one array per GPU, held until
+// the process ends. Host code never uses the name `scratch` as an address
+// (on the host it stands for the symbol, not device memory): it asks each
+// device for the array's address once (noalloc_scratch) and passes that.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / sizeof(uint64_t)];
+
+__global__ void zero_words_kernel(uint64_t* p, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+        p[i] = 0;
+}
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];   // the array's address on each device, once set up
+}  // namespace
+
+// The array's address on the current device. The first call on a device
+// looks it up (with that device current, as the lookup needs) and enqueues
+// a clear of the whole array on `stream` (a kernel: no memset node, so the
+// call can be captured in a graph). Allocates nothing.
+specv_status noalloc_scratch(hipStream_t stream, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SPECV_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(SPECV_ERR_UNSUPPORTED, "device %d: at most %d devices", dev,
+                                                  kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(SPECV_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s", hipGetErrorString(e));
+        hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(kThreads), 0, stream, static_cast<uint64_t*>(p),
+                           int64_t(kScratchBytes / sizeof(uint64_t)));
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(SPECV_ERR_HIP, "clearing the scratch array failed: %s", hipGetErrorString(e));
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return SPECV_OK;
+}
+
 }  // namespace specv
 
 using namespace specv;
@@ -354,6 +399,26 @@ specv_status specv_verify_topk(specv_logits target, specv_logits draft, const in
                                             static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SPECV_ERR_HIP, "specv_verify_topk launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+specv_status specv_verify_topk_noalloc(specv_logits target, specv_logits draft, const int32_t* draft_tokens,
+                                       const float* temperature, int32_t batch, int32_t gamma, int32_t vocab,
+                                       int32_t F, uint64_t seed, uint64_t offset, int32_t* out_tokens,
+                                       int32_t* out_num_accepted, float* out_probs, float* out_bonus_mass,
+                                       int32_t* out_topk, float* out_topk_logits, void* stream) {
+    specv_status st = check_chain_sizes(batch, gamma, vocab);
+    if (st != SPECV_OK) return st;
+    const size_t need = verify_topk_bytes(batch, gamma, vocab);
+    if (need > kScratchBytes)
+        return fail(SPECV_ERR_WORKSPACE,
+                    "specv_verify_topk_noalloc: batch %d, gamma %d, vocab %d need %zu workspace bytes, more than "
+                    "its static %zu; use specv_verify_topk with a workspace",
+                    batch, gamma, vocab, need, kScratchBytes);
+    void* ws = nullptr;
+    if ((st = noalloc_scratch(static_cast<hipStream_t>(stream), &ws)) != SPECV_OK) return st;
+    return specv_verify_topk(target, draft, draft_tokens, temperature, batch, gamma, vocab, F, seed, offset,
+                             out_tokens, out_num_accepted, out_probs, out_bonus_mass, out_topk, out_topk_logits, ws,
+                             kScratchBytes, stream);
 }
 
 specv_status specv_verify_cache_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, size_t* bytes) {

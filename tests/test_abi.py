@@ -170,6 +170,18 @@ def test_tree_validation(lib):
     assert call(B=0) == INVALID
 
 
+def test_verify_topk_noalloc_refuses_large_shapes(lib):
+    # The static workspace holds 4 MiB: a shape that needs more is refused
+    # with SPECV_ERR_WORKSPACE before anything reaches the GPU.
+    st, need = ws_size(lib, "specv_verify_topk_workspace_size", 4096, 8, 128256)
+    assert st == 0 and need > 4 << 20
+    r = lib.specv_verify_topk_noalloc(L(), L(), FAKE, FAKE, 4096, 8, 128256, 4, 1, 0,
+                                      FAKE, FAKE, None, None, FAKE, None, None)
+    assert r == 2 and b"4194304" in lib.specv_last_error()
+    assert lib.specv_verify_topk_noalloc(L(), L(), FAKE, FAKE, 0, 8, 128256, 4, 1, 0,
+                                         FAKE, FAKE, None, None, FAKE, None, None) == INVALID
+
+
 def test_verify_cache_validation(lib):
     st, n = ws_size(lib, "specv_verify_cache_workspace_size", 256, 8, 128256)
     # row pairs + 3 cache pairs per draft row, then the tile and bonus-workgroup pairs
