@@ -18,106 +18,9 @@
 #pragma once
 
 #include "specv_sample.hpp"
+#include "specv_topk_list.hpp"
 
 namespace specv {
-
-constexpr int kCandCap = 256;                  // candidate groups per wave
-constexpr int32_t kSingle = 0x40000000;       // candidate holds one element, not 8
-
-
-__device__ __forceinline__ uint64_t group_key(float vm, int64_t start) {
-    return (uint64_t(logit_key(vm)) << 32) | uint64_t(~uint32_t(start));
-}
-
-template <int DT, int K>
-struct TopKAcc {
-    static_assert(K >= 1 && K <= 32 && (K & (K - 1)) == 0, "K is a power of two <= 32");
-
-    int32_t* ent;        // this wave's candidates (LDS, kCandCap each): start
-    uint64_t* mkey;      //   index (| kSingle for one element) and group key
-    int count;           // wave-uniform
-    uint64_t theta;      // wave-uniform: K-th largest group key at the last compaction (0: none)
-    float th_val;        // its logit (-inf: none)
-
-    __device__ void init(int32_t* e, uint64_t* k) {
-        ent = e; mkey = k; count = 0;
-        theta = 0; th_val = -INFINITY;
-    }
-
-    __device__ __forceinline__ void push(bool pass, int32_t e, uint64_t key) {
-        const uint64_t m = __ballot(pass);
-        if (pass) {
-            const int pos = count + lanes_below(m);
-            ent[pos] = e;
-            mkey[pos] = key;
-        }
-        count += __popcll(m);
-    }
-
-    // Exact compaction from LDS: the K-th largest recorded group key becomes
-    // theta and only the groups whose key reaches it are kept (nothing
-    // changes while fewer than K candidates exist).
-    __device__ void compact() {
-        if (count < K) return;
-        // Keys are unique: round k finds the largest key below round k-1's.
-        uint64_t kth = ~0ull;
-        for (int k = 0; k < K; ++k) {
-            uint64_t l = 0;
-            for (int i = lane_id(); i < count; i += kWaveSize) {
-                const uint64_t x = mkey[i];
-                if (x < kth && x > l) l = x;
-            }
-            kth = wave_max_u64(l);
-        }
-        if (kth > theta) {
-            theta = kth;
-            th_val = key_logit(uint32_t(kth >> 32));
-        }
-        int n = 0;
-        for (int base = 0; base < count; base += kWaveSize) {
-            const int i = base + lane_id();
-            const bool keep = i < count && mkey[i] >= kth;
-            const int32_t e = keep ? ent[i] : 0;
-            const uint64_t x = keep ? mkey[i] : 0;
-            const uint64_t m = __ballot(keep);
-            if (keep) {
-                const int pos = n + lanes_below(m);
-                ent[pos] = e;
-                mkey[pos] = x;
-            }
-            n += __popcll(m);
-        }
-        count = n;
-    }
-
-    // One block pushes up to kWaveSize * U groups, onto at most
-    // kCandCap - kWaveSize * U (before a compaction) or K (after one): both
-    // must fit the list.
-    template <int U>
-    __device__ __forceinline__ void block(const float (&v)[U][kLaneElems], const int64_t* base, const bool* valid) {
-        static_assert(kWaveSize * U + K <= kCandCap && kWaveSize * U < kCandCap,
-                      "a block's candidates must fit the per-wave list after a compaction");
-        float vm[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) vm[u] = max8(v[u]);
-        if (count > kCandCap - kWaveSize * U) compact();
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bool pass = valid[u] && vm[u] >= th_val;
-            push(pass, int32_t(base[u]), pass ? group_key(vm[u], base[u]) : 0ull);
-        }
-    }
-
-    __device__ __forceinline__ void one(float z, int64_t j, bool ok) {
-        if (count > kCandCap - kWaveSize) compact();
-        const bool pass = ok && z >= th_val;
-        push(pass, int32_t(j) | kSingle, pass ? full_key(z, j) : 0ull);
-    }
-};
-
-// LDS words that topf_pick (and topf_finish) need for their key list.
-template <int K>
-constexpr int topf_keys() { return kWaves * kLaneElems * K; }
 
 // The `need` <= K largest keys of what acc streamed, largest first, in LDS
 // (0 = none): every wave compacts its candidates to at most K groups, the

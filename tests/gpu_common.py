@@ -155,3 +155,24 @@ def compare_tree(gpu, ref, seqs, name):
         f"{len(excused)} near ties differ {excused}")
     assert len(excused) <= excused_bound(len(seqs)), f"{name}: {len(excused)} near ties differ"
     return len(seqs) - len(excused), len(excused)
+
+
+_topf_refs = {}
+
+
+def oracle_topf_all(key, draft, tokens, F):
+    """The oracle's top-F ids and logits of every row of draft [B, R, V]
+    (float64), computed once per key in the test process (the headline's
+    2304 rows take tens of seconds), with progress lines."""
+    if key not in _topf_refs:
+        B = draft.shape[0]
+        ids, vals = [], []
+        for b0 in range(0, B, 32):
+            i, v = oracle.topf.bonus_topf_batch(draft[b0:b0 + 32].astype(np.float64),
+                                                None if tokens is None else tokens[b0:b0 + 32], F)
+            ids.append(i)
+            vals.append(v)
+            log(f"oracle top-F {key}: {min(b0 + 32, B)} of {B} sequences")
+        _topf_refs[key] = (np.concatenate(ids), np.concatenate(vals))
+    return _topf_refs[key]
+

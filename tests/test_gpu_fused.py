@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_common import chain_to_dev, compare_chain, log, run_chain_oracle
+from gpu_common import chain_to_dev, compare_chain, log, oracle_topf_all, run_chain_oracle
 from speculative_sampling_verification_04_amd import binding
 
 pytestmark = pytest.mark.gpu
@@ -67,6 +67,11 @@ def test_fused_equals_separate_and_oracle(name, B, gamma, V, dtype, temps, F):
         np.testing.assert_array_equal(f[k][clear], s[k][clear], err_msg=f"{name}: {k} differs")
     for k in ("probs", "bonus_mass"):
         np.testing.assert_allclose(f[k], s[k], atol=1e-6, err_msg=f"{name}: {k} differs")
+    if name == "headline":   # every row (the oracle's top-F, computed once per test process)
+        ids, vals = oracle_topf_all("headline", workloads.round_to_bf16(w.draft), w.draft_tokens, F)
+        np.testing.assert_array_equal(f["topk"], ids, err_msg=f"{name}: top-F ids")
+        np.testing.assert_array_equal(f["topk_logits"].astype(np.float64), vals, err_msg=f"{name}: top-F logits")
+        return
     sample = list(range(0, w.B, max(1, w.B // 24)))
     for b in sample:
         ids, vals = oracle.topf.bonus_topf_batch(w.draft[b:b + 1].astype(np.float64), w.draft_tokens[b:b + 1], F)

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_common import log, run_topf_gpu, to_dev
+from gpu_common import log, oracle_topf_all, run_topf_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -36,9 +36,13 @@ def check(draft, tokens, F, dtype, rows_to_check=None, name=""):
 
 
 def test_headline_top4():
+    # Every one of the 256 x 9 rows against the oracle.
     w = workloads.make_workload("v128256_bf16_b256_g8")
-    sample = list(range(0, 256, 5))      # 52 sequences x 9 rows through the oracle
-    check(w.draft, w.draft_tokens, w.F, "bf16", sample, "headline")
+    d = to_dev(w.draft, "bf16")
+    ids, vals = run_topf_gpu(d, torch.from_numpy(np.ascontiguousarray(w.draft_tokens, np.int32)).cuda(), w.F)
+    ref_ids, ref_vals = oracle_topf_all("headline", workloads.round_to_bf16(w.draft), w.draft_tokens, w.F)
+    np.testing.assert_array_equal(ids, ref_ids, err_msg="headline top-F ids")
+    np.testing.assert_array_equal(vals.astype(np.float64), ref_vals, err_msg="headline top-F logits")
 
 
 @pytest.mark.parametrize("F", [1, 2, 3, 4, 7, 8, 15, 16, 31])
