@@ -14,8 +14,11 @@ Prints one JSON line: verified rows/s (B * (gamma + 1) per step), the step
 kernel's roofline (algorithmic HBM bytes / its average duration, measured with
 HIP events on the launch stream), the separate specv_verify and
 specv_bonus_topk kernels for reference, and the oracle timed on the host cores
-on a bounded sample of the same workload. A `tree` field times token-tree
-verification (MSS) on 32 trees of 64 nodes over V = 152064 (--no-tree skips).
+(a process pool over the workload's sequences, run before the GPU is used),
+with its outcome compared to the step's on every sequence. A `tree` field
+times token-tree verification (MSS) on 32 trees of 64 nodes over V = 152064
+(--no-tree skips); `configs` times specv_verify on the B = 8, V = 32000 fp32
+and B = 64, V = 128256 peaked bf16 workloads.
 """
 import argparse
 import hashlib
@@ -98,53 +101,97 @@ def measured_traffic(kernel):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s=20.0, gpu=None):
-    """The oracle, as written, on a bounded sample of the workload: whole
-    sequences (verify + top-F), alternating greedy and sampled ones, until
-    the time budget is spent. With `gpu` (the fused step's outputs at the
-    workload's offset, on the host), the sampled sequences' outcomes are then
-    compared with the oracle's, outside the timed loop."""
+# The workload the CPU baseline's worker processes read (inherited through
+# fork: the pool is started before anything touches the GPU).
+_CPU_W = None
+
+
+def _oracle_sequence(b):
+    """The oracle, as written, on sequence b of the workload: verification
+    and top-F."""
     import oracle
 
-    order = []
-    half = w.B // 2
-    for i in range(half):
-        order += [i, half + i]
-    results = []
-    t0 = time.perf_counter()
-    done = 0
-    for b in order:
-        u, v = oracle.philox.chain_uniforms(w.seed, w.offset, b, w.gamma)
-        r = oracle.sampling.verify_sequence(w.target[b].astype(np.float64), w.draft[b].astype(np.float64),
-                                            w.draft_tokens[b], float(w.temperature[b]), u, v)
-        ids, _ = oracle.topf.bonus_topf_batch(w.draft[b:b + 1].astype(np.float64), w.draft_tokens[b:b + 1], w.F)
-        results.append((b, r, ids))
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    rows = done * (w.gamma + 1)
-    line = {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {w.B} sequences (alternating greedy / T=1), verify + top-F, "
-                      f"{rows} rows in {dt:.1f} s, numpy fp64 on one host thread"}
-    if gpu is not None:
-        equal = near = differ = topf_equal = 0
-        for b, r, ids in results:
-            toks = np.full(w.gamma + 1, -1, np.int64)
-            toks[:len(r.tokens)] = r.tokens
-            same = int(gpu["num_accepted"][b]) == r.k and np.array_equal(gpu["tokens"][b], toks)
-            if r.near_tie:
-                near += 1
-            elif same:
-                equal += 1
-            else:
-                differ += 1
-            topf_equal += int(np.array_equal(gpu["topk"][b], ids[0]))
-        line["parity"] = {"sequences": len(results), "outcome_equal": equal, "near_ties": near,
-                          "outcome_differs": differ, "topf_equal": topf_equal,
-                          "note": "the fused step's outcome (k, tokens) and top-F ids against the oracle's on the "
-                                  "sampled sequences; near ties are decisions within 1e-6 of a tie"}
-    return line
+    w = _CPU_W
+    u, v = oracle.philox.chain_uniforms(w.seed, w.offset, b, w.gamma)
+    r = oracle.sampling.verify_sequence(w.target[b].astype(np.float64), w.draft[b].astype(np.float64),
+                                        w.draft_tokens[b], float(w.temperature[b]), u, v)
+    ids, _ = oracle.topf.bonus_topf_batch(w.draft[b:b + 1].astype(np.float64), w.draft_tokens[b:b + 1], w.F)
+    toks = np.full(w.gamma + 1, -1, np.int64)
+    toks[:len(r.tokens)] = r.tokens
+    return b, int(r.k), toks, bool(r.near_tie), ids[0]
+
+
+def _warm(_):
+    import oracle  # noqa: F401
+    return os.getpid()
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, reps=3, max_workers=16):
+    """The oracle over every sequence of the workload (verify + top-F), in a
+    pool of worker processes, one sequence per task, on the host cores
+    available to this process (at most max_workers: the host's share for
+    one GPU); the median of `reps` runs. Must run before the GPU is used (the
+    pool forks). Returns (line, per-sequence oracle results)."""
+    import multiprocessing
+
+    global _CPU_W
+    _CPU_W = w
+    workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+    ctx = multiprocessing.get_context("fork")
+    times, results = [], None
+    with ctx.Pool(workers) as pool:
+        pool.map(_warm, range(workers))
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            res = pool.map(_oracle_sequence, range(w.B), chunksize=1)
+            times.append(time.perf_counter() - t0)
+            results = results or res
+    dt = float(np.median(times))
+    rows = w.B * (w.gamma + 1)
+    line = {"value": rows / dt, "unit": "rows/s", "cores": workers, "kind": "oracle",
+            "sample": f"all {w.B} sequences of the workload (half greedy, half T=1), verify + top-F, {rows} rows, "
+                      f"one sequence per task over {workers} worker processes (numpy fp64); median of {reps} runs "
+                      f"of {', '.join(f'{t:.2f}' for t in times)} s",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+            "gbps": 2 * rows * w.V * 2 / dt / 1e9}
+    return line, results
+
+
+def parity_of(results, gpu):
+    """The fused step's outcome (k, tokens) and top-F ids against the
+    oracle's, sequence by sequence."""
+    equal = near = differ = topf_equal = 0
+    for b, k, toks, near_tie, ids in results:
+        same = int(gpu["num_accepted"][b]) == k and np.array_equal(gpu["tokens"][b], toks)
+        if near_tie:
+            near += 1
+        elif same:
+            equal += 1
+        else:
+            differ += 1
+        topf_equal += int(np.array_equal(gpu["topk"][b], ids))
+    return {"sequences": len(results), "outcome_equal": equal, "near_ties": near, "outcome_differs": differ,
+            "topf_equal": topf_equal,
+            "note": "the fused step's outcome (k, tokens) and top-F ids against the oracle's on every sequence; "
+                    "near ties are decisions within 1e-6 of a tie"}
+
+
+def verify_bytes_of(w):
+    """Logit bytes specv_verify must read: every target row, and a draft row
+    of each T > 0 sequence's gamma positions."""
+    esz = 2 if w.dtype == "bf16" else 4
+    n_sampled = int((w.temperature > 0).sum())
+    return (w.B * (w.gamma + 1) + n_sampled * w.gamma) * w.V * esz
 
 
 def main():
@@ -153,7 +200,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-tree", action="store_true", help="skip the token-tree measurement")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -161,15 +208,20 @@ def main():
               "multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
 
+    import workloads
+
+    w = workloads.make_workload(WORKLOAD)
+    # The CPU baseline first: its worker processes are forked before this
+    # process touches the GPU.
+    cpu_line, cpu_results = (None, None) if args.no_cpu_baseline else cpu_baseline(w, args.cpu_reps)
+
     import torch
 
-    import workloads
     from speculative_sampling_verification_04_amd import binding
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     binding.load_library()
-    w = workloads.make_workload(WORKLOAD)
     target = torch.from_numpy(w.target).to(dev).to(torch.bfloat16)
     draft = torch.from_numpy(w.draft).to(dev).to(torch.bfloat16)
     sets = [(target, draft)] + [(target.clone(), draft.clone()) for _ in range(INPUT_SETS - 1)]
@@ -301,6 +353,31 @@ def main():
                 "mean_accepted": float(tout["num_accepted"].float().mean().item())}
         del tt, td, tsets, tws
 
+    # Configurations 2 and 3: specv_verify alone, on enough copies of the
+    # inputs that the calls in turn read past the 256 MB Infinity Cache
+    # (config 2's 9.2 MB, config 3's 180.6 MB). Not part of the step.
+    configs = {}
+    for cname, n_sets in (("v32000_f32", 32), ("v128256_bf16_peaked", 4)):
+        wc = workloads.make_workload(cname)
+        cdt = torch.bfloat16 if wc.dtype == "bf16" else torch.float32
+        ct = torch.from_numpy(wc.target).to(dev).to(cdt)
+        cd = torch.from_numpy(wc.draft).to(dev).to(cdt)
+        csets = [(ct, cd)] + [(ct.clone(), cd.clone()) for _ in range(n_sets - 1)]
+        ctok = torch.from_numpy(wc.draft_tokens).to(dev)
+        ctemp = torch.from_numpy(wc.temperature).to(dev)
+        cws_v = torch.zeros(binding.verify_workspace_bytes(wc.B, wc.gamma, wc.V), dtype=torch.uint8, device=dev)
+        cvout = binding.verify(ct, cd, ctok, ctemp, wc.seed, 0, workspace=cws_v)
+        c_ms = timed(lambda i: binding.verify(*csets[i % n_sets], ctok, ctemp, wc.seed, i, workspace=cws_v,
+                                              out=cvout), n=100)
+        c_bytes = verify_bytes_of(wc)
+        c_rows = wc.B * (wc.gamma + 1)
+        configs[cname] = {"entry": "specv_verify", "B": wc.B, "gamma": wc.gamma, "V": wc.V, "logits": wc.dtype,
+                          "input_sets": n_sets, "avg_ms": c_ms, "rows_per_s": c_rows / (c_ms * 1e-3),
+                          "algorithmic_bytes": c_bytes, "gbps": c_bytes / (c_ms * 1e-3) / 1e9,
+                          "frac": c_bytes / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                          "mean_accepted": float(cvout["num_accepted"].float().mean().item())}
+        del ct, cd, csets, cws_v
+
     # Yardstick for the memory counters and for what a plain streaming kernel
     # reaches: torch's elementwise negation of 1 GiB of int32 (reads 1 GiB, writes
     # 1 GiB; larger than the 256 MB last-level cache), outside the timed region.
@@ -349,12 +426,14 @@ def main():
         "cache": cache,
         "ragged": ragged,
         "tree": tree,
+        "configs": configs,
     }
-    if not args.no_cpu_baseline:
+    if cpu_line is not None:
         ref_out = binding.verify_topk(target, draft, tokens, temp, F, w.seed, w.offset)
         torch.cuda.synchronize()
         gpu = {k: ref_out[k].cpu().numpy() for k in ("tokens", "num_accepted", "topk")}
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, gpu)
+        cpu_line["parity"] = parity_of(cpu_results, gpu)
+        line["cpu_baseline"] = cpu_line
     print(json.dumps(line), flush=True)
 
 
