@@ -55,11 +55,11 @@ __global__ __launch_bounds__(kThreads) void ragged_verify_kernel(ChainArgs a) {
     __shared__ ResolveLds lds;
     ord.init(a.temperature, a.B);
     const Placement pl = place_task(ord, [&](int, int& s, int64_t& w) {
-        decode_chain(blockIdx.x, a.B, RS, a.H, a.D, s, w);
+        decode_chain(blockIdx.x, a.B, ord.nS, RS, a.H, a.D, s, w);
     });
     const int sidx = pl.sidx;   // dispatch slot of the sequence
     const int b = pl.b;
-    const float T = a.temperature[b];
+    const float T = ord.temperature_of(a.temperature, b);
     const bool greedy = !(T > 0.0f);
     const int32_t o0 = a.offsets[b], o1 = a.offsets[b + 1];
     const bool valid = o0 >= 0 && o0 <= o1 && o1 <= a.num_draft && o1 - o0 <= G;
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void ragged_finish_kernel(ChainArgs a) {
     const int32_t o0 = a.offsets[b], o1 = a.offsets[b + 1];
     const bool valid = o0 >= 0 && o0 <= o1 && o1 <= a.num_draft && o1 - o0 <= G;
     if (valid) {
-        chain_resolve<DT, NoDraft, false, true>(a, ragged_seq<DT, NoDraft>(a, b, o0, o1 - o0), a.temperature[b], slots,
+        chain_resolve<DT, NoDraft, false, true>(a, ragged_seq<DT, NoDraft>(a, b, o0, o1 - o0), ord.temperature_of(a.temperature, b), slots,
                                                 RS, a.tiles ? a.tiles + 4 * int64_t(sidx) * a.ntiles : nullptr,
                                                 a.parts ? a.parts + 4 * int64_t(sidx) * a.H : nullptr, mark, a.H - 1,
                                                 lds);

@@ -32,7 +32,7 @@ namespace specv {
 // Tiles in flight per wave in the bonus pass: the pass is spread over H
 // workgroups, and it shares the kernel's register allocation with the
 // streaming code, so one tile per wave keeps the streaming occupancy.
-constexpr int kBonusTiles = 1;
+constexpr int kBonusTiles = 2;
 
 __device__ __forceinline__ const void* row_ptr(const RowView& v, int esz, int64_t b, int64_t r) {
     return static_cast<const char*>(v.data) + (b * v.stride_seq + r * v.stride_row) * esz;

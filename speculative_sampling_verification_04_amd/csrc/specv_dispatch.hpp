@@ -70,12 +70,16 @@ inline SPECV_HD int32_t bonus_delay(int64_t B, int64_t RS) {
     return int32_t(d < B ? d : B);
 }
 
-// Chain launch: unit u = the RS row workgroups of the sequence in dispatch
-// slot u (u < B), then the H bonus workgroups of sequence u - D (u >= D).
-// Maps workgroup g to its sequence slot and its index w in that sequence
-// (w < RS: row chunk w; else bonus workgroup w - RS). 0 <= D <= B.
-inline SPECV_HD void decode_chain(int64_t g, int64_t B, int64_t RS, int64_t H, int64_t D, int& sidx,
+// Chain launch: slots 0 .. nS-1 hold the T > 0 sequences, nS .. B-1 the
+// greedy ones (nS = B: identity order). Unit u = the RS row workgroups of
+// the sequence in slot u (u < B), then the H bonus workgroups of slot u - D
+// (u >= D); units B .. B+D-1 hold the rest of the bonus workgroups: those of
+// T > 0 slots in order, then the last one of each greedy slot (the only one
+// with work), then the other greedy ones, which return at once. Maps workgroup g to its slot and its index w in the
+// slot's tasks (w < RS: row chunk w; else bonus workgroup w - RS).
+inline SPECV_HD void decode_chain(int64_t g, int64_t B, int64_t nS, int64_t RS, int64_t H, int64_t D, int& sidx,
                                   int64_t& w) {
+    if (D > B) D = B;
     const int64_t a_end = D * RS;                      // units 0..D-1: rows only
     const int64_t b_end = a_end + (B - D) * (RS + H);  // units D..B-1: rows, then bonus of u - D
     if (g < a_end) {
@@ -86,10 +90,23 @@ inline SPECV_HD void decode_chain(int64_t g, int64_t B, int64_t RS, int64_t H, i
         const int64_t o = (g - a_end) % (RS + H);
         sidx = int(o < RS ? u : u - D);
         w = o;
-    } else {                                           // units B..B+D-1: bonus only
+    } else {                                           // the bonus of slots B-D .. B-1
         const int64_t i = g - b_end;
-        sidx = int(B - D + i / H);
-        w = RS + i % H;
+        const int64_t s0 = B - D;
+        const int64_t nT = nS > s0 ? nS - s0 : 0;      // T > 0 slots among them
+        const int64_t g0 = s0 + nT;                    // the first greedy one
+        const int64_t nG = B - g0;
+        if (i < nT * H) {
+            sidx = int(s0 + i / H);
+            w = RS + i % H;
+        } else if (i - nT * H < nG) {
+            sidx = int(g0 + (i - nT * H));
+            w = RS + H - 1;
+        } else {
+            const int64_t j = i - nT * H - nG;
+            sidx = int(g0 + j % nG);
+            w = RS + j / nG;
+        }
     }
 }
 
@@ -99,11 +116,14 @@ inline SPECV_HD void decode_chain(int64_t g, int64_t B, int64_t RS, int64_t H, i
 // rows in all. The rows come in B units of RS workgroups: first the T > 0
 // sequences (unit u = sequence u), then the greedy sequences' rows as one
 // list, all draft rows (top-K: the longest rows) before all target rows
-// (argmax: the shortest). The H bonus workgroups of T > 0 sequence v follow
-// row unit v + D, so their draws (which re-read a row) overlap later rows,
-// greedy ones included; the greedy sequences' bonus workgroups come last.
-// The launch thus ends on its shortest rows: longest first keeps the partly
-// idle tail of the launch short. With nS = B this is decode_chain.
+// (argmax: the shortest); within a T > 0 unit the draft rows (softmax and
+// top-K, the slowest) come before the target rows. The H bonus workgroups of
+// T > 0 sequence v follow row unit v + D, so their draws (which re-read a
+// row) overlap later rows, greedy ones included. The greedy sequences' bonus
+// workgroups come last: first the last one (h = H-1, the only one with work:
+// the greedy bonus is an argmax of published words) of each, then the
+// others, which return at once. The launch thus ends on its shortest rows
+// and cheapest tasks.
 inline SPECV_HD void decode_fused(int64_t g, int64_t B, int64_t nS, int64_t half, int64_t H, int64_t D, int& sidx,
                                   int64_t& w) {
     const int64_t RS = 2 * half;
@@ -133,14 +153,20 @@ inline SPECV_HD void decode_fused(int64_t g, int64_t B, int64_t nS, int64_t half
         sidx = int(u2 - D + (g - r3) / H);
         w = RS + (g - r3) % H;
         return;
-    } else {                                            // greedy bonus workgroups
-        sidx = int(nS + (g - r4) / H);
-        w = RS + (g - r4) % H;
+    } else {                                            // greedy bonus workgroups: the last of each, then the rest
+        const int64_t i = g - r4;
+        if (i < nG) {
+            sidx = int(nS + i);
+            w = RS + H - 1;
+        } else {
+            sidx = int(nS + (i - nG) % nG);
+            w = RS + (i - nG) / nG;
+        }
         return;
     }
     if (u < nS) {
         sidx = int(u);
-        w = o;
+        w = o < half ? o + half : o - half;             // draft rows first
         return;
     }
     const int64_t k = (u - nS) * RS + o;                // index in the greedy row list

@@ -144,7 +144,9 @@ __device__ __forceinline__ int64_t claim_one(uint64_t* ticket, int64_t n) {
 // workgroup builds the order once (one ballot per 64 temperatures) and maps
 // each task's sequence slot to its sequence.
 struct SeqOrder {
+    static constexpr int kKeptTemps = 256;          // batches up to this keep their temperatures here
     uint64_t masks[kMaxOrderedBatch / kWaveSize];   // bit b: sequence b has T > 0
+    float temps[kKeptTemps];
     int nS;                                          // T > 0 sequences (B when not ordered)
     int B;
     bool ordered;
@@ -159,7 +161,9 @@ struct SeqOrder {
                 const int nm = (B_ + kWaveSize - 1) / kWaveSize;
                 for (int c = 0; c < nm; ++c) {
                     const int i = c * kWaveSize + lane;
-                    const uint64_t m = __ballot(i < B_ && temperature[i] > 0.0f);
+                    const float t = i < B_ ? temperature[i] : 0.0f;
+                    if (B_ <= kKeptTemps && i < B_) temps[i] = t;
+                    const uint64_t m = __ballot(t > 0.0f);
                     if (lane == 0) masks[c] = m;
                     nseq += __popcll(m);
                 }
@@ -167,6 +171,12 @@ struct SeqOrder {
             if (lane == 0) { nS = nseq; B = B_; ordered = ord; }
         }
         __syncthreads();
+    }
+    // Sequence b's temperature: from LDS when init kept it (no second
+    // round trip to memory before the task can start), else from memory.
+    __device__ __forceinline__ float temperature_of(const float* temperature, int b) const {
+        const float t = (ordered && B <= kKeptTemps) ? temps[b] : temperature[b];
+        return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t)));
     }
     // The sequence in slot sidx. Whole wave (the same in every lane).
     __device__ __forceinline__ int seq_wave(int sidx) const {

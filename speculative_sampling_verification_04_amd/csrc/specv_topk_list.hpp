@@ -9,12 +9,12 @@
 // bookkeeping can also be compiled on the host against an emulated wave.
 //
 // Bookkeeping invariant: a wave's list never holds more than kCandCap
-// entries. A block of U steps pushes at most kWaveSize * U entries; it first
-// compacts a list holding more than kCandCap - kWaveSize * U down to K (keys
-// are unique, so exactly K are kept), so after the block the list holds at
-// most max(kCandCap - kWaveSize * U, K) + kWaveSize * U <= kCandCap entries,
-// which the static_assert in block() requires of every instantiation (one()
-// is the case U = 1). After the final compaction a wave keeps at most K
+// entries. Each step (of a block, or one()) pushes at most kWaveSize
+// entries; it first compacts a list holding more than kCandCap - kWaveSize
+// down to K (keys are unique, so exactly K are kept), so after the step the
+// list holds at most max(kCandCap - kWaveSize, K) + kWaveSize <= kCandCap
+// entries, which the static_assert in block() requires (kWaveSize + K <=
+// kCandCap), whatever the number of steps per block. After the final compaction a wave keeps at most K
 // entries of at most kLaneElems elements each, so the keys gathered from all
 // waves fit topf_keys<K>().
 #pragma once
@@ -90,19 +90,18 @@ struct TopKAcc {
         count = n;
     }
 
-    // One block pushes up to kWaveSize * U groups, onto at most
-    // kCandCap - kWaveSize * U (before a compaction) or K (after one): both
-    // must fit the list.
+    // Each step of a block pushes up to kWaveSize groups, onto at most
+    // kCandCap - kWaveSize (before a compaction) or K (after one): both fit
+    // the list, whatever the number of steps U.
     template <int U>
     __device__ __forceinline__ void block(const float (&v)[U][kLaneElems], const int64_t* base, const bool* valid) {
-        static_assert(kWaveSize * U + K <= kCandCap && kWaveSize * U < kCandCap,
-                      "a block's candidates must fit the per-wave list after a compaction");
+        static_assert(kWaveSize + K <= kCandCap, "a step's candidates must fit the per-wave list after a compaction");
         float vm[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) vm[u] = max8(v[u]);
-        if (count > kCandCap - kWaveSize * U) compact();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            if (count > kCandCap - kWaveSize) compact();
             const bool pass = valid[u] && vm[u] >= th_val;
             push(pass, int32_t(base[u]), pass ? group_key(vm[u], base[u]) : 0ull);
         }

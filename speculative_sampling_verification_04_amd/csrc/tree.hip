@@ -560,7 +560,7 @@ __global__ __launch_bounds__(kThreads, 3) void tree_fused_kernel(TreeArgs a) {
     const int64_t g = claim_one(a.queue, int64_t(a.B) * (RS + a.H));   // the one-launch grid (tree_grid)
     int b;
     int64_t w;
-    decode_chain(g, a.B, RS, a.H, a.D, b, w);
+    decode_chain(g, a.B, a.B, RS, a.H, a.D, b, w);
     if (w >= RS) tree_walk<DT, kFusedTreeNodes, kFusedWalkTiles, true>(a, b, int(w - RS));
     else tree_row<DT>(a, b, w);
 }

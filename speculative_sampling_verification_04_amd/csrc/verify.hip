@@ -34,11 +34,11 @@ __global__ __launch_bounds__(kThreads) void chain_verify_kernel(ChainArgs a) {
     const int64_t RS = int64_t(R) * a.S;                 // row tasks per sequence
     ord.init(a.temperature, a.B);
     const Placement pl = place_task(ord, [&](int, int& s, int64_t& w) {
-        decode_chain(blockIdx.x, a.B, RS, a.H, a.D, s, w);
+        decode_chain(blockIdx.x, a.B, ord.nS, RS, a.H, a.D, s, w);
     });
     const int sidx = pl.sidx;   // dispatch slot of the sequence
     const int b = pl.b;
-    const float T = a.temperature[b];
+    const float T = ord.temperature_of(a.temperature, b);
     const bool greedy = !(T > 0.0f);
     uint64_t* slots = a.slots + 2 * int64_t(sidx) * RS;
     // Row task w of the sequence: chunk w % S of row slot w / S, published
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void chain_finish_kernel(ChainArgs a) {
     ord.init(a.temperature, a.B);
     const int b = uniform_i64(ord.seq_wave(sidx));
     const int64_t RS = int64_t(2 * a.gamma + 1) * a.S;
-    chain_resolve<DT, false, false, true>(a, dense_seq<DT>(a, b), a.temperature[b], a.slots + 2 * int64_t(sidx) * RS,
+    chain_resolve<DT, false, false, true>(a, dense_seq<DT>(a, b), ord.temperature_of(a.temperature, b), a.slots + 2 * int64_t(sidx) * RS,
                                           RS, a.tiles ? a.tiles + 4 * int64_t(sidx) * a.ntiles : nullptr,
                                           a.parts ? a.parts + 4 * int64_t(sidx) * a.H : nullptr, mark, a.H - 1, lds);
     zero_pairs(mark, 2);

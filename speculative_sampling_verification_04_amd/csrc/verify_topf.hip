@@ -29,7 +29,7 @@ namespace {
 // Streaming shapes (16-byte steps per lane per iteration; 0 = prefetch form):
 // target rows carry only the softmax or argmax, draft rows also the top-K.
 constexpr int kTargetU = 4, kTargetD = 0;
-constexpr int kDraftU = 2, kDraftD = 0;
+constexpr int kDraftU = 4, kDraftD = 0;
 
 template <int DT, int K>
 struct SoftmaxTopK {
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void verify_topf_kernel(ChainArgs a) {
     });
     const int sidx = pl.sidx;
     const int b = pl.b;
-    const float T = a.temperature[b];
+    const float T = ord.temperature_of(a.temperature, b);
     const bool greedy = !(T > 0.0f);
     const int64_t words = int64_t(R1) * S + (Cache ? 3 * (a.gamma + 1) : 0);  // pairs per sequence
     uint64_t* slots = a.slots + 2 * int64_t(sidx) * words;
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void topf_finish_kernel(ChainArgs a) {
     if (threadIdx.x == 0) __hip_atomic_fetch_add(a.deferred, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     ord.init(a.temperature, a.B);
     const int b = uniform_i64(ord.seq_wave(sidx));
-    const float T = a.temperature[b];
+    const float T = ord.temperature_of(a.temperature, b);
     const bool greedy = !(T > 0.0f);
     const int S = a.S;
     const int64_t words = int64_t(2 * a.gamma + 2) * S + (Cache ? 3 * (a.gamma + 1) : 0);

@@ -2,8 +2,7 @@
 csrc/specv_topk_list.hpp): tests/topk_list_host.cpp compiles the same header
 with g++ against an emulated 64-lane wave and feeds it rows the way the
 streaming loop does (all equal, strictly ascending, ascending by step,
-descending, random, -inf/-0/+0), for U = 1 and the shipped U = 2 and every
-K. After every push and compaction the list must hold <= kCandCap entries,
+descending, random, -inf/-0/+0), for U = 1, 2, 4 and 8 and every K. After every push and compaction the list must hold <= kCandCap entries,
 and the keys gathered after the final compaction must fit topf_keys<K>() and
 contain the K largest. A wider streaming shape must pass this before it runs
 on a GPU."""

@@ -7,7 +7,7 @@
 // kCandCap, so an overflow is seen by the checks instead of corrupting
 // memory.
 //
-// For each shipped steps-per-iteration U (and U = 1, the tail's one()), each
+// For each steps-per-iteration U up to 8 (U = 1 also covers the tail's one()), each
 // K and each row shape, one wave is fed a row the way stream_chunk feeds it
 // (lane l of wave 0 sees step it * 256 * U + u * 256 + l of 8 elements, then
 // the tail one element per lane) and after every block() / one() the list's
@@ -226,7 +226,9 @@ void all_k() {
 
 int main() {
     all_k<1>();   // one() and single-step blocks
-    all_k<2>();   // the shipped draft-row and top-F streaming shape
+    all_k<2>();   // draft-row and top-F streaming shapes
+    all_k<4>();
+    all_k<8>();
     if (g_failed) {
         std::printf("FAILED: %s\n", g_why.c_str());
         return 1;
