@@ -48,10 +48,16 @@ namespace specv {
 
 namespace {
 
-constexpr int kU = 4;          // 16-byte steps per lane per iteration
-constexpr int kD = 0;          // prefetch form (see stream_chunk)
+// Row streaming (16-byte steps per lane per iteration, prefetch form; see
+// stream_chunk): the stats launch streams 4 steps deep at full occupancy;
+// the one-launch form, whose walker holds three workgroups per CU (its
+// registers), streams 8 deep, so each row workgroup keeps twice the bytes in
+// flight in registers it has anyway.
+constexpr int kU = 4;
+constexpr int kFusedU = 8;
+constexpr int kD = 0;
 constexpr int kWalkTiles = 8;       // tiles in flight per wave in a walk pass (walk launch)
-constexpr int kFusedWalkTiles = 1;  // the same in the one-launch form (its registers set the rows' occupancy)
+constexpr int kFusedWalkTiles = 2;  // the same in the one-launch form (its registers set the rows' occupancy)
 
 __device__ __forceinline__ const void* row_ptr(const RowView& v, int esz, int64_t b, int64_t r) {
     return static_cast<const char*>(v.data) + (b * v.stride_seq + r * v.stride_row) * esz;
@@ -63,7 +69,7 @@ __device__ __forceinline__ float log2e_over(float T) { return float(1.4426950408
 
 // Row task w of tree b (w = task * S + chunk; task < N: target row of node
 // task, else draft row of node task - N) -> its statistics word.
-template <int DT>
+template <int DT, int U>
 __device__ __forceinline__ void tree_row(const TreeArgs& a, int b, int64_t w) {
     constexpr int esz = ElemT<DT>::kBytes;
     const int N = a.N;
@@ -89,12 +95,12 @@ __device__ __forceinline__ void tree_row(const TreeArgs& a, int b, int64_t w) {
         const void* rp = row_ptr(draft_row ? a.draft : a.target, esz, b, node);
         if (greedy) {
             ArgmaxAcc acc;
-            stream_chunk<DT, kU, kD>(rp, lo, hi, acc);
+            stream_chunk<DT, U, kD>(rp, lo, hi, acc);
             block_merge_argmax(acc.best, acc.idx);
             word = pack_argmax(acc.best, acc.idx);
         } else {
             SoftmaxAcc acc(log2e_over(T));
-            stream_chunk_as<DT, kU, kD>(node < a.cache_nodes, rp, lo, hi, acc);
+            stream_chunk_as<DT, U, kD>(node < a.cache_nodes, rp, lo, hi, acc);
             block_merge_softmax(acc.m, acc.mc, acc.s);
             word = pack_softmax(acc.m, acc.s);
         }
@@ -105,7 +111,7 @@ __device__ __forceinline__ void tree_row(const TreeArgs& a, int b, int64_t w) {
 template <int DT>
 __global__ __launch_bounds__(kThreads) void tree_stats_kernel(TreeArgs a) {
     const int64_t RS = int64_t(2) * a.N * a.S;
-    tree_row<DT>(a, int(blockIdx.x / RS), blockIdx.x % RS);   // rows never wait: hardware order is fine
+    tree_row<DT, kU>(a, int(blockIdx.x / RS), blockIdx.x % RS);   // rows never wait: hardware order is fine
 }
 
 // ------------------------------------------------------------------ walk
@@ -552,8 +558,9 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeArgs a) {
 // trees instead of waiting for the end of the whole stream. The walker's LDS
 // is sized for the small trees and its passes keep fewer tiles in flight, so
 // that the row workgroups keep their residency.
-// The walker's registers (about 165) set the whole launch's allocation; the
-// bound keeps it at three workgroups per CU for the row workgroups.
+// The walker's registers (about 168 with two tiles in flight per wave, a few
+// bytes spilled) set the whole launch's allocation; the bound keeps it at
+// three workgroups per CU for the row workgroups.
 template <int DT>
 __global__ __launch_bounds__(kThreads, 3) void tree_fused_kernel(TreeArgs a) {
     const int64_t RS = int64_t(2) * a.N * a.S;
@@ -562,7 +569,7 @@ __global__ __launch_bounds__(kThreads, 3) void tree_fused_kernel(TreeArgs a) {
     int64_t w;
     decode_chain(g, a.B, a.B, RS, a.H, a.D, b, w);
     if (w >= RS) tree_walk<DT, kFusedTreeNodes, kFusedWalkTiles, true>(a, b, int(w - RS));
-    else tree_row<DT>(a, b, w);
+    else tree_row<DT, kFusedU>(a, b, w);
 }
 
 template <int DT>
