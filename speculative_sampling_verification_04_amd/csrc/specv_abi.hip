@@ -650,7 +650,12 @@ specv_status specv_tree_verify(specv_logits target, specv_logits draft, const in
     a.slots = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kHeader);
     a.H = H;
     a.ntiles = int32_t((int64_t(vocab) + kTileElems - 1) / kTileElems);
-    a.D = tree_fused(nodes) ? bonus_delay(batch, 2 * int64_t(nodes) * L.S) : 0;
+    // The walkers of tree b follow the rows of tree b + 2: a walk lasts
+    // longer than its tree's rows take to stream (its passes are serial), so
+    // it starts as soon as they are under way and follows them node by node
+    // (measured: 245-250 us at 0-4 trees of delay, 263 us at ~one GPU-full,
+    // 298 us at 24, for 32 trees of 64 nodes over V = 152064).
+    a.D = tree_fused(nodes) ? (batch < 2 ? batch : 2) : 0;
     a.cache_nodes = cached_positions(batch, int64_t(vocab) * elem_size(target.dtype), nodes);
     a.walk = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + tree_walk_offset(batch, nodes, vocab));
     a.epoch = next_epoch();

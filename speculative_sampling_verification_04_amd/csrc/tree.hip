@@ -554,8 +554,8 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeArgs a) {
 
 // Trees of up to kFusedTreeNodes nodes: rows and walkers in one launch, in the
 // dispatch order of the chain launches (decode_chain): the H walkers of tree b
-// follow the rows of tree b + D, so that each walk overlaps the rows of later
-// trees instead of waiting for the end of the whole stream. The walker's LDS
+// follow the rows of tree b + D (D = 2), so that each walk overlaps the rows
+// of later trees instead of waiting for the end of the whole stream. The walker's LDS
 // is sized for the small trees and its passes keep fewer tiles in flight, so
 // that the row workgroups keep their residency.
 // The walker's registers (about 168 with two tiles in flight per wave, a few
