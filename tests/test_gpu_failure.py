@@ -3,7 +3,7 @@
 Workgroups wait for each other's published words (row statistics, tile sums,
 top-F keys, a tree's pass totals), and every wait is bounded. Here the bound
 is set to one tick of the 100 MHz clock for one call, so that waits run out.
-A chain launch (verify, verify_topk) then leaves the sequences whose bonus
+A chain launch (verify, verify_topk, verify_cache, verify_ragged) then leaves the sequences whose bonus
 workgroups gave up to its finisher launch, which completes them: every
 sequence must still give the oracle's outcome, and the workspace header's
 count of sequences completed that way must have grown. A tree launch has no
@@ -151,4 +151,32 @@ def test_ragged_waits_that_run_out_are_finished(with_draft):
     again = {k: v.cpu().numpy() for k, v in out.items() if v is not None}
     for k in again:
         np.testing.assert_array_equal(gpu[k], again[k], err_msg=f"ragged: {k}")
+    assert int(ws.count_nonzero().item()) == 0
+
+
+@pytest.mark.parametrize("B,gamma,V", [(3, 4, 40000), (48, 5, 30000)])
+def test_cache_waits_that_run_out_are_finished(B, gamma, V):
+    # specv_verify_cache: with chunked rows (B = 3) the resolve waits for the
+    # cache pairs that each draft row's chunk merge publishes, so a merge that
+    # gives up defers the resolve too and the finisher runs both, merges
+    # first; with one chunk per row (B = 48) the draft rows publish them.
+    w = workloads.make_chain(B, gamma, V, dtype="bf16", sigma=3.0, noise=1.0, temps="half0_half1",
+                             gen_seed=91 + B, philox_seed=91)
+    d = chain_to_dev(w)
+    fan = [5, 4, 3, 2, 2, 1][:gamma + 1]
+    ws = torch.zeros(binding.verify_cache_workspace_bytes(B, gamma, V), dtype=torch.uint8, device="cuda")
+    call = lambda: binding.verify_cache(d["target"], d["draft"], d["tokens"], d["temperature"], fan, w.seed, 0,
+                                        saguaro_C=0.5, workspace=ws)
+    log(f"short waits: verify_cache B={B} gamma={gamma} V={V}")
+    short = with_short_waits(call)
+    n = deferred_count(ws)
+    log(f"verify_cache short waits: the finisher completed {n} of {B} sequences")
+    assert n > 0, "verify_cache: no wait ran out: the deferral path was not exercised"
+    ws[8:16].zero_()
+    out = call()
+    torch.cuda.synchronize()
+    again = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
+    for k in again:
+        if again[k] is not None:
+            np.testing.assert_array_equal(short[k], again[k], err_msg=f"verify_cache: {k}")
     assert int(ws.count_nonzero().item()) == 0
