@@ -292,16 +292,17 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
             // Each helper read the row values before publishing its tiles, so
             // once every tile pair is seen the row pairs may be zeroed.
             if (!last) return;
+            __shared__ uint64_t s_parts[2 * kMaxBonusHelpers];
             const bool ok = wait_pairs(tiles, 2 * int64_t(ntiles), ep, ticks) &&
-                            (!resid || wait_pairs(parts, 2 * int64_t(a.H), ep, ticks));
+                            (!resid || gather_pairs(parts, 2 * a.H, ep, ticks, s_parts));
             if (!ok) {
                 give_up();
                 return;
             }
             if (resid) {  // the helpers' correction sums, in helper order
                 for (int j = 0; j < a.H; ++j) {
-                    ps += unpack_f64(read_pair(parts, 2 * j));
-                    pgs += unpack_f64(read_pair(parts, 2 * j + 1));
+                    ps += unpack_f64(s_parts[2 * j]);
+                    pgs += unpack_f64(s_parts[2 * j + 1]);
                 }
             }
             const double ca = resid ? correction_a(correction_kappa(ps, pgs)) : 0.0;

@@ -81,7 +81,7 @@ struct ChainArgs {
 // per chunk (pair (b * 2N + task) * S + chunk of `slots`), and H walkers that
 // meet in `walk` (kWalkWords words per tree: the walkers' pass messages for
 // two pass parities, one acknowledgement per walker, the drawn token).
-constexpr int kMaxWalkers = 16;
+constexpr int kMaxWalkers = 16;   // their pass messages (4 pairs each) are gathered by one wave
 constexpr int kMaxTreeNodes = 4096;  // SPECV_MAX_TREE_NODES
 // Tiles of one walker's share: ceil(tiles / H) with H = tree_walkers(V) is at
 // most 32 while tiles <= 512, and at most kMaxTiles / kMaxWalkers beyond.
@@ -133,15 +133,18 @@ struct TopFArgs {
 };
 
 // Workgroups that share the bonus draw of one T > 0 sequence: about 32 tiles
-// (16K elements of the row pair) each, at most 16. Batches of up to 64
+// (16K elements of the row pair) each, at most kMaxBonusHelpers (their two
+// correction sums each are gathered by one wave). Batches of up to 64
 // sequences leave most of the GPU idle while the draws run, so there each
 // takes about 16 tiles (a shorter draw; at larger batches the extra
 // workgroups cost more slots than they save).
+constexpr int kMaxBonusHelpers = 16;
+static_assert(2 * kMaxBonusHelpers <= kWaveSize, "one pair per lane in the resolve's gather");
 inline int32_t bonus_helpers(int64_t V, int64_t B) {
     const int64_t ntiles = (V + kTileElems - 1) / kTileElems;
     const int64_t per = B <= 64 ? 16 : 32;
     const int64_t h = (ntiles + per - 1) / per;
-    return int32_t(h < 1 ? 1 : h > 16 ? 16 : h);
+    return int32_t(h < 1 ? 1 : h > kMaxBonusHelpers ? kMaxBonusHelpers : h);
 }
 
 // Positions whose rows a T > 0 sequence streams with ordinary (cacheable)

@@ -252,6 +252,32 @@ __device__ bool wait_pairs(const uint64_t* p, int64_t n, uint32_t tag, uint64_t 
     return s_ok != 0;
 }
 
+// wait_pairs for a few pairs (n <= kWaveSize) whose values are wanted too:
+// lane i of wave 0 polls pair i, and the poll that finds them all tagged
+// leaves their values in out[0, n) (LDS). A loop that read them one at a time
+// afterwards would wait one memory round trip per pair. Whole workgroup;
+// false if the bound was reached.
+__device__ bool gather_pairs(const uint64_t* p, int n, uint32_t tag, uint64_t ticks, uint64_t* out) {
+    __shared__ int s_ok;
+    if (wave_id() == 0) {
+        int ok = 0;
+        const int i = lane_id();
+        for (const WaitBound t(ticks); !t.expired();) {
+            const uint64_t hi = i < n ? peek(p + 2 * i) : 0ull;
+            const uint64_t lo = i < n ? peek(p + 2 * i + 1) : 0ull;
+            if (__all(i >= n || pair_ok(hi, lo, tag))) {
+                if (i < n) out[i] = pair_value(hi, lo);
+                ok = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (i == 0) s_ok = ok;
+    }
+    __syncthreads();
+    return s_ok != 0;
+}
+
 // Returns n pairs (2n words) to zero, the workspace's resting state.
 __device__ __forceinline__ void zero_pairs(uint64_t* p, int64_t n) {
     for (int64_t i = threadIdx.x; i < 2 * n; i += kThreads) clear_word(p + i);

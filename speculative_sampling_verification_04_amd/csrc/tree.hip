@@ -123,6 +123,7 @@ __global__ __launch_bounds__(kThreads) void tree_stats_kernel(TreeArgs a) {
 // pass number), one acknowledgement per walker and the drawn token (tag =
 // the epoch).
 constexpr int kPassValues = 4;
+static_assert(kMaxWalkers * kPassValues <= kWaveSize, "one pair per lane in the pass exchange's gather");
 struct WalkWords {
     uint64_t* part;   // [2][kMaxWalkers][kPassValues] pairs
     uint64_t* ack;    // [kMaxWalkers] pairs
@@ -144,9 +145,11 @@ __device__ __forceinline__ uint32_t pass_tag(uint32_t epoch, uint32_t pass) {
 }
 
 // Waits until the words of node `node`'s target row (and, with `draft`, its
-// draft row) are published (wave 0 polls). Whole workgroup; false if the
-// bound was reached.
-__device__ bool wait_node(const uint64_t* slots, int N, int S, int node, bool draft, uint32_t ep, uint64_t ticks) {
+// draft row) are published (wave 0 polls), and leaves their values in out
+// (LDS): chunk j of the target row at out[j], of the draft row at out[S + j]
+// (S <= kWaveSize). Whole workgroup; false if the bound was reached.
+__device__ bool wait_node(const uint64_t* slots, int N, int S, int node, bool draft, uint32_t ep, uint64_t ticks,
+                          uint64_t* out) {
     __shared__ int s_ok;
     if (wave_id() == 0) {
         int ok = 0;
@@ -155,7 +158,9 @@ __device__ bool wait_node(const uint64_t* slots, int N, int S, int node, bool dr
             bool mine = true;
             for (int i = lane_id(); i < n; i += kWaveSize) {
                 const int64_t k = i < S ? int64_t(node) * S + i : int64_t(N + node) * S + (i - S);
-                mine &= pair_ok(peek(slots + 2 * k), peek(slots + 2 * k + 1), ep);
+                const uint64_t hi = peek(slots + 2 * k), lo = peek(slots + 2 * k + 1);
+                mine &= pair_ok(hi, lo, ep);
+                out[i] = pair_value(hi, lo);   // the last poll's values stay
             }
             if (__all(mine)) { ok = 1; break; }
             __builtin_amdgcn_s_sleep(2);
@@ -175,6 +180,8 @@ struct WalkLds {
     double pc[kThreads], qc[kThreads];  // p(t), q(t) of each child's token t (streaming statistics)
     float zp[kThreads], zq[kThreads];   // the two logits at each child's token
     float u[kThreads];            // each child's uniform
+    uint64_t msg[kMaxWalkers * kPassValues];  // the walkers' pass messages, as gathered
+    uint64_t nodew[2 * kWaveSize];  // the current node's row words, as the wait for them found them
     double part[kMaxWalkers];     // the walkers' totals of the last pass (corrected)
     double tile[kMaxWalkTiles];   // this walker's tile sums of the last pass (corrected)
     float tile_q[kMaxWalkTiles];  // their q~ sums (a pass that measures the correction)
@@ -249,21 +256,20 @@ struct Walker {
             publish_pair(mine + 4, pack_f64(ps), tag);
             publish_pair(mine + 6, pack_f64(pgs), tag);
         }
-        if (!wait_pairs(part, int64_t(a.H) * kPassValues, tag, a.wait_ticks)) return false;
+        if (!gather_pairs(part, a.H * kPassValues, tag, a.wait_ticks, s.msg)) return false;
         __shared__ double s_kappa, s_A;
         if (threadIdx.x == 0) {
             double P = 0.0, PG = 0.0;
             if (kind == kPassFirst) {
                 for (int k = 0; k < a.H; ++k) {
-                    P += unpack_f64(read_pair(part, kPassValues * k + 2));
-                    PG += unpack_f64(read_pair(part, kPassValues * k + 3));
+                    P += unpack_f64(s.msg[kPassValues * k + 2]);
+                    PG += unpack_f64(s.msg[kPassValues * k + 3]);
                 }
             }
             const double kap = kind == kPassFirst ? correction_kappa(P, PG) : kappa;
             const double ca = kind == kPassFirst ? correction_a(kap) : 0.0;
             for (int k = 0; k < a.H; ++k)
-                s.part[k] = unpack_f64(read_pair(part, kPassValues * k)) +
-                            ca * unpack_f64(read_pair(part, kPassValues * k + 1));
+                s.part[k] = unpack_f64(s.msg[kPassValues * k]) + ca * unpack_f64(s.msg[kPassValues * k + 1]);
             s_kappa = kap;
             s_A = kind == kPassFirst ? P : A;
         }
@@ -288,7 +294,7 @@ struct Walker {
     // the node's words ran out.
     __device__ __forceinline__ bool next_batch(int node, bool first) {
         const uint64_t* slots = a.slots + 2 * int64_t(b) * 2 * N * a.S;
-        if (kStreaming && first && !wait_node(slots, N, a.S, node, true, a.epoch, a.wait_ticks)) return false;
+        if (kStreaming && first && !wait_node(slots, N, a.S, node, true, a.epoch, a.wait_ticks, s.nodew)) return false;
         if (wave_id() == 0) {
             int n = 0, base = first ? node + 1 : s.from;
             for (; base < N && n <= kThreads - kWaveSize; base += kWaveSize) {
@@ -302,8 +308,11 @@ struct Walker {
         }
         if (first && wave_id() == 1) {  // the node's statistics, beside wave 0's scan
             const bool lane_ok = lane_id() < a.S;
-            const uint64_t wp = lane_ok ? read_pair(slots, int64_t(node) * a.S + lane_id()) : 0ull;
-            const uint64_t wq = lane_ok ? read_pair(slots, int64_t(N + node) * a.S + lane_id()) : 0ull;
+            uint64_t wp = 0ull, wq = 0ull;
+            if (lane_ok) {
+                wp = kStreaming ? s.nodew[lane_id()] : read_pair(slots, int64_t(node) * a.S + lane_id());
+                wq = kStreaming ? s.nodew[a.S + lane_id()] : read_pair(slots, int64_t(N + node) * a.S + lane_id());
+            }
             const RowStats sp = merge_chunk_words(wp, a.S, false, c);
             const RowStats sq = merge_chunk_words(wq, a.S, false, c);
             if (lane_id() == 0) { s.sp = sp; s.sq = sq; }
@@ -408,12 +417,13 @@ __device__ __forceinline__ void tree_walk(const TreeArgs& a, int b, int h) {
     if (greedy) {  // VerifyGreedy
         int node = 0;
         while (true) {
-            if (kStreaming && !wait_node(slots, N, a.S, node, false, a.epoch, a.wait_ticks)) {
+            if (kStreaming && !wait_node(slots, N, a.S, node, false, a.epoch, a.wait_ticks, s.nodew)) {
                 if (threadIdx.x == 0) s_fail = 1;
                 break;
             }
             if (wave_id() == 0) {
-                const uint64_t wg = lane_id() < a.S ? read_pair(slots, int64_t(node) * a.S + lane_id()) : 0ull;
+                uint64_t wg = 0ull;
+                if (lane_id() < a.S) wg = kStreaming ? s.nodew[lane_id()] : read_pair(slots, int64_t(node) * a.S + lane_id());
                 const RowStats sg = merge_chunk_words(wg, a.S, true, 0.0f);
                 if (lane_id() == 0) s.sp = sg;
             }
