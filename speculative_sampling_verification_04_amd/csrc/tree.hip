@@ -289,12 +289,12 @@ struct Walker {
 
     // The next batch of the node's children (ascending ids; the first batch
     // of a node starts after the node and also brings the node's statistics)
-    // and their accept-test inputs. The statistics pairs and the children's
-    // logits are read in one round trip. Whole workgroup; false if a wait for
-    // the node's words ran out.
+    // and their accept-test inputs. The children's logits are loaded while
+    // the node's words are awaited (the wait leaves them in LDS), so the two
+    // take one round trip. Whole workgroup; false if a wait for the node's
+    // words ran out.
     __device__ __forceinline__ bool next_batch(int node, bool first) {
         const uint64_t* slots = a.slots + 2 * int64_t(b) * 2 * N * a.S;
-        if (kStreaming && first && !wait_node(slots, N, a.S, node, true, a.epoch, a.wait_ticks, s.nodew)) return false;
         if (wave_id() == 0) {
             int n = 0, base = first ? node + 1 : s.from;
             for (; base < N && n <= kThreads - kWaveSize; base += kWaveSize) {
@@ -306,24 +306,30 @@ struct Walker {
             }
             if (lane_id() == 0) { s.nk = n; s.from = base; }
         }
-        if (first && wave_id() == 1) {  // the node's statistics, beside wave 0's scan
-            const bool lane_ok = lane_id() < a.S;
-            uint64_t wp = 0ull, wq = 0ull;
-            if (lane_ok) {
-                wp = kStreaming ? s.nodew[lane_id()] : read_pair(slots, int64_t(node) * a.S + lane_id());
-                wq = kStreaming ? s.nodew[a.S + lane_id()] : read_pair(slots, int64_t(N + node) * a.S + lane_id());
-            }
-            const RowStats sp = merge_chunk_words(wp, a.S, false, c);
-            const RowStats sq = merge_chunk_words(wq, a.S, false, c);
-            if (lane_id() == 0) { s.sp = sp; s.sq = sq; }
-        }
         __syncthreads();
+        // The children's logits are inputs: their loads are in flight while
+        // the node's words are awaited.
         const bool mine = threadIdx.x < s.nk;
         const int ch = mine ? s.kid[threadIdx.x] : 0;
         const int32_t t = mine ? s.tok[ch] : -1;
         const bool in_range = t >= 0 && t < a.V;
         const float zp = in_range ? load_elem<DT>(prow, t) : -INFINITY;
         const float zq = in_range ? load_elem<DT>(qrow, t) : -INFINITY;
+        if (first) {
+            if (kStreaming && !wait_node(slots, N, a.S, node, true, a.epoch, a.wait_ticks, s.nodew)) return false;
+            if (wave_id() == 1) {  // the node's statistics
+                const bool lane_ok = lane_id() < a.S;
+                uint64_t wp = 0ull, wq = 0ull;
+                if (lane_ok) {
+                    wp = kStreaming ? s.nodew[lane_id()] : read_pair(slots, int64_t(node) * a.S + lane_id());
+                    wq = kStreaming ? s.nodew[a.S + lane_id()]
+                                    : read_pair(slots, int64_t(N + node) * a.S + lane_id());
+                }
+                const RowStats sp = merge_chunk_words(wp, a.S, false, c);
+                const RowStats sq = merge_chunk_words(wq, a.S, false, c);
+                if (lane_id() == 0) { s.sp = sp; s.sq = sq; }
+            }
+        }
         __syncthreads();
         if (mine) {
             s.pc[threadIdx.x] = in_range ? prob_of(zp, c, s.sp) : 0.0;

@@ -34,8 +34,9 @@ def test_named_tree_workload():
     (12, 7, 3000, "f32", "all0.6", 6, 1, 0.3, 5),
     (6, 200, 1000, "bf16", "all1", 10, 8, 0.3, 6),
     (40, 10, 8, "f32", "all1.5", 3, 4, 2.0, 7),
-    # passes shared by H = ceil(tiles / 32) walkers per tree (at most 16)
+    # passes shared by H = ceil(tiles / 24) walkers per tree (at most 16)
     (6, 16, 20000, "bf16", "all1", 4, 4, 1.0, 8),          # 40 tiles: H = 2
+    (5, 10, 12289, "bf16", "all1", 3, 3, 1.0, 17),         # 25 tiles, the last of one element: H = 2
     (3, 24, 300000, "f32", "all0.8", 5, 4, 1.0, 9),        # 586 tiles: H = 16
     (400, 4, 20000, "bf16", "half0_half1", 3, 2, 1.0, 10),  # 400 trees x 2 walkers may exceed residency
     # trees of 256 nodes or fewer: rows and walkers in one launch; larger: two
