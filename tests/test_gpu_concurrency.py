@@ -1,12 +1,15 @@
 """Calls on two streams at once (MI355X).
 
 Workgroups of one call wait for words published by other workgroups of the
-same call; they take their task numbers from a ticket counter in the call's
-workspace, so a waiting task only waits for tasks already claimed by running
-workgroups, whatever else the GPU runs. Here a fused chain call and a tree
+same call. A chain call's waits are bounded and its finisher launch completes
+whatever a wait left; a tree call's workgroups take their task numbers from a
+ticket counter in the call's workspace, so a waiting task only waits for
+tasks already claimed by running workgroups. Neither depends on what else the
+GPU runs. Here a fused chain call and a tree
 call run concurrently on two streams with separate workspaces (the binding's
 default workspaces are per stream), repeatedly, and every outcome must match
-the oracle with no -1 (a wait that ran out)."""
+the oracle with no -1 (a wait that ran out); then a ragged call and a cache
+call, whose outcomes must equal the same calls made alone."""
 import numpy as np
 import pytest
 import torch
@@ -51,3 +54,54 @@ def test_fused_and_tree_on_two_streams():
         assert np.all(gc["num_accepted"] >= 0) and np.all(gt["num_accepted"] >= 0), "a wait ran out"
         compare_chain(gc, ref_c, seqs_c, w.gamma, f"two streams chain {rep}")
         compare_tree(gt, ref_t, seqs_t, f"two streams tree {rep}")
+
+
+def test_ragged_and_cache_on_two_streams():
+    # The other two chain entry points, each with its own finisher launch,
+    # concurrently on two streams; every concurrent outcome must equal the
+    # same call made alone (the computation is deterministic), and neither
+    # reports -1 or -2. Their parity with the oracle is tested elsewhere.
+    rng = np.random.default_rng(303)
+    B, G, V = 64, 6, 65536
+    counts = rng.integers(0, G + 1, B)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    nd = int(offsets[-1])
+    rt = torch.from_numpy(workloads.round_to_bf16(rng.normal(0, 3, (nd + B, V)).astype(np.float32))).cuda().bfloat16()
+    rd = torch.from_numpy(workloads.round_to_bf16(rng.normal(0, 3, (nd, V)).astype(np.float32))).cuda().bfloat16()
+    rtok = torch.from_numpy(rng.integers(0, V, nd).astype(np.int32)).cuda()
+    rtemp = torch.from_numpy(np.where(np.arange(B) % 2 == 0, 0.0, 1.0).astype(np.float32)).cuda()
+    roffs = torch.from_numpy(offsets).cuda()
+    w = workloads.make_chain(48, 5, V, dtype="bf16", sigma=3.0, noise=1.0, temps="half0_half1", gen_seed=304,
+                             philox_seed=304)
+    dc = chain_to_dev(w)
+    fan = [6, 5, 4, 3, 2, 2]
+
+    def ragged():
+        return binding.verify_ragged(rt, rd, roffs, rtok, rtemp, G, 303, 0)
+
+    def cache():
+        return binding.verify_cache(dc["target"], dc["draft"], dc["tokens"], dc["temperature"], fan, w.seed, 0,
+                                    saguaro_C=0.5)
+
+    def host(o):
+        return {k: v.cpu().numpy() for k, v in o.items() if v is not None}
+
+    alone_r, alone_c = host(ragged()), host(cache())
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for rep in range(4):
+        log(f"two streams (ragged, cache), round {rep}")
+        with torch.cuda.stream(s1):
+            o_r = ragged()
+        with torch.cuda.stream(s2):
+            o_c = cache()
+        outs.append((o_r, o_c))
+    torch.cuda.synchronize()
+    assert np.all(alone_r["num_accepted"] >= 0) and np.all(alone_c["num_accepted"] >= 0)
+    for rep, (o_r, o_c) in enumerate(outs):
+        gr, gc = host(o_r), host(o_c)
+        for k in alone_r:
+            np.testing.assert_array_equal(gr[k], alone_r[k], err_msg=f"ragged {k}, round {rep}")
+        for k in alone_c:
+            np.testing.assert_array_equal(gc[k], alone_c[k], err_msg=f"cache {k}, round {rep}")
