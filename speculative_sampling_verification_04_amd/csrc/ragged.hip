@@ -53,7 +53,28 @@ __global__ __launch_bounds__(kThreads) void ragged_verify_kernel(ChainArgs a) {
     const int64_t RS = int64_t(R) * a.S;
     __shared__ SeqOrder ord;
     __shared__ ResolveLds lds;
-    ord.init(a.temperature, a.B);
+    // Up to kKeptTemps sequences the offsets are read with the temperatures,
+    // in the same round trip, so the task needs no second one to find its
+    // rows.
+    __shared__ int32_t s_offs[SeqOrder::kKeptTemps + 1];
+    const bool offs_kept = a.B <= SeqOrder::kKeptTemps;
+    ord.init(a.temperature, a.B, [&] {
+        if (!offs_kept) return;
+        constexpr int kChunks = SeqOrder::kKeptTemps / kWaveSize;
+        int32_t o[kChunks];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {   // unconditional loads, clamped index
+            const int i = c * kWaveSize + lane_id();
+            o[c] = a.offsets[i <= a.B ? i : a.B];
+        }
+        const int32_t ob = a.offsets[a.B];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int i = c * kWaveSize + lane_id();
+            if (i <= a.B) s_offs[i] = o[c];
+        }
+        if (lane_id() == 0) s_offs[a.B] = ob;
+    });
     const Placement pl = place_task(ord, [&](int, int& s, int64_t& w) {
         decode_chain(blockIdx.x, a.B, ord.nS, RS, a.H, a.D, s, w);
     });
@@ -61,7 +82,8 @@ __global__ __launch_bounds__(kThreads) void ragged_verify_kernel(ChainArgs a) {
     const int b = pl.b;
     const float T = ord.temperature_of(a.temperature, b);
     const bool greedy = !(T > 0.0f);
-    const int32_t o0 = a.offsets[b], o1 = a.offsets[b + 1];
+    const int32_t o0 = offs_kept ? __builtin_amdgcn_readfirstlane(s_offs[b]) : a.offsets[b];
+    const int32_t o1 = offs_kept ? __builtin_amdgcn_readfirstlane(s_offs[b + 1]) : a.offsets[b + 1];
     const bool valid = o0 >= 0 && o0 <= o1 && o1 <= a.num_draft && o1 - o0 <= G;
     const int gb = valid ? o1 - o0 : 0;
     uint64_t* slots = a.slots + 2 * int64_t(sidx) * RS;

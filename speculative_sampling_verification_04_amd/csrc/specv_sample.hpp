@@ -150,27 +150,58 @@ struct SeqOrder {
     int nS;                                          // T > 0 sequences (B when not ordered)
     int B;
     bool ordered;
-    // Whole workgroup (wave 0 reads the temperatures).
-    __device__ __forceinline__ void init(const float* temperature, int B_) {
+    // Whole workgroup (wave 0 reads the temperatures). Up to kKeptTemps
+    // sequences, every lane issues its kKeptTemps / 64 loads before any is
+    // used, so the placement costs one memory round trip (a loop that used
+    // each chunk before loading the next took one round trip per 64
+    // sequences); larger batches take the loop. `pre` runs in wave 0 after
+    // those loads are issued and before they are used: a caller's own loads
+    // issued there share the round trip.
+    template <class Pre>
+    __device__ __forceinline__ void init(const float* temperature, int B_, Pre pre) {
         if (wave_id() == 0) {
             const int lane = lane_id();
             const bool ord = B_ <= kMaxOrderedBatch;
             int nseq = B_;
-            if (ord) {
-                nseq = 0;
-                const int nm = (B_ + kWaveSize - 1) / kWaveSize;
-                for (int c = 0; c < nm; ++c) {
+            if (ord && B_ <= kKeptTemps) {
+                constexpr int kChunks = kKeptTemps / kWaveSize;
+                float t[kChunks];
+#pragma unroll
+                for (int c = 0; c < kChunks; ++c) {   // unconditional loads, clamped index
                     const int i = c * kWaveSize + lane;
-                    const float t = i < B_ ? temperature[i] : 0.0f;
-                    if (B_ <= kKeptTemps && i < B_) temps[i] = t;
-                    const uint64_t m = __ballot(t > 0.0f);
+                    t[c] = temperature[i < B_ ? i : B_ - 1];
+                }
+                pre();
+                nseq = 0;
+#pragma unroll
+                for (int c = 0; c < kChunks; ++c) {
+                    const int i = c * kWaveSize + lane;
+                    const float tc = i < B_ ? t[c] : 0.0f;
+                    if (i < B_) temps[i] = tc;
+                    const uint64_t m = __ballot(tc > 0.0f);
                     if (lane == 0) masks[c] = m;
                     nseq += __popcll(m);
+                }
+            } else {
+                pre();
+                if (ord) {
+                    nseq = 0;
+                    const int nm = (B_ + kWaveSize - 1) / kWaveSize;
+                    for (int c = 0; c < nm; ++c) {
+                        const int i = c * kWaveSize + lane;
+                        const float t = i < B_ ? temperature[i] : 0.0f;
+                        const uint64_t m = __ballot(t > 0.0f);
+                        if (lane == 0) masks[c] = m;
+                        nseq += __popcll(m);
+                    }
                 }
             }
             if (lane == 0) { nS = nseq; B = B_; ordered = ord; }
         }
         __syncthreads();
+    }
+    __device__ __forceinline__ void init(const float* temperature, int B_) {
+        init(temperature, B_, [] {});
     }
     // Sequence b's temperature: from LDS when init kept it (no second
     // round trip to memory before the task can start), else from memory.
