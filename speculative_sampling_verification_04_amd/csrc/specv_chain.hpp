@@ -153,6 +153,19 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
             publish_pair(mark, 1ull, ep);
         }
     };
+    // The accept tests' inputs that the caller provides (the drafted tokens
+    // and the logits at them) are loaded before the wait for the rows'
+    // words, by the lanes that use them, so the two dependent round trips
+    // overlap the wait instead of following it.
+    int32_t pre_x = -1;
+    float pre_zt = -INFINITY, pre_zd = -INFINITY;
+    if (wave_id() == 0 && lane_id() < gamma) {
+        pre_x = q.tokens[lane_id()];
+        if (!greedy && pre_x >= 0 && pre_x < a.V) {
+            pre_zt = load_elem<DT>(q.target(lane_id()), pre_x);
+            if (!NoDraft) pre_zd = load_elem<DT>(q.draft(lane_id()), pre_x);
+        }
+    }
     if (!wait_pairs(slots, nslots, ep, ticks)) {
         give_up();
         return;
@@ -189,7 +202,7 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
         const int i = lane_id();
         bool reject = false;
         if (i < gamma) {
-            const int32_t x = q.tokens[i];
+            const int32_t x = pre_x;
             const bool in_range = x >= 0 && x < a.V;
             float pt_out = 0.0f, pd_out = 1.0f;
             if (greedy) {
@@ -199,11 +212,11 @@ __device__ __forceinline__ void chain_resolve(const ChainArgs& a, const SeqView&
             } else {
                 double pt = 0.0, pd = 0.0;
                 if (in_range) {
-                    pt = prob_of(load_elem<DT>(q.target(i), x), c, st[i]);
+                    pt = prob_of(pre_zt, c, st[i]);
                     if (NoDraft) {
                         pd = 1.0;
                     } else {
-                        const float zd = load_elem<DT>(q.draft(i), x);
+                        const float zd = pre_zd;
                         RowStats qs = st[G + 1 + i];
                         double scale = 1.0;
                         if (Cache) {  // Saguaro sampling: q = sigma_{F_i,C}(draft_i / T)
