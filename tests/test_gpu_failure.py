@@ -10,7 +10,8 @@ count of sequences completed that way must have grown. A tree launch has no
 finisher (its walkers need each other): a tree whose wait ran out reports -1,
 the others give the oracle's outcome. The bound is then restored and the
 same call on the same workspace must match the oracle again and leave the
-workspace zero (but for that count)."""
+workspace zero (but for that count). A guard region after the workspace
+checks that no call writes past it."""
 import numpy as np
 import pytest
 import torch
@@ -47,6 +48,23 @@ def deferred_count(ws):
     return int(ws[8:16].view(torch.int64).item())
 
 
+GUARD = 4096
+
+
+def guarded_workspace(nbytes):
+    """A zeroed workspace of nbytes and, right after it in the same buffer, a
+    guard region of 0xAB bytes (returned too): no call may write past its
+    workspace."""
+    buf = torch.zeros(nbytes + GUARD, dtype=torch.uint8, device="cuda")
+    buf[nbytes:] = 0xAB
+    return buf[:nbytes], buf[nbytes:]
+
+
+def assert_guard(guard, what):
+    torch.cuda.synchronize()
+    assert bool((guard == 0xAB).all().item()), f"{what}: memory past the workspace was written"
+
+
 @pytest.mark.parametrize("B,gamma,V,entry", [(64, 4, 20000, "verify"), (3, 4, 40000, "verify_topk"),
                                              (48, 5, 30000, "verify_topk")])
 def test_chain_waits_that_run_out_are_finished(B, gamma, V, entry):
@@ -54,10 +72,10 @@ def test_chain_waits_that_run_out_are_finished(B, gamma, V, entry):
                              gen_seed=71 + B, philox_seed=71)
     d = chain_to_dev(w)
     if entry == "verify":
-        ws = torch.zeros(binding.verify_workspace_bytes(B, gamma, V), dtype=torch.uint8, device="cuda")
+        ws, guard = guarded_workspace(binding.verify_workspace_bytes(B, gamma, V))
         call = lambda: binding.verify(d["target"], d["draft"], d["tokens"], d["temperature"], w.seed, 0, workspace=ws)
     else:
-        ws = torch.zeros(binding.verify_topk_workspace_bytes(B, gamma, V), dtype=torch.uint8, device="cuda")
+        ws, guard = guarded_workspace(binding.verify_topk_workspace_bytes(B, gamma, V))
         call = lambda: binding.verify_topk(d["target"], d["draft"], d["tokens"], d["temperature"], 4, w.seed, 0,
                                            workspace=ws)
     log(f"short waits: {entry} B={B} gamma={gamma} V={V}")
@@ -66,6 +84,7 @@ def test_chain_waits_that_run_out_are_finished(B, gamma, V, entry):
     n = deferred_count(ws)
     log(f"{entry} short waits: the finisher completed {n} of {B} sequences")
     assert n > 0, f"{entry}: no wait ran out: the deferral path was not exercised"
+    assert_guard(guard, f"{entry} short waits")
     compare_chain(gpu, ref, seqs, gamma, f"{entry} short waits")
     ws[8:16].zero_()
     out = call()
@@ -130,7 +149,7 @@ def test_ragged_waits_that_run_out_are_finished(with_draft):
          for k in ("target", "draft", "tokens", "temperature")}
     bad = offsets.copy()
     bad[6] = bad[5] - 1                       # sequence 5: decreasing offsets
-    ws = torch.zeros(binding.verify_ragged_workspace_bytes(40, 5, 20000, with_draft), dtype=torch.uint8, device="cuda")
+    ws, guard = guarded_workspace(binding.verify_ragged_workspace_bytes(40, 5, 20000, with_draft))
     draft = d["draft"] if with_draft else None
 
     def call(offs):
@@ -140,10 +159,12 @@ def test_ragged_waits_that_run_out_are_finished(with_draft):
     log(f"short waits: ragged B=40 G=5 V=20000 with_draft={with_draft}")
     gpu = with_short_waits(lambda: call(offsets))
     assert deferred_count(ws) > 0, "ragged: no wait ran out: the deferral path was not exercised"
+    assert_guard(guard, "ragged short waits")
     ref = oracle.ragged.verify_ragged_batch(r["target"], r["draft"] if with_draft else None, offsets, r["tokens"],
                                             r["temperature"], r["seed"], 0, r["G"])
     compare(gpu, ref, r, "ragged short waits")
     bad_out = with_short_waits(lambda: call(bad))
+    assert_guard(guard, "ragged short waits, bad offsets")
     assert bad_out["num_accepted"][5] == -2
     ws[8:16].zero_()
     out = call(offsets)
@@ -164,7 +185,7 @@ def test_cache_waits_that_run_out_are_finished(B, gamma, V):
                              gen_seed=91 + B, philox_seed=91)
     d = chain_to_dev(w)
     fan = [5, 4, 3, 2, 2, 1][:gamma + 1]
-    ws = torch.zeros(binding.verify_cache_workspace_bytes(B, gamma, V), dtype=torch.uint8, device="cuda")
+    ws, guard = guarded_workspace(binding.verify_cache_workspace_bytes(B, gamma, V))
     call = lambda: binding.verify_cache(d["target"], d["draft"], d["tokens"], d["temperature"], fan, w.seed, 0,
                                         saguaro_C=0.5, workspace=ws)
     log(f"short waits: verify_cache B={B} gamma={gamma} V={V}")
@@ -172,6 +193,7 @@ def test_cache_waits_that_run_out_are_finished(B, gamma, V):
     n = deferred_count(ws)
     log(f"verify_cache short waits: the finisher completed {n} of {B} sequences")
     assert n > 0, "verify_cache: no wait ran out: the deferral path was not exercised"
+    assert_guard(guard, "verify_cache short waits")
     ws[8:16].zero_()
     out = call()
     torch.cuda.synchronize()
@@ -180,3 +202,35 @@ def test_cache_waits_that_run_out_are_finished(B, gamma, V):
         if again[k] is not None:
             np.testing.assert_array_equal(short[k], again[k], err_msg=f"verify_cache: {k}")
     assert int(ws.count_nonzero().item()) == 0
+
+
+def test_finisher_with_most_sequences_deferred():
+    # 40 sequences over long rows: every workgroup of the call is resident at
+    # once, so with waits of one tick nearly every bonus task gives up and the
+    # finisher completes nearly every sequence, those of slots 31 and up
+    # included (the finisher reads each wave's 64-bit mask of deferred slots;
+    # a mask widened with a sign would name slots past the batch). Outputs
+    # must equal the oracle's and nothing past the workspace may be written.
+    B, gamma, V = 40, 4, 128256
+    w = workloads.make_chain(B, gamma, V, dtype="bf16", sigma=3.0, noise=1.0, temps="half0_half1",
+                             gen_seed=41, philox_seed=41)
+    d = chain_to_dev(w)
+    ref, seqs = run_chain_oracle(w)
+    for entry in ("verify", "verify_topk"):
+        if entry == "verify":
+            ws, guard = guarded_workspace(binding.verify_workspace_bytes(B, gamma, V))
+            call = lambda: binding.verify(d["target"], d["draft"], d["tokens"], d["temperature"], w.seed, 0,
+                                          workspace=ws)
+        else:
+            ws, guard = guarded_workspace(binding.verify_topk_workspace_bytes(B, gamma, V))
+            call = lambda: binding.verify_topk(d["target"], d["draft"], d["tokens"], d["temperature"], 4, w.seed, 0,
+                                               workspace=ws)
+        log(f"most deferred: {entry} B={B} gamma={gamma} V={V}")
+        gpu = with_short_waits(call)
+        n = deferred_count(ws)
+        log(f"{entry}: the finisher completed {n} of {B} sequences")
+        assert n > 0
+        assert_guard(guard, f"{entry}, most deferred")
+        compare_chain(gpu, ref, seqs, gamma, f"{entry}, most deferred")
+        ws[8:16].zero_()
+        assert int(ws.count_nonzero().item()) == 0
