@@ -1,21 +1,24 @@
-"""Seeded random shapes across the entry points: batch, draft length,
-vocabulary, dtype, temperatures, F and tree sizes drawn at random (small
-enough for the oracle), each call compared with the oracle as in the
-per-entry-point tests. The seeds are fixed, so every run checks the same
-shapes."""
+"""Seeded random shapes for every entry point against the oracle (MI355X).
+
+Each seed draws a batch, draft length, vocabulary (tiny, medium or large),
+dtype, temperature mix and draft noise; the chain case runs specv_verify and
+specv_verify_topk (top-F compared on a sample of sequences), the ragged case
+specv_verify_ragged with and without draft logits, the tree case
+specv_tree_verify on a random topology. The parity bar is the one of the
+fixed-shape tests: every outcome bit-exact except oracle-flagged near ties."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from gpu_common import (chain_to_dev, compare_chain, compare_tree, log, run_chain_oracle, run_tree_gpu,
-                        run_tree_oracle)
+from gpu_common import chain_to_dev, compare_chain, compare_tree, log, run_chain_oracle, run_tree_oracle, tree_to_dev
 from speculative_sampling_verification_04_amd import binding
 
 pytestmark = pytest.mark.gpu
 
-TEMPS = ("all1", "all0", "half0_half1", "all0.7", "all1.5")
+TEMPS = ("half0_half1", "all1", "all0.7", "all0", "all1.5")
+SEEDS = range(40)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -25,70 +28,67 @@ def gpu():
     binding.load_library()
 
 
-def draw_chain_shape(rng):
-    """(B, gamma, V) with B * (gamma + 1) * V <= 1.5e6 elements; half the draws
-    have V >= 16384 (rows split into chunks at small batches)."""
-    while True:
-        if rng.random() < 0.5:
-            V = int(rng.integers(16384, 70001))
-        else:
-            V = int(np.exp(rng.uniform(0.0, np.log(16384))))
-        gamma = int(rng.integers(1, 17))
-        B = int(np.exp(rng.uniform(0.0, np.log(300))))
-        if B * (gamma + 1) * V <= 1_500_000:
-            return B, gamma, max(V, 1)
+def host(o):
+    return {k: (v.cpu().numpy() if v is not None else None) for k, v in o.items()}
 
 
-def draw_tree_shape(rng):
-    """(N, depth, branching) for which the tree generator can place every node."""
-    while True:
-        N = int(rng.integers(2, 300))
-        depth = int(rng.integers(1, min(N - 1, 10) + 1))
-        branching = int(rng.integers(2, 6))
-        if sum(branching ** d for d in range(1, depth + 1)) >= N - 1:
-            return N, depth, branching
-
-
-@pytest.mark.parametrize("seed", range(12))
-def test_random_chain_and_fused(seed):
-    rng = np.random.default_rng(9000 + seed)
-    B, gamma, V = draw_chain_shape(rng)
-    dtype = "bf16" if rng.random() < 0.6 else "f32"
-    temps = TEMPS[int(rng.integers(len(TEMPS)))]
-    F = int(rng.integers(1, min(31, V - 1) + 1)) if V > 1 else None
-    w = workloads.make_chain(B, gamma, V, dtype=dtype, sigma=float(rng.uniform(1, 4)),
-                             noise=float(rng.uniform(0.2, 2)), temps=temps, gen_seed=9100 + seed,
-                             philox_seed=seed, F=F or 1)
-    log(f"random chain {seed}: B={B} gamma={gamma} V={V} {dtype} {temps} F={F}")
+@pytest.mark.parametrize("seed", SEEDS)
+def test_chain_random_shapes(seed):
+    rng = np.random.default_rng(80000 + seed)
+    gamma = int(rng.integers(1, 9))
+    V = int(rng.choice([int(rng.integers(2, 300)), int(rng.integers(300, 5000)), int(rng.integers(5000, 70000))]))
+    B = max(1, min(int(np.exp(rng.uniform(0, np.log(600)))), 3_000_000 // ((gamma + 1) * V)))
+    dtype = "bf16" if seed % 2 else "f32"
+    noise = float(rng.choice([1.0, 0.3, 0.05]))
+    F = int(rng.integers(1, min(31, V - 1) + 1)) if V > 2 else 1
+    name = f"chain random {seed}: B={B} gamma={gamma} V={V} {dtype} {TEMPS[seed % 5]} noise={noise} F={F}"
+    log(name)
+    w = workloads.make_chain(B, gamma, V, dtype=dtype, sigma=3.0, noise=noise, temps=TEMPS[seed % 5],
+                             gen_seed=81000 + seed, philox_seed=seed)
     d = chain_to_dev(w)
     ref, seqs = run_chain_oracle(w)
-    out = binding.verify(d["target"], d["draft"], d["tokens"], d["temperature"], w.seed, 0)
-    torch.cuda.synchronize()
-    compare_chain({k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}, ref, seqs, gamma,
-                  f"random verify {seed}")
-    if F is None:
-        return
-    fo = binding.verify_topk(d["target"], d["draft"], d["tokens"], d["temperature"], F, w.seed, 0)
-    torch.cuda.synchronize()
-    f = {k: (v.cpu().numpy() if v is not None else None) for k, v in fo.items()}
-    compare_chain(f, ref, seqs, gamma, f"random verify_topk {seed}")
-    ids, vals = oracle.topf.bonus_topf_batch(w.draft.astype(np.float64), w.draft_tokens, F)
-    np.testing.assert_array_equal(f["topk"], ids, err_msg=f"random top-F {seed}")
-    np.testing.assert_array_equal(f["topk_logits"].astype(np.float64), vals)
+    v = host(binding.verify(d["target"], d["draft"], d["tokens"], d["temperature"], w.seed, w.offset))
+    compare_chain(v, ref, seqs, gamma, name + " verify")
+    if V > F:
+        f = host(binding.verify_topk(d["target"], d["draft"], d["tokens"], d["temperature"], F, w.seed, w.offset))
+        compare_chain(f, ref, seqs, gamma, name + " verify_topk")
+        for b in range(0, B, max(1, B // 8)):
+            ids, _ = oracle.topf.bonus_topf_batch(w.draft[b:b + 1].astype(np.float64), w.draft_tokens[b:b + 1], F)
+            np.testing.assert_array_equal(f["topk"][b], ids[0], err_msg=f"{name}: top-F of sequence {b}")
 
 
-@pytest.mark.parametrize("seed", range(6))
-def test_random_tree(seed):
-    rng = np.random.default_rng(9500 + seed)
-    N, depth, branching = draw_tree_shape(rng)
-    V = int(np.exp(rng.uniform(np.log(8), np.log(40000))))
-    B = max(1, min(int(rng.integers(1, 24)), 3_000_000 // (2 * N * V)))
-    temps = TEMPS[int(rng.integers(len(TEMPS)))]
-    t = workloads.make_tree(B, N, V, depth=depth, branching=branching, dtype="bf16" if seed % 2 else "f32",
-                            sigma=3.0, noise=float(rng.uniform(0.3, 1.5)), temps=temps, gen_seed=9600 + seed,
-                            philox_seed=seed)
-    log(f"random tree {seed}: B={B} N={N} V={V} depth={depth} branching={branching} {temps}")
-    gpu = run_tree_gpu(t)
+@pytest.mark.parametrize("seed", SEEDS)
+def test_ragged_random_shapes(seed):
+    from test_gpu_ragged import compare, make_ragged, run
+    rng = np.random.default_rng(82000 + seed)
+    G = int(rng.integers(1, 7))
+    V = int(rng.integers(2, 20000))
+    B = max(1, min(int(rng.integers(1, 400)), 2_000_000 // ((2 * G + 1) * V)))
+    r = make_ragged(B, G, V, "bf16" if seed % 2 else "f32", "mixed" if seed % 3 else "1", 83000 + seed)
+    for with_draft in (True, False):
+        log(f"ragged random {seed}: B={B} G={G} V={V} with_draft={with_draft}")
+        gpu, ref = run(r, with_draft)
+        assert compare(gpu, ref, r, f"ragged random {seed}") <= max(1, B // 10)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_tree_random_shapes(seed):
+    rng = np.random.default_rng(84000 + seed)
+    N = int(rng.integers(1, 80))
+    V = int(rng.integers(2, 30000))
+    B = max(1, min(int(rng.integers(1, 60)), 2_000_000 // (2 * N * V)))
+    depth = min(int(rng.integers(1, 7)), N - 1)
+    br = int(rng.integers(1, 5))
+    capacity = depth + 1 if br == 1 else (br ** (depth + 1) - 1) // (br - 1)
+    if capacity < 2 * N:   # a topology with room for every node
+        depth, br = min(6, N - 1), 4
+    noise = float(rng.choice([1.0, 0.2]))
+    name = f"tree random {seed}: B={B} N={N} V={V} depth={depth} branching={br} noise={noise}"
+    log(name)
+    t = workloads.make_tree(B, N, V, depth=depth, branching=br, dtype="bf16" if seed % 2 else "f32", sigma=3.0,
+                            noise=noise, temps=TEMPS[(seed + 1) % 5], gen_seed=85000 + seed, philox_seed=seed)
+    dt = tree_to_dev(t)
+    gpu = host(binding.tree_verify(dt["target"], dt["draft"], dt["parent"], dt["tokens"], dt["temperature"], t.seed,
+                                   t.offset))
     ref, seqs = run_tree_oracle(t)
-    good, bad = compare_tree(gpu, ref, seqs, f"random tree {seed}")
-    assert bad <= max(1, B // 10)
+    compare_tree(gpu, ref, seqs, name)
