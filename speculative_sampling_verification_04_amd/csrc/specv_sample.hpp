@@ -483,9 +483,12 @@ struct TargetWeights {
 // once known), B = log2 of each row's normaliser. With a pending correction
 // (kCorrected use: a != 0 after kappa is known) the weight of an element with
 // h < 0 is w~ + a q~ (see the file comment); pass A returns w~ and q~.
-template <int DT, bool kTop = false>
+// kMeasure = false: the weights of a pass whose correction is already folded
+// into Hk (a = 0): only w~, the same values bit for bit, without the terms of
+// the correction sums and q~.
+template <int DT, bool kTop = false, bool kMeasure = true>
 struct ResidualWeights {
-    static constexpr bool kCorrected = true;
+    static constexpr bool kCorrected = kMeasure;
     struct Raw { Raw8<DT> p, q; };
     const void* prow;
     const void* qrow;
@@ -530,10 +533,25 @@ struct ResidualWeights {
             if (!(p > 0.0f)) wt = qt = 0.0f;
         }
     }
+    // w~ alone: p (1 - 2^h) where h < 0, else 0. Where p is 0 or 2^h leaves
+    // fp32's range the product is 0 or not a number and fmaxf returns 0, as
+    // element() does.
+    __device__ __forceinline__ float light(float zp, float zq, int64_t j) const {
+        const bool top = kTop && full_key(zq, j) >= top_key;
+        const float p = exp2_reduced(fma(double(zp), c, -Bp));
+        double h = fma(double(zq) - double(zp), c, -Hk);
+        if (top) h += log2C;
+        return fmaxf(p * -exp2m1(float(h)), 0.0f);
+    }
     __device__ __forceinline__ void sums(const Raw& r, int64_t j0, GroupSums& g) const {
         float zp[kLaneElems], zq[kLaneElems];
         unpack8<DT>(r.p, zp);
         unpack8<DT>(r.q, zq);
+        if constexpr (!kMeasure) {   // the same sum, in the same order, as below
+#pragma unroll
+            for (int e = 0; e < kLaneElems; ++e) g.w += light(zp[e], zq[e], j0 + e);
+            return;
+        }
         const double nq = -(Hk + Bp);                                // log2 q~ = zq c [+ log2 C] + nq
 #pragma unroll
         for (int e = 0; e < kLaneElems; ++e) {

@@ -226,10 +226,14 @@ struct Walker {
             TargetWeights<DT> f;
             f.init(prow, c64, s.sp, a.V);
             weight_tile_range<TIF>(f, lo, hi, put, ps, pgs);
+        } else if (kind == kPassResid) {   // the correction is known: w~ alone
+            ResidualWeights<DT, false, false> f;
+            f.init(prow, qrow, c64, s.sp, log2_norm(s.sq), coef, a.V);
+            f.Hk += kappa;
+            weight_tile_range<TIF>(f, lo, hi, put, ps, pgs);
         } else {
             ResidualWeights<DT> f;
             f.init(prow, qrow, c64, s.sp, log2_norm(s.sq), coef, a.V);
-            if (kind == kPassResid) f.Hk += kappa;
             weight_tile_range<TIF>(f, lo, hi, put, ps, pgs);
         }
         const int nt = hi - lo;
